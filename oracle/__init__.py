@@ -1,0 +1,202 @@
+"""CPU oracle for MoE token dispatch and combine -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  It wraps ``oracle.c`` (plain C, built
+with gcc, no fast-math) through ctypes and numpy; it shares no code with the
+HIP library and never imports it.
+
+Every function here is argument marshalling around the C routines, whose
+header comment lists the passages each step follows.  Formats:
+
+* ``"bf16"``  payload ``uint16 [R_max, H]``, no scales;
+* ``"fp8"``   payload ``uint8 [R_max, H]`` (OCP E4M3 codes), scales
+  ``float32 [R_max, H/128]``;
+* ``"mxfp4"`` payload ``uint8 [R_max, H/2]`` (two E2M1 codes a byte, element
+  2m in the low nibble), scales ``uint8 [R_max, H/32]`` (E8M0 exponents).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "oracle.c")
+LIB = os.path.join(HERE, "liboracle.so")
+
+FMT = {"bf16": 0, "fp8": 1, "mxfp4": 2}
+BAD_ID, DUP_ID, CAPACITY = 1, 2, 4
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile ``oracle.c`` into ``liboracle.so`` next to it."""
+    if force or not os.path.exists(LIB):
+        tmp = LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(
+            ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-ffp-contract=off",
+             "-Wall", "-o", tmp, SRC, "-lm"])
+        os.replace(tmp, LIB)
+    return LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB):
+            build(force=False)
+        lib = ctypes.CDLL(LIB)
+        p = ctypes.c_void_p
+        i64, i32 = ctypes.c_int64, ctypes.c_int
+        lib.oracle_max_rows.restype = i64
+        lib.oracle_max_rows.argtypes = [i64, i32, i32, i32]
+        lib.oracle_plan.restype = None
+        lib.oracle_plan.argtypes = [i64, i32, i32, i32, i32, i64, i64] + [p] * 8
+        lib.oracle_encode_row.restype = None
+        lib.oracle_encode_row.argtypes = [i32, i64, p, p, p]
+        lib.oracle_dispatch.restype = None
+        lib.oracle_dispatch.argtypes = [i32, i64, i64, i64, p, p, p, p, i32]
+        lib.oracle_combine.restype = None
+        lib.oracle_combine.argtypes = [i64, i32, i64, p, p, p, p]
+        for name in ("oracle_f32_to_bf16_array", "oracle_e4m3_encode_array",
+                     "oracle_e2m1_encode_array"):
+            getattr(lib, name).restype = None
+            getattr(lib, name).argtypes = [p, p, i64]
+        lib.oracle_e4m3_value.restype = ctypes.c_double
+        lib.oracle_e4m3_value.argtypes = [i32]
+        lib.oracle_e2m1_value.restype = ctypes.c_double
+        lib.oracle_e2m1_value.argtypes = [i32]
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def max_rows(n: int, k: int, e: int, a: int) -> int:
+    """R_max = N*k + E*(A-1)."""
+    return int(_load().oracle_max_rows(n, k, e, a))
+
+
+def payload_shape(fmt: str, r_max: int, h: int):
+    """(payload dtype, payload shape, scale dtype or None, scale shape)."""
+    if fmt == "bf16":
+        return np.uint16, (r_max, h), None, (r_max, 0)
+    if fmt == "fp8":
+        return np.uint8, (r_max, h), np.float32, (r_max, h // 128)
+    if fmt == "mxfp4":
+        return np.uint8, (r_max, h // 2), np.uint8, (r_max, h // 32)
+    raise ValueError(fmt)
+
+
+def plan(ids: np.ndarray, n_experts: int, ep: int, pad_multiple: int,
+         recv_capacity: int, hidden: int) -> dict:
+    """Counts, padded offsets, (4, EP) table, slots and packed sources.
+
+    ``ids`` is ``int32 [N, k]`` with -1 for a masked slot.
+    """
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    n, k = ids.shape
+    e = n_experts
+    r_max = max_rows(n, k, e, pad_multiple)
+    out = dict(
+        expert_counts=np.zeros(e, np.int32),
+        expert_offsets=np.zeros(e + 1, np.int32),
+        dest_counts=np.zeros(ep, np.int32),
+        rank_table=np.zeros((4, ep), np.uint32),
+        slot=np.zeros((n, k), np.int32),
+        packed_src=np.zeros(max(r_max, 0), np.int32),
+        status=np.zeros(1, np.uint32),
+    )
+    _load().oracle_plan(n, k, e, ep, pad_multiple, recv_capacity, hidden,
+                        _ptr(ids), _ptr(out["expert_counts"]),
+                        _ptr(out["expert_offsets"]), _ptr(out["dest_counts"]),
+                        _ptr(out["rank_table"]), _ptr(out["slot"]),
+                        _ptr(out["packed_src"]), _ptr(out["status"]))
+    out["r_max"] = r_max
+    out["r_used"] = int(out["expert_offsets"][e])
+    out["status"] = int(out["status"][0])
+    return out
+
+
+def encode_rows(fmt: str, x: np.ndarray):
+    """Encode whole hidden rows ``uint16 [M, H]``: (payload rows, scale rows)."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    m, h = x.shape
+    pdt, pshape, sdt, sshape = payload_shape(fmt, m, h)
+    pay = np.zeros(pshape, pdt)
+    sc = np.zeros(sshape, sdt if sdt is not None else np.uint8)
+    lib = _load()
+    for r in range(m):
+        lib.oracle_encode_row(FMT[fmt], h, _ptr(x[r]), _ptr(pay[r]),
+                              _ptr(sc[r]) if sdt is not None else None)
+    return pay, (sc if sdt is not None else None)
+
+
+def dispatch(fmt: str, x: np.ndarray, pl: dict, zero_tail: bool = True,
+             payload: np.ndarray | None = None, scales: np.ndarray | None = None):
+    """Packed payload and scales for the whole buffer (gather form).
+
+    Rows past R_used are zero when ``zero_tail``; otherwise they keep what the
+    given ``payload``/``scales`` arrays held (zeros if none are given).
+    """
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    h = x.shape[1]
+    r_max = pl["r_max"]
+    pdt, pshape, sdt, sshape = payload_shape(fmt, r_max, h)
+    if payload is None:
+        payload = np.zeros(pshape, pdt)
+    if scales is None:
+        scales = np.zeros(sshape, sdt if sdt is not None else np.uint8)
+    _load().oracle_dispatch(FMT[fmt], h, r_max, pl["r_used"],
+                            _ptr(pl["packed_src"]), _ptr(x), _ptr(payload),
+                            _ptr(scales), int(zero_tail))
+    return payload, (scales if sdt is not None else None)
+
+
+def combine(slot: np.ndarray, w: np.ndarray, y: np.ndarray) -> np.ndarray:
+    """``out uint16 [N, H]`` (bf16 bits) from ``slot [N,k]``, ``w f32 [N,k]``
+    and expert outputs ``y uint16 [rows, H]``."""
+    slot = np.ascontiguousarray(slot, dtype=np.int32)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    y = np.ascontiguousarray(y, dtype=np.uint16)
+    n, k = slot.shape
+    h = y.shape[1]
+    out = np.zeros((n, h), np.uint16)
+    _load().oracle_combine(n, k, h, _ptr(slot), _ptr(w), _ptr(y), _ptr(out))
+    return out
+
+
+def f32_to_bf16(a: np.ndarray) -> np.ndarray:
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    out = np.zeros(a.shape, np.uint16)
+    _load().oracle_f32_to_bf16_array(_ptr(a), _ptr(out), a.size)
+    return out
+
+
+def e4m3_encode(a: np.ndarray) -> np.ndarray:
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    out = np.zeros(a.shape, np.uint8)
+    _load().oracle_e4m3_encode_array(_ptr(a), _ptr(out), a.size)
+    return out
+
+
+def e2m1_encode(a: np.ndarray) -> np.ndarray:
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    out = np.zeros(a.shape, np.uint8)
+    _load().oracle_e2m1_encode_array(_ptr(a), _ptr(out), a.size)
+    return out
+
+
+def e4m3_value(code: int) -> float:
+    """Value of a non-negative E4M3 code 0..126."""
+    return float(_load().oracle_e4m3_value(code))
+
+
+def e2m1_value(code: int) -> float:
+    return float(_load().oracle_e2m1_value(code))
