@@ -1,0 +1,338 @@
+#!/usr/bin/env python3
+"""Benchmark: MoE dispatch + combine on one MI355X.
+
+One step = the whole path on one batch: moe_dispatch_plan, moe_dispatch,
+moe_combine (identity experts for bf16 workloads: the combine reads the
+packed rows the dispatch wrote; random bf16 expert outputs otherwise).
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
+
+Prints ONE JSON line on stdout.  ``value`` = algorithmic bytes of one step
+(plan + dispatch + combine, see ``step_bytes``) / measured step time, in
+GB/s.  Inputs are resident in HBM before timing starts; consecutive steps
+rotate over several copies of all buffers so that a step does not find its
+inputs in the 256 MB last-level cache from the step before.
+
+Per-kernel durations for the roofline come from HIP events recorded around
+every launch on the stream the kernels run on, in a second pass over the
+same number of steps.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, published
+DEFAULT_WORKLOAD = "uniform_bf16_n4096"
+METRIC = "dispatch+combine effective HBM GB/s (% of peak) on 1 GPU; µs at decode shape"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def row_bytes(fmt, h):
+    return {"bf16": 2 * h, "fp8": h + 4 * (h // 128), "mxfp4": h // 2 + h // 32}[fmt]
+
+
+def step_bytes(w, r_used, r_max):
+    """Algorithmic bytes of one step (each array read or written once)."""
+    nk = w.n * w.k
+    plan = 4 * nk + 4 * nk + 4 * r_max                     # ids, slot, packed_src
+    dispatch = 2 * w.n * w.h + r_used * row_bytes(w.fmt, w.h)  # read x once, write live+pad rows
+    combine = 4 * nk + 4 * nk + 2 * w.h * nk + 2 * w.n * w.h   # slot, w, k rows of y, out
+    return dict(plan=plan, dispatch=dispatch, combine=combine,
+                total=plan + dispatch + combine)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(os.path.join(ROOT, "combine_topk_ids_amd", "csrc"))):
+        with open(os.path.join(ROOT, "combine_topk_ids_amd", "csrc", name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(workload, kernel, launch_bytes):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, or None
+    if there are none for this workload/kernel or the kernels changed since."""
+    path = os.path.join(ROOT, "profiles", f"counters_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    if not k:
+        return None
+    return k["hbm_bytes_per_launch"]
+
+
+class Path:
+    """Device buffers and the three calls of one step, for one workload."""
+
+    def __init__(self, moe, torch, w, inp, copies):
+        self.moe, self.torch, self.w = moe, torch, w
+        self.p = moe.problem(w.n, w.h, w.k, w.e, w.ep, recv_capacity=w.capacity,
+                             pad_multiple=w.a, fmt=w.fmt, zero_tail=False)
+        self.r_max = moe.moe_max_rows(self.p)
+        dev = "cuda"
+        x = torch.from_numpy(inp["hidden"].view(np.int16)).to(dev).view(torch.bfloat16)
+        ids = torch.from_numpy(inp["ids"]).to(dev)
+        wts = torch.from_numpy(inp["weights"]).to(dev)
+        y = None
+        if "expert_out" in inp:
+            y = torch.from_numpy(inp["expert_out"].view(np.int16)).to(dev).view(torch.bfloat16)
+        self.sets = []
+        for c in range(copies):
+            plan = moe.alloc_plan(self.p, dev)
+            payload, scales = moe.alloc_payload(self.p, dev)
+            payload.view(torch.uint8).zero_()
+            if scales is not None:
+                scales.zero_()
+            self.sets.append(dict(
+                x=x if c == 0 else x.clone(), ids=ids if c == 0 else ids.clone(),
+                w=wts if c == 0 else wts.clone(),
+                y=(y if c == 0 else y.clone()) if y is not None else payload,
+                plan=plan, payload=payload, scales=scales,
+                out=torch.empty((w.n, w.h), dtype=torch.bfloat16, device=dev)))
+
+    def step(self, i, ev=None):
+        s = self.sets[i % len(self.sets)]
+        m, p = self.moe, self.p
+        if ev is not None:
+            ev[0].record()
+        m.moe_dispatch_plan(p, s["ids"], s["plan"])
+        if ev is not None:
+            ev[1].record()
+        m.moe_dispatch(p, s["plan"], s["x"], s["payload"], s["scales"])
+        if ev is not None:
+            ev[2].record()
+        m.moe_combine(p, s["plan"], s["y"], s["w"], s["out"])
+        if ev is not None:
+            ev[3].record()
+
+    def r_used(self):
+        return int(self.sets[0]["plan"].expert_offsets[-1].item())
+
+
+def time_steps(torch, path, steps, warmup):
+    for i in range(warmup):
+        path.step(i)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(steps):
+        path.step(warmup + i)
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return start.elapsed_time(end) / steps, wall
+
+
+def time_kernels(torch, path, steps):
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        path.step(i, evs[i])
+    torch.cuda.synchronize()
+    d = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])]
+                  for e in evs])
+    return dict(plan=float(np.mean(d[:, 0])), dispatch=float(np.mean(d[:, 1])),
+                combine=float(np.mean(d[:, 2])),
+                plan_p50=float(np.median(d[:, 0])), dispatch_p50=float(np.median(d[:, 1])),
+                combine_p50=float(np.median(d[:, 2])))
+
+
+def copy_reference(torch, gib=1.0):
+    """Achievable-bandwidth context: a plain device copy (read + write)."""
+    n = int(gib * (1 << 30)) // 2
+    a = torch.empty(n, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    s.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / reps
+    del a, b
+    return 2 * n * 2 / (ms * 1e-3) / 1e9
+
+
+def decode_latency(moe, torch, w, inp, iters=200):
+    """µs per plan + dispatch + combine at the decode shape: plain launches
+    and as a replayed HIP graph."""
+    path = Path(moe, torch, w, inp, copies=1)
+    for i in range(20):
+        path.step(0)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for i in range(iters):
+        path.step(0)
+    e.record()
+    torch.cuda.synchronize()
+    plain = s.elapsed_time(e) / iters * 1e3
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        path.step(0)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        path.step(0)
+    for _ in range(20):
+        g.replay()
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(iters):
+        g.replay()
+    e.record()
+    torch.cuda.synchronize()
+    graph = s.elapsed_time(e) / iters * 1e3
+    # the graph's result must equal the eager one
+    ref = path.sets[0]["out"].clone()
+    path.step(0)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(ref.view(torch.int16), path.sets[0]["out"].view(torch.int16)))
+    return dict(workload=w.name, us_plain=round(plain, 2), us_graph=round(graph, 2),
+                graph_matches_eager=same, iters=iters)
+
+
+def cpu_baseline(w, inp, r_max, budget_s=10.0):
+    """The CPU oracle on the host (single thread), repeated over the whole
+    workload (or over token subsets for large quantised ones) until ~budget_s
+    of CPU time; GB/s with the same algorithmic byte formula."""
+    import oracle
+    oracle.build(force=False)
+    ids, wts, x = inp["ids"], inp["weights"], inp["hidden"]
+    y = inp.get("expert_out")
+    runs, total_bytes, t_total = 0, 0, 0.0
+    while t_total < budget_s and runs < 50:
+        t0 = time.process_time()
+        pl = oracle.plan(ids, w.e, w.ep, w.a, w.capacity, w.h)
+        pay, _ = oracle.dispatch(w.fmt, x, pl, zero_tail=False)
+        yy = pay.view(np.uint16).reshape(r_max, -1) if y is None else y
+        oracle.combine(pl["slot"], wts, yy)
+        t_total += time.process_time() - t0
+        total_bytes += step_bytes(w, pl["r_used"], r_max)["total"]
+        runs += 1
+    return dict(value=round(total_bytes / t_total / 1e9, 3), unit="GB/s", cores=1,
+                kind="oracle",
+                sample=f"{runs} full passes of plan+dispatch+combine over {w.name} "
+                       f"({w.describe()}), {t_total:.1f} s CPU, single thread")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--copies", type=int, default=0, help="buffer sets rotated over (0: auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-copy-ref", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build "
+              "measures one GPU's share of the work, with expert-parallel ranks simulated as "
+              "segments of one buffer.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import combine_topk_ids_amd.moe as moe
+    from combine_topk_ids_amd.workloads import WORKLOADS, make_inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    w = WORKLOADS[args.workload]
+    log(f"[bench] workload {w.name}: {w.describe()}")
+    r_max = w.n * w.k + w.e * (w.a - 1)
+    inp = make_inputs(w, seed=0, expert_rows=r_max)
+    set_bytes = (w.n * w.h * 2 * 2 + r_max * row_bytes(w.fmt, w.h)
+                 + (r_max * w.h * 2 if "expert_out" in inp else 0))
+    copies = args.copies or max(2, min(8, -(-(768 << 20) // max(set_bytes, 1)) + 1))
+    path = Path(moe, torch, w, inp, copies)
+    log(f"[bench] {copies} buffer sets of {set_bytes / 1e6:.1f} MB rotated")
+
+    ms, wall = time_steps(torch, path, args.steps, args.warmup)
+    log(f"[bench] timed {args.steps} steps: {ms * 1e3:.2f} us/step (wall {wall:.3f} s)")
+    kt = time_kernels(torch, path, args.steps)
+    log(f"[bench] per-kernel means (us): plan {kt['plan'] * 1e3:.2f} dispatch "
+        f"{kt['dispatch'] * 1e3:.2f} combine {kt['combine'] * 1e3:.2f}")
+    ru = path.r_used()
+    b = step_bytes(w, ru, r_max)
+    value = b["total"] / (ms * 1e-3) / 1e9
+
+    dom = "dispatch" if kt["dispatch"] >= kt["combine"] else "combine"
+    achieved = b[dom] / (kt[dom] * 1e-3) / 1e9
+    kname = {"dispatch": "dispatch_kernel", "combine": "combine_kernel"}[dom]
+    traffic = traffic_from_profile(w.name, kname, b[dom])
+    roofline = dict(bound="hbm", kernel=kname, achieved=round(achieved, 1),
+                    peak=PEAK_HBM_GBPS, unit="GB/s", frac=round(achieved / PEAK_HBM_GBPS, 4),
+                    traffic=traffic, algorithmic_bytes=b[dom],
+                    avg_launch_us=round(kt[dom] * 1e3, 2))
+
+    extra = {}
+    if not args.no_copy_ref:
+        extra["copy_ref_gbps"] = round(copy_reference(torch), 1)
+        log(f"[bench] 1 GiB device copy: {extra['copy_ref_gbps']} GB/s")
+    if not args.no_decode:
+        dw = WORKLOADS["decode_mxfp4_n128"]
+        dinp = make_inputs(dw, seed=0, expert_rows=dw.n * dw.k + dw.e * (dw.a - 1))
+        extra["decode"] = decode_latency(moe, torch, dw, dinp)
+        log(f"[bench] decode: {extra['decode']}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, inp, r_max)
+        log(f"[bench] cpu baseline: {cpu}")
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.fmt if w.fmt != "mxfp4" else "mxfp4",
+        "data": "synthetic",
+        "config": {"workload": w.name, "tokens": w.n, "hidden": w.h, "experts": w.e,
+                   "top_k": w.k, "ep_ranks_simulated": w.ep, "pad_multiple": w.a,
+                   "format": w.fmt, "routing": w.routing, "r_used": ru, "r_max": r_max,
+                   "buffer_sets": copies},
+        "frac_of_peak": round(value / PEAK_HBM_GBPS, 4),
+        "bytes_per_step": b,
+        "kernel_us": {k: round(v * 1e3, 2) for k, v in kt.items()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    rec.update(extra)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,41 @@
+"""Build libmoe.so (HIP, gfx950) in-tree with hipcc."""
+from __future__ import annotations
+
+import os
+import subprocess
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+LIB = os.path.join(PKG, "libmoe.so")
+SOURCES = ["api.hip", "plan.hip", "dispatch.hip", "combine.hip"]
+ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
+
+
+def hipcc_command(out: str) -> list[str]:
+    return [
+        "hipcc", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+        "-fvisibility=hidden",
+        # keep the compiler from emitting packed-fp32 VALU forms
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-Wall", "-Wno-unused-command-line-argument",
+        "-I", os.path.join(ROOT, "include"),
+        "-o", out,
+    ] + [os.path.join(CSRC, s) for s in SOURCES]
+
+
+def build(force: bool = True, verbose: bool = False) -> str:
+    """Compile every HIP source into combine_topk_ids_amd/libmoe.so."""
+    if not force and os.path.exists(LIB):
+        return LIB
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = hipcc_command(tmp)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.check_call(cmd, cwd=PKG)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(force=True, verbose=True))

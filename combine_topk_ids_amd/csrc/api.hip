@@ -1,0 +1,129 @@
+// api.hip -- the C ABI of libmoe: argument checks, sizes, and launches.
+// Declarations, argument meaning, layouts and error behaviour: include/moe.h.
+#include <stdint.h>
+
+#include "moe.h"
+#include "moe_kernels.hpp"
+
+namespace {
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int64_t max_rows_unchecked(const moe_problem &p) {
+  return p.n_tokens * p.top_k + static_cast<int64_t>(p.n_experts) * (p.pad_multiple - 1);
+}
+
+int check(const moe_problem *p) {
+  if (!p) return MOE_EINVAL;
+  if (p->n_tokens < 0 || p->hidden <= 0 || p->hidden % 8 != 0) return MOE_EINVAL;
+  if (p->n_experts < 1 || p->n_experts > moe::kMaxExperts) return MOE_EINVAL;
+  if (p->top_k < 1 || p->top_k > p->n_experts || p->top_k > moe::kMaxTopK) return MOE_EINVAL;
+  if (p->ep < 1 || p->n_experts % p->ep != 0) return MOE_EINVAL;
+  if (p->pad_multiple < 1 || p->recv_capacity < 0) return MOE_EINVAL;
+  if (p->flags & ~MOE_FLAG_ZERO_TAIL) return MOE_EINVAL;
+  switch (p->fmt) {
+    case MOE_FMT_BF16: break;
+    case MOE_FMT_FP8_E4M3_B128: if (p->hidden % 128 != 0) return MOE_EINVAL; break;
+    case MOE_FMT_MXFP4_B32: if (p->hidden % 32 != 0) return MOE_EINVAL; break;
+    default: return MOE_EINVAL;
+  }
+  // pair indices, rows and token*H offsets are int32 / uint32 on the device
+  if (p->n_tokens > INT32_MAX / p->top_k) return MOE_EOVERFLOW;
+  const int64_t r_max = max_rows_unchecked(*p);
+  if (r_max > INT32_MAX) return MOE_EOVERFLOW;
+  if (r_max * static_cast<int64_t>(p->hidden) >= (int64_t{1} << 32)) return MOE_EOVERFLOW;
+  if (p->n_tokens * static_cast<int64_t>(p->hidden) >= (int64_t{1} << 40)) return MOE_EOVERFLOW;
+  return MOE_OK;
+}
+
+int launched(hipError_t err) { return err == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+MOE_API int moe_check_problem(const moe_problem *p) { return check(p); }
+
+MOE_API int64_t moe_max_rows(const moe_problem *p) {
+  const int rc = check(p);
+  return rc != MOE_OK ? rc : max_rows_unchecked(*p);
+}
+
+MOE_API int64_t moe_payload_row_bytes(const moe_problem *p) {
+  const int rc = check(p);
+  if (rc != MOE_OK) return rc;
+  if (p->fmt == MOE_FMT_BF16) return 2 * static_cast<int64_t>(p->hidden);
+  if (p->fmt == MOE_FMT_FP8_E4M3_B128) return p->hidden;
+  return p->hidden / 2;
+}
+
+MOE_API int64_t moe_scale_row_bytes(const moe_problem *p) {
+  const int rc = check(p);
+  if (rc != MOE_OK) return rc;
+  if (p->fmt == MOE_FMT_BF16) return 0;
+  if (p->fmt == MOE_FMT_FP8_E4M3_B128) return 4 * static_cast<int64_t>(p->hidden / 128);
+  return p->hidden / 32;
+}
+
+MOE_API size_t moe_workspace_bytes(const moe_problem *p) {
+  if (check(p) != MOE_OK) return 0;
+  return moe::plan_workspace_bytes(*p);
+}
+
+MOE_API int moe_dispatch_plan(const moe_problem *p, const int32_t *topk_ids, const moe_plan *plan,
+                              void *workspace, void *stream) {
+  const int rc = check(p);
+  if (rc != MOE_OK) return rc;
+  if (!plan || !plan->expert_counts || !plan->expert_offsets || !plan->dest_counts ||
+      !plan->rank_table || !plan->status)
+    return MOE_EINVAL;
+  const int64_t npairs = p->n_tokens * p->top_k;
+  if (npairs > 0 && (!topk_ids || !plan->slot)) return MOE_EINVAL;
+  if (max_rows_unchecked(*p) > 0 && !plan->packed_src) return MOE_EINVAL;
+  if (moe::plan_workspace_bytes(*p) > 0 && !workspace) return MOE_EINVAL;
+  if (!aligned(topk_ids, 4) || !aligned(plan->expert_counts, 4) || !aligned(plan->expert_offsets, 4) ||
+      !aligned(plan->dest_counts, 4) || !aligned(plan->rank_table, 4) || !aligned(plan->slot, 4) ||
+      !aligned(plan->packed_src, 4) || !aligned(plan->status, 4) || !aligned(workspace, 256))
+    return MOE_EALIGN;
+  return launched(moe::launch_plan(*p, topk_ids, *plan, workspace, static_cast<hipStream_t>(stream)));
+}
+
+MOE_API int moe_dispatch(const moe_problem *p, const moe_plan *plan, const uint16_t *hidden,
+                         void *payload, void *scales, void *stream) {
+  const int rc = check(p);
+  if (rc != MOE_OK) return rc;
+  if (!plan || !plan->expert_counts || !plan->expert_offsets) return MOE_EINVAL;
+  if (p->n_tokens > 0 && (!hidden || !plan->slot)) return MOE_EINVAL;
+  const bool quant = p->fmt != MOE_FMT_BF16;
+  if (max_rows_unchecked(*p) > 0 && (!payload || (quant && !scales))) return MOE_EINVAL;
+  if (!quant && scales) return MOE_EINVAL;
+  if (!aligned(hidden, 16) || !aligned(payload, 16) || !aligned(plan->slot, 4) ||
+      !aligned(plan->expert_counts, 4) || !aligned(plan->expert_offsets, 4) ||
+      (p->fmt == MOE_FMT_FP8_E4M3_B128 && !aligned(scales, 4)))
+    return MOE_EALIGN;
+  return launched(moe::launch_dispatch(*p, *plan, hidden, payload, scales, static_cast<hipStream_t>(stream)));
+}
+
+MOE_API int moe_combine(const moe_problem *p, const moe_plan *plan, const uint16_t *expert_out,
+                        const float *topk_weights, uint16_t *out, void *stream) {
+  const int rc = check(p);
+  if (rc != MOE_OK) return rc;
+  if (!plan) return MOE_EINVAL;
+  if (p->n_tokens > 0 && (!expert_out || !topk_weights || !out || !plan->slot)) return MOE_EINVAL;
+  if (!aligned(expert_out, 16) || !aligned(out, 16) || !aligned(topk_weights, 4) || !aligned(plan->slot, 4))
+    return MOE_EALIGN;
+  return launched(moe::launch_combine(*p, *plan, expert_out, topk_weights, out, static_cast<hipStream_t>(stream)));
+}
+
+MOE_API const char *moe_strerror(int code) {
+  switch (code) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument (null pointer, shape or divisibility)";
+    case MOE_EALIGN: return "misaligned pointer (rows need 16 bytes, index arrays 4)";
+    case MOE_EOVERFLOW: return "problem too large for 32-bit row indices or element counts";
+    case MOE_EHIP: return "HIP launch error";
+    default: return "unknown error code";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,139 @@
+// combine.hip -- gather each token's expert outputs and sum them weighted by
+// the gate values.
+//
+// What is computed (pages cited by title and section):
+//   DeepSpeed v0.19.4 function index, page 15 -- the combine entry: expert
+//     results of each token are gathered back and weighted by gate values.
+//   NeMo Automodel token_dispatcher API -- token_unpermutation /
+//     combine_preprocess (restore the pre-expert token order),
+//     TokenDispatcherConfig.moe_router_dtype (weighted averaging in fp32).
+//   Mojo shmem ep_comm module -- router_weights_wrapper_type (one fp32 gate
+//     weight per (token, top-k slot)).
+//
+// out[t][c] = bf16_rne(acc), acc = +0 then acc = fma(w[t][j], Y[slot][c], acc)
+// for j = 0..k-1 in order, skipping masked slots: the same fp32 rounding
+// sequence on every element, so results do not depend on the launch shape.
+//
+// Design for gfx950.  One wave64 per token; each lane owns 8 consecutive
+// columns (one 16-byte bf16 vector) of two 512-column chunks at a time.  All
+// k row loads of a chunk pair are issued before the first FMA, so a wave
+// keeps k x 2 KiB in flight; gate weights and slots are wave-uniform scalar
+// loads.
+#include "moe_device.hpp"
+#include "moe_kernels.hpp"
+
+namespace moe {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kBatch = 8;  // top-k slots whose loads are issued together
+
+struct CombineArgs {
+  const uint16_t *y;
+  const int32_t *slot;
+  const float *w;
+  uint16_t *out;
+  int64_t n;
+  int k, h;
+};
+
+__device__ __forceinline__ void fma8(float (&acc)[8], float w, const u32x4 v) {
+  acc[0] = __builtin_fmaf(w, bf16_lo(v.x), acc[0]);
+  acc[1] = __builtin_fmaf(w, bf16_hi(v.x), acc[1]);
+  acc[2] = __builtin_fmaf(w, bf16_lo(v.y), acc[2]);
+  acc[3] = __builtin_fmaf(w, bf16_hi(v.y), acc[3]);
+  acc[4] = __builtin_fmaf(w, bf16_lo(v.z), acc[4]);
+  acc[5] = __builtin_fmaf(w, bf16_hi(v.z), acc[5]);
+  acc[6] = __builtin_fmaf(w, bf16_lo(v.w), acc[6]);
+  acc[7] = __builtin_fmaf(w, bf16_hi(v.w), acc[7]);
+}
+
+__device__ __forceinline__ u32x4 pack8(const float (&a)[8]) {
+  u32x4 r;
+  r.x = f32_to_bf16(a[0]) | (f32_to_bf16(a[1]) << 16);
+  r.y = f32_to_bf16(a[2]) | (f32_to_bf16(a[3]) << 16);
+  r.z = f32_to_bf16(a[4]) | (f32_to_bf16(a[5]) << 16);
+  r.w = f32_to_bf16(a[6]) | (f32_to_bf16(a[7]) << 16);
+  return r;
+}
+
+// KC > 0: k is the compile-time constant KC; KC == 0: runtime k, in batches.
+template <int KC>
+__global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs g) {
+  constexpr int U = 2;  // 16-byte vectors per lane per step
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
+  if (t >= g.n) return;
+  const int lane = lane_id();
+  const int k = KC > 0 ? KC : g.k;
+  const int nvec = g.h / 8;
+  const int32_t *sl = g.slot + t * k;
+  const float *wt = g.w + t * k;
+  const u32x4 *ybase = reinterpret_cast<const u32x4 *>(g.y);
+  u32x4 *dst = reinterpret_cast<u32x4 *>(g.out + t * g.h);
+  for (int v0 = 0; v0 < nvec; v0 += kWave * U) {
+    float acc[U][8];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[u][i] = 0.0f;
+    constexpr int KB = KC > 0 ? KC : kBatch;
+    for (int j0 = 0; j0 < k; j0 += KB) {
+      u32x4 v[KB][U];
+      int s[KB];
+#pragma unroll
+      for (int jj = 0; jj < KB; ++jj) {
+        s[jj] = (KC > 0 || j0 + jj < k) ? sl[j0 + jj] : -1;
+        const int64_t row = s[jj] >= 0 ? s[jj] : 0;  // masked: harmless in-bounds read
+        const u32x4 *src = ybase + row * nvec;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int idx = v0 + u * kWave + lane;
+          if (idx < nvec) v[jj][u] = __builtin_nontemporal_load(src + idx);
+        }
+      }
+#pragma unroll
+      for (int jj = 0; jj < KB; ++jj) {
+        if (s[jj] < 0) continue;
+        const float wj = wt[j0 + jj];
+#pragma unroll
+        for (int u = 0; u < U; ++u) fma8(acc[u], wj, v[jj][u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int idx = v0 + u * kWave + lane;
+      if (idx < nvec) __builtin_nontemporal_store(pack8(acc[u]), dst + idx);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const moe_problem &p, const moe_plan &plan, const uint16_t *expert_out,
+                          const float *weights, uint16_t *out, hipStream_t stream) {
+  CombineArgs g;
+  g.y = expert_out;
+  g.slot = plan.slot;
+  g.w = weights;
+  g.out = out;
+  g.n = p.n_tokens;
+  g.k = p.top_k;
+  g.h = p.hidden;
+  const int grid = static_cast<int>((p.n_tokens + kWaves - 1) / kWaves);
+  if (grid == 0) return hipSuccess;
+  switch (p.top_k) {
+    case 1: combine_kernel<1><<<grid, kThreads, 0, stream>>>(g); break;
+    case 2: combine_kernel<2><<<grid, kThreads, 0, stream>>>(g); break;
+    case 4: combine_kernel<4><<<grid, kThreads, 0, stream>>>(g); break;
+    case 6: combine_kernel<6><<<grid, kThreads, 0, stream>>>(g); break;
+    case 8: combine_kernel<8><<<grid, kThreads, 0, stream>>>(g); break;
+    default: combine_kernel<0><<<grid, kThreads, 0, stream>>>(g); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

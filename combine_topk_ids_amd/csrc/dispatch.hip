@@ -1,0 +1,292 @@
+// dispatch.hip -- pack token rows into the expert-major buffer, optionally
+// quantising them on the way.
+//
+// What is computed (pages cited by title and section):
+//   NKI permute_a2av API reference -- description and :return: (rows packed
+//     per destination, then deterministic zero padding).
+//   NeMo Automodel token_dispatcher API -- get_permuted_hidden_states_by_experts
+//     (rows permuted into expert order by a fused kernel),
+//     TokenDispatcherConfig.moe_router_expert_pad_multiple (pad rows).
+//   Mojo shmem ep_comm module -- BF16TokenFormat (rows carried in bf16),
+//     BlockwiseFP8TokenFormat (FP8 with one scale per block),
+//     MXTokenFormat (MX FP4), EP_COPY_SRC_WIDTH (8 source elements per
+//     thread per copy item), block_memcpy (vector loads and stores).
+//   Formats: OCP 8-bit Floating Point (E4M3) and OCP MX v1.0 (E2M1, E8M0),
+//     with the per-1x128 amax/448 fp32 scale of the FP8 recipe.
+//
+// Design for gfx950.  Token-stationary: one wave64 owns one token, reads its
+// row once with 16-byte loads (8 bf16 per lane, 1 KiB per wave instruction),
+// encodes it once, and writes the result to each of its k packed rows, so
+// the cost does not depend on how skewed the routing is.  FP8 block maxima
+// are a 16-lane DPP row reduction (one 1x128 block = 16 lanes x 8 values);
+// MX block maxima a 4-lane quad reduction.  Pad rows are zeroed by a second
+// range of workgroups in the same launch, the optional tail by a third.
+#include "moe_device.hpp"
+#include "moe_kernels.hpp"
+
+namespace moe {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kPadRowsPerWave = 4;
+constexpr int kTailBlocks = 512;
+
+struct DispatchArgs {
+  const uint16_t *x;
+  const int32_t *slot;
+  const int32_t *counts;
+  const int32_t *offsets;
+  uint8_t *payload;
+  uint8_t *scales;
+  int64_t n;
+  int64_t r_max;
+  int64_t row_bytes;    // payload bytes per packed row
+  int64_t scale_bytes;  // scale bytes per packed row
+  int k, h, e;
+  int token_blocks, pad_blocks, tail_blocks;
+  int pad_groups;  // pad-row groups of kPadRowsPerWave per expert
+};
+
+template <bool NT, typename V>
+__device__ __forceinline__ void store(V *p, V v) {
+  if (NT)
+    __builtin_nontemporal_store(v, p);
+  else
+    *p = v;
+}
+
+// ---- bf16: copy the row to every destination ------------------------------
+template <bool NT>
+__device__ void token_bf16(const DispatchArgs &g, int64_t t) {
+  constexpr int U = 8;  // 16-byte vectors per lane in flight
+  const int lane = lane_id();
+  const int nvec = g.h / 8;
+  const u32x4 *src = reinterpret_cast<const u32x4 *>(g.x + t * g.h);
+  const int32_t *sl = g.slot + t * g.k;
+  for (int v0 = 0; v0 < nvec; v0 += kWave * U) {
+    u32x4 buf[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int idx = v0 + u * kWave + lane;
+      if (idx < nvec) buf[u] = __builtin_nontemporal_load(src + idx);
+    }
+    for (int j = 0; j < g.k; ++j) {
+      const int s = sl[j];
+      if (s < 0) continue;
+      u32x4 *dst = reinterpret_cast<u32x4 *>(g.payload + static_cast<int64_t>(s) * g.row_bytes);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int idx = v0 + u * kWave + lane;
+        if (idx < nvec) store<NT>(dst + idx, buf[u]);
+      }
+    }
+  }
+}
+
+// ---- FP8 E4M3, one fp32 scale per 1x128 block -------------------------------
+template <bool NT>
+__device__ void token_fp8(const DispatchArgs &g, int64_t t) {
+  constexpr int U = 4;  // 512-element chunks per batch
+  const int lane = lane_id();
+  const int nchunk = (g.h + 511) / 512;
+  const u32x4 *src = reinterpret_cast<const u32x4 *>(g.x + t * g.h);
+  const int32_t *sl = g.slot + t * g.k;
+  const int sblocks = g.h / 128;
+  for (int c0 = 0; c0 < nchunk; c0 += U) {
+    u32x4 raw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int elem = (c0 + u) * 512 + lane * 8;
+      raw[u] = elem < g.h ? __builtin_nontemporal_load(src + elem / 8) : u32x4{0u, 0u, 0u, 0u};
+    }
+    u32x2 codes[U];
+    float scale[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float f[8];
+      uint4 r4;
+      r4.x = raw[u].x; r4.y = raw[u].y; r4.z = raw[u].z; r4.w = raw[u].w;
+      unpack8(r4, f);
+      uint32_t am = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) am = max(am, __float_as_uint(f[i]) & 0x7FFFFFFFu);
+      am = row16_max(am);
+      const float s = __uint_as_float(am) / 448.0f;
+      uint32_t b[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) b[i] = s == 0.0f ? 0u : e4m3_rne_sat(f[i] / s);
+      codes[u].x = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
+      codes[u].y = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
+      scale[u] = s;
+    }
+    for (int j = 0; j < g.k; ++j) {
+      const int s = sl[j];
+      if (s < 0) continue;
+      uint8_t *prow = g.payload + static_cast<int64_t>(s) * g.row_bytes;
+      float *srow = reinterpret_cast<float *>(g.scales + static_cast<int64_t>(s) * g.scale_bytes);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int elem = (c0 + u) * 512 + lane * 8;
+        if (elem < g.h) {
+          store<NT>(reinterpret_cast<u32x2 *>(prow + elem), codes[u]);
+          if ((lane & 15) == 0) store<NT>(srow + elem / 128, scale[u]);
+        }
+      }
+    }
+  }
+  (void)sblocks;
+}
+
+// ---- MX-FP4: E2M1 codes, one E8M0 scale per 32 values -----------------------
+template <bool NT>
+__device__ void token_mx(const DispatchArgs &g, int64_t t) {
+  constexpr int U = 4;
+  const int lane = lane_id();
+  const int nchunk = (g.h + 511) / 512;
+  const u32x4 *src = reinterpret_cast<const u32x4 *>(g.x + t * g.h);
+  const int32_t *sl = g.slot + t * g.k;
+  for (int c0 = 0; c0 < nchunk; c0 += U) {
+    u32x4 raw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int elem = (c0 + u) * 512 + lane * 8;
+      raw[u] = elem < g.h ? __builtin_nontemporal_load(src + elem / 8) : u32x4{0u, 0u, 0u, 0u};
+    }
+    uint32_t word[U];
+    uint32_t sbyte[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float f[8];
+      uint4 r4;
+      r4.x = raw[u].x; r4.y = raw[u].y; r4.z = raw[u].z; r4.w = raw[u].w;
+      unpack8(r4, f);
+      uint32_t am = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) am = max(am, __float_as_uint(f[i]) & 0x7FFFFFFFu);
+      am = quad_max(am);
+      const int X = mx_exponent(am);
+      const float mul = __uint_as_float(static_cast<uint32_t>(127 - X) << 23);  // 2^-X
+      uint32_t w = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w |= e2m1_rne_sat(f[i] * mul) << (4 * i);
+      word[u] = am == 0 ? 0u : w;
+      sbyte[u] = am == 0 ? 0u : static_cast<uint32_t>(X + 127);
+    }
+    for (int j = 0; j < g.k; ++j) {
+      const int s = sl[j];
+      if (s < 0) continue;
+      uint8_t *prow = g.payload + static_cast<int64_t>(s) * g.row_bytes;
+      uint8_t *srow = g.scales + static_cast<int64_t>(s) * g.scale_bytes;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int elem = (c0 + u) * 512 + lane * 8;
+        if (elem < g.h) {
+          store<NT>(reinterpret_cast<uint32_t *>(prow + elem / 2), word[u]);
+          if ((lane & 3) == 0) store<NT>(srow + elem / 32, static_cast<uint8_t>(sbyte[u]));
+        }
+      }
+    }
+  }
+}
+
+// ---- zero fill of one packed row (payload and scales) -----------------------
+template <bool NT>
+__device__ void zero_row(const DispatchArgs &g, int64_t r) {
+  const int lane = lane_id();
+  u32x4 *p = reinterpret_cast<u32x4 *>(g.payload + r * g.row_bytes);
+  const int nvec = static_cast<int>(g.row_bytes / 16);
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  for (int i = lane; i < nvec; i += kWave) store<NT>(p + i, z);
+  if (g.scale_bytes) {
+    uint8_t *s = g.scales + r * g.scale_bytes;
+    if ((g.scale_bytes & 3) == 0) {
+      uint32_t *s4 = reinterpret_cast<uint32_t *>(s);
+      for (int i = lane; i < g.scale_bytes / 4; i += kWave) store<NT>(s4 + i, 0u);
+    } else {
+      for (int i = lane; i < g.scale_bytes; i += kWave) store<NT>(s + i, static_cast<uint8_t>(0));
+    }
+  }
+}
+
+template <int FMT, bool NT>
+__global__ __launch_bounds__(kThreads) void dispatch_kernel(DispatchArgs g) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  int blk = blockIdx.x;
+  if (blk < g.token_blocks) {
+    const int64_t t = static_cast<int64_t>(blk) * kWaves + wave;
+    if (t >= g.n) return;
+    if (FMT == MOE_FMT_BF16) token_bf16<NT>(g, t);
+    else if (FMT == MOE_FMT_FP8_E4M3_B128) token_fp8<NT>(g, t);
+    else token_mx<NT>(g, t);
+    return;
+  }
+  blk -= g.token_blocks;
+  if (blk < g.pad_blocks) {
+    const int q = blk * kWaves + wave;
+    const int e = q / g.pad_groups;
+    if (e >= g.e) return;
+    const int grp = q - e * g.pad_groups;
+    const int lo = g.offsets[e] + g.counts[e];
+    const int hi = g.offsets[e + 1];
+    const int r0 = lo + grp * kPadRowsPerWave;
+    const int r1 = min(r0 + kPadRowsPerWave, hi);
+    for (int r = r0; r < r1; ++r) zero_row<NT>(g, r);
+    return;
+  }
+  blk -= g.pad_blocks;
+  // optional tail [R_used, R_max)
+  const int64_t used = g.offsets[g.e];
+  const int64_t stride = static_cast<int64_t>(g.tail_blocks) * kWaves;
+  for (int64_t r = used + static_cast<int64_t>(blk) * kWaves + wave; r < g.r_max; r += stride)
+    zero_row<NT>(g, r);
+}
+
+template <int FMT>
+void launch_fmt(const DispatchArgs &g, int grid, hipStream_t stream) {
+  dispatch_kernel<FMT, false><<<grid, kThreads, 0, stream>>>(g);
+}
+
+}  // namespace
+
+hipError_t launch_dispatch(const moe_problem &p, const moe_plan &plan, const uint16_t *hidden,
+                           void *payload, void *scales, hipStream_t stream) {
+  DispatchArgs g;
+  g.x = hidden;
+  g.slot = plan.slot;
+  g.counts = plan.expert_counts;
+  g.offsets = plan.expert_offsets;
+  g.payload = static_cast<uint8_t *>(payload);
+  g.scales = static_cast<uint8_t *>(scales);
+  g.n = p.n_tokens;
+  g.r_max = p.n_tokens * p.top_k + static_cast<int64_t>(p.n_experts) * (p.pad_multiple - 1);
+  g.k = p.top_k;
+  g.h = p.hidden;
+  g.e = p.n_experts;
+  if (p.fmt == MOE_FMT_BF16) {
+    g.row_bytes = 2 * static_cast<int64_t>(p.hidden);
+    g.scale_bytes = 0;
+  } else if (p.fmt == MOE_FMT_FP8_E4M3_B128) {
+    g.row_bytes = p.hidden;
+    g.scale_bytes = 4 * static_cast<int64_t>(p.hidden / 128);
+  } else {
+    g.row_bytes = p.hidden / 2;
+    g.scale_bytes = p.hidden / 32;
+  }
+  g.token_blocks = static_cast<int>((p.n_tokens + kWaves - 1) / kWaves);
+  g.pad_groups = (p.pad_multiple - 1 + kPadRowsPerWave - 1) / kPadRowsPerWave;
+  g.pad_blocks = g.pad_groups == 0 ? 0 : (p.n_experts * g.pad_groups + kWaves - 1) / kWaves;
+  if (g.pad_groups == 0) g.pad_groups = 1;  // keep the division in the kernel defined
+  g.tail_blocks = (p.flags & MOE_FLAG_ZERO_TAIL) && g.r_max > 0 ? kTailBlocks : 0;
+  const int grid = g.token_blocks + g.pad_blocks + g.tail_blocks;
+  if (grid == 0) return hipSuccess;
+  if (p.fmt == MOE_FMT_BF16) launch_fmt<MOE_FMT_BF16>(g, grid, stream);
+  else if (p.fmt == MOE_FMT_FP8_E4M3_B128) launch_fmt<MOE_FMT_FP8_E4M3_B128>(g, grid, stream);
+  else launch_fmt<MOE_FMT_MXFP4_B32>(g, grid, stream);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,142 @@
+// moe_device.hpp -- wave64 helpers and number-format conversions shared by
+// the plan, dispatch and combine kernels (gfx950, CDNA4).
+//
+// Format rules implemented here (all round to nearest, ties to even):
+//   bf16   from fp32: IEEE rounding of the low 16 bits (bias-add form).
+//   E4M3   OCP 8-bit floating point, 4 exponent bits (bias 7), 3 mantissa
+//          bits, largest finite 448, no infinities; values past 448 saturate.
+//   E2M1   OCP MX v1.0 element: magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6;
+//          saturating at 6.
+//   E8M0   OCP MX v1.0 shared scale: X = floor(log2 amax) - 2 (2 is the
+//          largest E2M1 exponent), stored as X + 127.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- waves ---
+
+__device__ __forceinline__ int lane_id() {
+  return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
+
+// Number of set bits of `m` in lanes below this one.
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+}
+
+__device__ __forceinline__ uint64_t ballot(bool p) {
+  return static_cast<uint64_t>(__ballot(p));
+}
+
+// Lanes of `active` holding the same key as this lane (keys < 2^bits).  One
+// ballot per key bit: a lane survives bit b if its bit matches ours.
+__device__ __forceinline__ uint64_t match_any(uint32_t key, int bits, uint64_t active) {
+  uint64_t m = active;
+  for (int b = 0; b < bits; ++b) {
+    const bool set = (key >> b) & 1u;
+    const uint64_t ones = ballot(set);
+    m &= set ? ones : ~ones;
+  }
+  return m;
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false));
+}
+
+// DPP controls (gfx9): quad_perm [1,0,3,2], quad_perm [2,3,0,1],
+// row_half_mirror (lane i <- 7-i within 8), row_mirror (i <- 15-i within 16).
+constexpr int kQuadSwap1 = 0xB1;
+constexpr int kQuadSwap2 = 0x4E;
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+
+// Maximum over the 4 lanes of a quad (unsigned compare).
+__device__ __forceinline__ uint32_t quad_max(uint32_t v) {
+  v = max(v, dpp<kQuadSwap1>(v));
+  v = max(v, dpp<kQuadSwap2>(v));
+  return v;
+}
+
+// Maximum over the 16 lanes of a DPP row (unsigned compare).
+__device__ __forceinline__ uint32_t row16_max(uint32_t v) {
+  v = quad_max(v);
+  v = max(v, dpp<kRowHalfMirror>(v));
+  v = max(v, dpp<kRowMirror>(v));
+  return v;
+}
+
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int u = __shfl_up(v, d, kWave);
+    if (lane >= d) v += u;
+  }
+  return v;
+}
+
+// ---------------------------------------------------------------- bf16 ---
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;  // keep NaN a NaN
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ void unpack8(const uint4 v, float (&f)[8]) {
+  f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
+  f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+  f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
+  f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+}
+
+// ---------------------------------------------------------------- E4M3 ---
+
+// |v| is at most a hair above 448 here (v = x / (amax/448)).
+__device__ __forceinline__ uint32_t e4m3_rne_sat(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  uint32_t code;
+  if (a >= 0x43E00000u) {            // |v| >= 448: largest finite code
+    code = 0x7Eu;
+  } else if (a < 0x3C800000u) {      // |v| < 2^-6: subnormal codes, step 2^-9
+    code = static_cast<uint32_t>(__builtin_rintf(__uint_as_float(a) * 512.0f));
+  } else {                           // normal: keep 3 mantissa bits
+    const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
+    code = (r >> 20) - (120u << 3);  // exponent bias 127 -> 7
+  }
+  return sign | code;
+}
+
+// ---------------------------------------------------------------- E2M1 ---
+
+// Midpoints between neighbouring E2M1 magnitudes; a tie goes to the even
+// code, hence the alternation of > and >=.
+__device__ __forceinline__ uint32_t e2m1_rne_sat(float v) {
+  const float a = fabsf(v);
+  const uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) +
+                     (a > 2.5f) + (a >= 3.5f) + (a > 5.0f);
+  return c | ((__float_as_uint(v) >> 28) & 8u);
+}
+
+// E8M0 exponent X of a block with maximum magnitude bits `amax_bits` > 0:
+// floor(log2 amax) - 2, clamped below at -127 (subnormal maxima land there).
+__device__ __forceinline__ int mx_exponent(uint32_t amax_bits) {
+  return max(static_cast<int>(amax_bits >> 23) - 129, -127);
+}
+
+}  // namespace moe

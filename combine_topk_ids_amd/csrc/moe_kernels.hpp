@@ -1,0 +1,39 @@
+// moe_kernels.hpp -- launchers behind the C ABI (internal to libmoe).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 64;
+constexpr int kPlanThreads = 256;          // 4 waves
+constexpr int kPlanWaves = kPlanThreads / 64;
+constexpr int64_t kSingleBlockPairs = 4096;  // plans this small run in one block
+constexpr int kMaxTiles = 64;              // tiles of the two-kernel plan
+
+// How the (token, k) pairs are split into tiles for the plan kernels.
+struct PlanGeom {
+  int64_t npairs;      // N * k
+  int64_t tile_pairs;  // pairs per tile (a multiple of kPlanThreads)
+  int ntiles;          // ceil(npairs / tile_pairs), >= 1
+  bool single;         // one block does count, scan and assignment
+  int key_bits;        // bits needed for an expert id (ceil(log2 E))
+};
+
+PlanGeom plan_geometry(const moe_problem &p);
+size_t plan_workspace_bytes(const moe_problem &p);
+
+hipError_t launch_plan(const moe_problem &p, const int32_t *ids, const moe_plan &plan,
+                       void *workspace, hipStream_t stream);
+
+hipError_t launch_dispatch(const moe_problem &p, const moe_plan &plan, const uint16_t *hidden,
+                           void *payload, void *scales, hipStream_t stream);
+
+hipError_t launch_combine(const moe_problem &p, const moe_plan &plan, const uint16_t *expert_out,
+                          const float *weights, uint16_t *out, hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,227 @@
+"""ctypes binding of libmoe (HIP, gfx950): MoE dispatch plan, dispatch, combine.
+
+Argument marshalling only: every step of the path runs in libmoe's kernels.
+PyTorch supplies device memory (tensors' ``data_ptr()``) and the stream
+(``torch.cuda.current_stream()``).  The C ABI, with the meaning, layout and
+error behaviour of every argument, is ``include/moe.h``; the functions here
+carry the same names.
+
+Importing this module loads ``libmoe.so`` and fails loudly if it has not been
+built (``python -m combine_topk_ids_amd._build``); there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+
+import torch  # first: libmoe then binds to the HIP runtime torch has loaded
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+
+MOE_OK, MOE_EINVAL, MOE_EALIGN, MOE_EOVERFLOW, MOE_EHIP = 0, -1, -2, -3, -4
+STATUS_BAD_ID, STATUS_DUP_ID, STATUS_CAPACITY = 1, 2, 4
+FMT = {"bf16": 0, "fp8": 1, "mxfp4": 2}
+FLAG_ZERO_TAIL = 1
+
+# every symbol include/moe.h declares
+EXPORTS = ("moe_check_problem", "moe_max_rows", "moe_payload_row_bytes",
+           "moe_scale_row_bytes", "moe_workspace_bytes", "moe_dispatch_plan",
+           "moe_dispatch", "moe_combine", "moe_strerror")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__(f"{where}: {strerror(code)} (code {code})")
+        self.code = code
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("n_tokens", ctypes.c_int64), ("hidden", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("n_experts", ctypes.c_int32),
+                ("ep", ctypes.c_int32), ("recv_capacity", ctypes.c_int64),
+                ("pad_multiple", ctypes.c_int32), ("fmt", ctypes.c_int32),
+                ("flags", ctypes.c_uint32)]
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in (
+        "expert_counts", "expert_offsets", "dest_counts", "rank_table", "slot",
+        "packed_src", "status")]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m combine_topk_ids_amd._build` "
+            "(there is no CPU fallback)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, V = ctypes.POINTER(Problem), ctypes.c_void_p
+    sig = {
+        "moe_check_problem": (ctypes.c_int, [P]),
+        "moe_max_rows": (ctypes.c_int64, [P]),
+        "moe_payload_row_bytes": (ctypes.c_int64, [P]),
+        "moe_scale_row_bytes": (ctypes.c_int64, [P]),
+        "moe_workspace_bytes": (ctypes.c_size_t, [P]),
+        "moe_dispatch_plan": (ctypes.c_int, [P, V, ctypes.POINTER(Plan), V, V]),
+        "moe_dispatch": (ctypes.c_int, [P, ctypes.POINTER(Plan), V, V, V, V]),
+        "moe_combine": (ctypes.c_int, [P, ctypes.POINTER(Plan), V, V, V, V]),
+        "moe_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype, fn.argtypes = res, args
+    return lib
+
+
+lib = _load()
+
+
+def strerror(code: int) -> str:
+    return lib.moe_strerror(code).decode()
+
+
+def problem(n_tokens: int, hidden: int, top_k: int, n_experts: int, ep: int,
+            recv_capacity: int | None = None, pad_multiple: int = 1,
+            fmt: str = "bf16", zero_tail: bool = False) -> Problem:
+    """Build a moe_problem; recv_capacity None means the dropless bound."""
+    if recv_capacity is None:
+        recv_capacity = n_tokens * min(top_k, n_experts // max(ep, 1))
+    return Problem(n_tokens, hidden, top_k, n_experts, ep, recv_capacity,
+                   pad_multiple, FMT[fmt], FLAG_ZERO_TAIL if zero_tail else 0)
+
+
+def _checked(value: int, where: str) -> int:
+    if value < 0:
+        raise MoeError(value, where)
+    return int(value)
+
+
+def moe_check_problem(p: Problem) -> int:
+    return int(lib.moe_check_problem(ctypes.byref(p)))
+
+
+def moe_max_rows(p: Problem) -> int:
+    return _checked(lib.moe_max_rows(ctypes.byref(p)), "moe_max_rows")
+
+
+def moe_payload_row_bytes(p: Problem) -> int:
+    return _checked(lib.moe_payload_row_bytes(ctypes.byref(p)), "moe_payload_row_bytes")
+
+
+def moe_scale_row_bytes(p: Problem) -> int:
+    return _checked(lib.moe_scale_row_bytes(ctypes.byref(p)), "moe_scale_row_bytes")
+
+
+def moe_workspace_bytes(p: Problem) -> int:
+    return int(lib.moe_workspace_bytes(ctypes.byref(p)))
+
+
+@dataclasses.dataclass
+class PlanBuffers:
+    """Device tensors a plan is written to, plus the plan kernels' workspace."""
+    expert_counts: torch.Tensor
+    expert_offsets: torch.Tensor
+    dest_counts: torch.Tensor
+    rank_table: torch.Tensor
+    slot: torch.Tensor
+    packed_src: torch.Tensor
+    status: torch.Tensor
+    workspace: torch.Tensor
+
+    def as_struct(self) -> Plan:
+        return Plan(*(getattr(self, f).data_ptr() for f, _ in Plan._fields_))
+
+    def read_status(self) -> int:
+        """Synchronises the current stream and returns the status bits."""
+        return int(self.status.item())
+
+
+def alloc_plan(p: Problem, device="cuda") -> PlanBuffers:
+    r_max = moe_max_rows(p)
+    i32 = dict(dtype=torch.int32, device=device)
+    return PlanBuffers(
+        expert_counts=torch.empty(p.n_experts, **i32),
+        expert_offsets=torch.empty(p.n_experts + 1, **i32),
+        dest_counts=torch.empty(p.ep, **i32),
+        rank_table=torch.empty((4, p.ep), **i32),  # uint32 bits in int32 storage
+        slot=torch.empty((p.n_tokens, p.top_k), **i32),
+        packed_src=torch.empty(max(r_max, 1), **i32),
+        status=torch.empty(1, **i32),
+        workspace=torch.empty(max(moe_workspace_bytes(p), 256), dtype=torch.uint8,
+                              device=device),
+    )
+
+
+def alloc_payload(p: Problem, device="cuda"):
+    """(payload, scales) device tensors of R_max rows for p.fmt."""
+    r_max = moe_max_rows(p)
+    h = p.hidden
+    if p.fmt == FMT["bf16"]:
+        return torch.empty((r_max, h), dtype=torch.bfloat16, device=device), None
+    if p.fmt == FMT["fp8"]:
+        return (torch.empty((r_max, h), dtype=torch.uint8, device=device),
+                torch.empty((r_max, h // 128), dtype=torch.float32, device=device))
+    return (torch.empty((r_max, h // 2), dtype=torch.uint8, device=device),
+            torch.empty((r_max, h // 32), dtype=torch.uint8, device=device))
+
+
+def _dev(t: torch.Tensor | None, name: str, dtypes, numel: int | None = None) -> int:
+    if t is None:
+        return 0
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} has {t.numel()} elements, needs {numel}")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def moe_dispatch_plan(p: Problem, topk_ids: torch.Tensor, plan: PlanBuffers, stream=None) -> None:
+    ids = _dev(topk_ids, "topk_ids", (torch.int32,), p.n_tokens * p.top_k)
+    _dev(plan.slot, "plan.slot", (torch.int32,), p.n_tokens * p.top_k)
+    _dev(plan.packed_src, "plan.packed_src", (torch.int32,), moe_max_rows(p))
+    _dev(plan.workspace, "plan.workspace", (torch.uint8,), moe_workspace_bytes(p))
+    pl = plan.as_struct()
+    rc = lib.moe_dispatch_plan(ctypes.byref(p), ids, ctypes.byref(pl),
+                               plan.workspace.data_ptr(), _stream(stream))
+    _checked(rc, "moe_dispatch_plan")
+
+
+def moe_dispatch(p: Problem, plan: PlanBuffers, hidden: torch.Tensor, payload: torch.Tensor,
+                 scales: torch.Tensor | None, stream=None) -> None:
+    r_max = moe_max_rows(p)
+    x = _dev(hidden, "hidden", _BF16, p.n_tokens * p.hidden)
+    pb = moe_payload_row_bytes(p)
+    sb = moe_scale_row_bytes(p)
+    if payload.numel() * payload.element_size() < r_max * pb:
+        raise ValueError("payload is smaller than R_max rows")
+    if scales is not None and scales.numel() * scales.element_size() < r_max * sb:
+        raise ValueError("scales is smaller than R_max rows")
+    pay = _dev(payload, "payload", (torch.bfloat16, torch.int16, torch.uint16, torch.uint8,
+                                    torch.float8_e4m3fn))
+    sc = _dev(scales, "scales", (torch.float32, torch.uint8))
+    pl = plan.as_struct()
+    rc = lib.moe_dispatch(ctypes.byref(p), ctypes.byref(pl), x, pay, sc or None, _stream(stream))
+    _checked(rc, "moe_dispatch")
+
+
+def moe_combine(p: Problem, plan: PlanBuffers, expert_out: torch.Tensor,
+                topk_weights: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+    y = _dev(expert_out, "expert_out", _BF16, moe_max_rows(p) * p.hidden)
+    w = _dev(topk_weights, "topk_weights", (torch.float32,), p.n_tokens * p.top_k)
+    o = _dev(out, "out", _BF16, p.n_tokens * p.hidden)
+    pl = plan.as_struct()
+    rc = lib.moe_combine(ctypes.byref(p), ctypes.byref(pl), y, w, o, _stream(stream))
+    _checked(rc, "moe_combine")

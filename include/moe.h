@@ -1,0 +1,193 @@
+/*
+ * moe.h -- C ABI of libmoe: MoE token dispatch and combine on one AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The library turns top-k expert IDs into a routing plan, packs token rows
+ * into an expert-major buffer (optionally quantised to blockwise FP8 or
+ * MX-FP4 on the way) and combines expert outputs back into token order,
+ * weighted by the gate values.  Expert-parallel destination ranks are
+ * simulated as contiguous segments of the one packed buffer.
+ *
+ * Conventions for every entry point
+ *   - Pointers named in a moe_plan, and every data pointer argument, are
+ *     DEVICE pointers the caller allocated; the library never allocates,
+ *     frees or synchronises, and keeps no state between calls.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued on it and the call returns at once; no host wait is
+ *     made, so the calls can be captured into a HIP graph.
+ *   - Return value: MOE_OK (0) or a negative MOE_E* code.  On an error
+ *     nothing has been launched.  No C++ exception crosses this ABI.
+ *   - Data-dependent faults (IDs out of range, repeated IDs within a token,
+ *     a destination rank over recv_capacity) never fail a call: they set
+ *     bits in plan->status on the device, and every row is still placed
+ *     inside the static buffer (out-of-range IDs are treated as masked).
+ *   - Calls on one stream are ordered; calls that share output buffers on
+ *     different streams race, as with any kernel.
+ *
+ * Passages followed (pages cited by title and section):
+ *   NKI permute_a2av API reference: description (rows packed per destination
+ *     at cumsum(send_counts) offsets; a (4, EP) uint32 table of send counts,
+ *     send displacements, receive counts and receive displacements, in
+ *     elements), :param packed_source_indices: (int32 source rows in [0, N),
+ *     destination-major), :param recv_capacity: (dropless bound
+ *     N * min(top_k, L); duplicate IDs void it), :return: (packed rows, then
+ *     deterministic zero padding).
+ *   NeMo Automodel token_dispatcher API: dispatch_preprocess2 (compact
+ *     token_indices[T, K] and token_probs[T, K]), dispatch_postprocess (rows
+ *     permuted by expert plus tokens per expert), _indices_to_multihot (-1
+ *     masks a slot), TokenDispatcherConfig.moe_router_expert_pad_multiple and
+ *     .moe_router_dtype (fp32 weighted averaging).
+ *   Mojo ep.dispatch_async.block.scaled.nv struct: execute (input_tokens
+ *     [num_tokens, hidden_size], topk_ids [num_tokens, top_k]).
+ *   Mojo shmem ep_comm module: BF16TokenFormat, BlockwiseFP8TokenFormat,
+ *     MXTokenFormat, router_weights_wrapper_type (fp32 gate weight per
+ *     (token, k)).
+ *   DeepSpeed v0.19.4 function index, page 15: the combine entry (gather
+ *     expert results back, weight by gate values) and the SplitPlan entry
+ *     (per-expert histogram as an [ep_size, E_local] matrix).
+ *   Formats: OCP 8-bit Floating Point Specification (E4M3, max 448, no
+ *     infinities) and OCP Microscaling Formats v1.0 (E2M1 elements, E8M0
+ *     scale, X = floor(log2 amax) - 2).
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_API __attribute__((visibility("default")))
+
+/* ---- return codes ------------------------------------------------------ */
+#define MOE_OK 0
+#define MOE_EINVAL (-1)    /* null pointer, bad shape or divisibility       */
+#define MOE_EALIGN (-2)    /* a row pointer is not 16-byte aligned          */
+#define MOE_EOVERFLOW (-3) /* R_max*H >= 2^32 (table) or rows >= 2^31       */
+#define MOE_EHIP (-4)      /* the HIP runtime reported a launch error       */
+
+/* ---- bits of plan->status (device, written by moe_dispatch_plan) ------- */
+#define MOE_STATUS_BAD_ID 1u   /* an ID outside [-1, E): treated as masked   */
+#define MOE_STATUS_DUP_ID 2u   /* an ID repeated within one token: routed    */
+#define MOE_STATUS_CAPACITY 4u /* some rank receives more than recv_capacity */
+
+/* ---- payload formats ---------------------------------------------------- */
+typedef enum moe_fmt {
+  /* bf16 rows copied bit for bit: payload uint16 [R_max][H], no scales.   */
+  MOE_FMT_BF16 = 0,
+  /* OCP E4M3 codes, one fp32 scale s = amax/448 per 1x128 block, code =
+   * E4M3(x / s) rounded to nearest even and saturated; an all-zero block
+   * has s = 0 and zero codes.  payload uint8 [R_max][H],
+   * scales float [R_max][H/128].  Needs H % 128 == 0.                     */
+  MOE_FMT_FP8_E4M3_B128 = 1,
+  /* OCP MX-FP4: E2M1 codes with one E8M0 scale per 32 values,
+   * X = clamp(floor(log2 amax) - 2, -127, 127), scale byte X + 127, code =
+   * E2M1(x * 2^-X) rounded to nearest even and saturated; element 2m in the
+   * low nibble of byte m; an all-zero block has scale byte 0 and zero
+   * codes.  payload uint8 [R_max][H/2], scales uint8 [R_max][H/32].
+   * Needs H % 32 == 0.                                                    */
+  MOE_FMT_MXFP4_B32 = 2
+} moe_fmt;
+
+/* ---- flags -------------------------------------------------------------- */
+/* Also zero the tail rows [R_used, R_max) of payload and scales.  Without it
+ * those rows are left as they were (pad rows inside R_used are always
+ * zeroed). */
+#define MOE_FLAG_ZERO_TAIL 1u
+
+/* ---- problem description (host memory) ---------------------------------- */
+typedef struct moe_problem {
+  int64_t n_tokens;      /* N >= 0 token rows                                */
+  int32_t hidden;        /* H > 0, H % 8 == 0 (16-byte bf16 rows); see fmt   */
+  int32_t top_k;         /* k, 1 <= k <= min(E, 64)                          */
+  int32_t n_experts;     /* E, 1 <= E <= 1024                                */
+  int32_t ep;            /* EP simulated ranks, E % EP == 0; expert e lives
+                            on rank e / (E/EP)                               */
+  int64_t recv_capacity; /* C: rows a rank may receive before CAPACITY is
+                            flagged; the dropless bound is N * min(k, E/EP)  */
+  int32_t pad_multiple;  /* A >= 1: every expert's row count is padded up to
+                            a multiple of A with zero rows                   */
+  int32_t fmt;           /* a moe_fmt value                                  */
+  uint32_t flags;        /* MOE_FLAG_*                                       */
+} moe_problem;
+
+/* ---- routing plan (device pointers; written by moe_dispatch_plan) ------- */
+typedef struct moe_plan {
+  int32_t *expert_counts;  /* [E]   c_e: valid (token, k) pairs of expert e   */
+  int32_t *expert_offsets; /* [E+1] exclusive cumsum of A*ceil(c_e/A);
+                                    [E] = R_used rows in use                 */
+  int32_t *dest_counts;    /* [EP]  S_r = sum of c_e over rank r's experts   */
+  uint32_t *rank_table;    /* [4][EP] row-major, in elements (rows * H):
+                              0 send counts S_r*H, 1 their exclusive cumsum,
+                              2 padded segment sizes P_r*H, 3 their exclusive
+                              cumsum (P_r = sum of padded counts; with A = 1
+                              rows 2-3 equal rows 0-1)                      */
+  int32_t *slot;           /* [N][k] packed row of pair (t, j), -1 if masked
+                              or invalid; rows of one expert follow flat pair
+                              order t*k + j                                  */
+  int32_t *packed_src;     /* [R_max] source token of each packed row, -1 for
+                              pad and tail rows                              */
+  uint32_t *status;        /* [1]   MOE_STATUS_* bits of this plan           */
+} moe_plan;
+
+/* ---- host-only helpers (no GPU work, safe without a device) ------------- */
+
+/* MOE_OK if the problem is well formed, else the error code the entry
+ * points would return for it. */
+MOE_API int moe_check_problem(const moe_problem *p);
+
+/* R_max = N*k + E*(A-1): rows of the static packed buffer (always >= R_used).
+ * Negative error code if the problem is invalid. */
+MOE_API int64_t moe_max_rows(const moe_problem *p);
+
+/* Bytes of one payload row (2H, H or H/2) and of one scale row (0, 4*H/128
+ * or H/32).  Negative error code if the problem is invalid. */
+MOE_API int64_t moe_payload_row_bytes(const moe_problem *p);
+MOE_API int64_t moe_scale_row_bytes(const moe_problem *p);
+
+/* Device scratch bytes moe_dispatch_plan needs (0 if none; the pointer may
+ * then be NULL).  The caller owns it; its contents need no initialisation
+ * and are dead once the plan's kernels have run.  Returns 0 for an invalid
+ * problem (moe_dispatch_plan reports the error). */
+MOE_API size_t moe_workspace_bytes(const moe_problem *p);
+
+/* ---- entry points -------------------------------------------------------- */
+
+/* Routing plan from topk_ids (device int32 [N][k], -1 = masked): fills every
+ * array of *plan.  workspace: moe_workspace_bytes(p) device bytes, 256-byte
+ * aligned.  Deterministic: no output depends on the order in which atomic
+ * operations land. */
+MOE_API int moe_dispatch_plan(const moe_problem *p, const int32_t *topk_ids,
+                              const moe_plan *plan, void *workspace,
+                              void *stream);
+
+/* Pack token rows: hidden (device bf16 bits [N][H]) is read once per token;
+ * each valid pair (t, j) writes encode(hidden[t]) to packed row
+ * plan->slot[t*k+j] of payload (and its scale row of scales); pad rows of
+ * every expert are written as zero bytes; rows past R_used are zeroed only
+ * with MOE_FLAG_ZERO_TAIL.  payload/scales layouts are given by p->fmt;
+ * scales must be NULL for MOE_FMT_BF16.  Reads slot, expert_counts and
+ * expert_offsets of a plan made for the same problem. */
+MOE_API int moe_dispatch(const moe_problem *p, const moe_plan *plan,
+                         const uint16_t *hidden, void *payload, void *scales,
+                         void *stream);
+
+/* Combine: out[t][c] = bf16_rne( fp32 fused multiply-add chain, starting
+ * from +0 and running over j = 0..k-1 in order, of
+ * topk_weights[t][j] * expert_out[slot[t][j]][c] ), skipping slots < 0.
+ * expert_out: device bf16 bits [R_max][H] (only rows some slot names are
+ * read); topk_weights: device float [N][k]; out: device bf16 bits [N][H]. */
+MOE_API int moe_combine(const moe_problem *p, const moe_plan *plan,
+                        const uint16_t *expert_out, const float *topk_weights,
+                        uint16_t *out, void *stream);
+
+/* Static text for a return code. */
+MOE_API const char *moe_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */
