@@ -176,45 +176,47 @@ def copy_reference(torch, gib=1.0):
     return 2 * n * 2 / (ms * 1e-3) / 1e9
 
 
-def decode_latency(moe, torch, w, inp, iters=200):
-    """µs per plan + dispatch + combine at the decode shape: plain launches
-    and as a replayed HIP graph."""
+def decode_latency(moe, torch, w, inp, iters=200, per_graph=16):
+    """µs per plan + dispatch + combine at the decode shape, three ways:
+    back-to-back calls from Python (host-bound: each call costs a few µs of
+    Python and ctypes), one HIP graph per step, and one HIP graph holding
+    `per_graph` steps (closest to the GPU's own time per step)."""
     path = Path(moe, torch, w, inp, copies=1)
     for i in range(20):
         path.step(0)
     torch.cuda.synchronize()
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s.record()
-    for i in range(iters):
-        path.step(0)
-    e.record()
-    torch.cuda.synchronize()
-    plain = s.elapsed_time(e) / iters * 1e3
-    g = torch.cuda.CUDAGraph()
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        path.step(0)
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    with torch.cuda.graph(g):
-        path.step(0)
-    for _ in range(20):
-        g.replay()
-    torch.cuda.synchronize()
-    s.record()
-    for _ in range(iters):
-        g.replay()
-    e.record()
-    torch.cuda.synchronize()
-    graph = s.elapsed_time(e) / iters * 1e3
-    # the graph's result must equal the eager one
+
+    def clock(fn, reps):
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        s.record()
+        for _ in range(reps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / reps * 1e3
+
+    plain = clock(lambda: path.step(0), iters)
     ref = path.sets[0]["out"].clone()
-    path.step(0)
+    graphs = {}
+    for n in (1, per_graph):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(n):
+                path.step(0)
+        graphs[n] = (g, clock(g.replay, max(iters // n, 10)) / n)
+    # every replay recomputes the same output as the eager path
+    path.sets[0]["out"].zero_()
+    graphs[per_graph][0].replay()
     torch.cuda.synchronize()
     same = bool(torch.equal(ref.view(torch.int16), path.sets[0]["out"].view(torch.int16)))
-    return dict(workload=w.name, us_plain=round(plain, 2), us_graph=round(graph, 2),
-                graph_matches_eager=same, iters=iters)
+    out = dict(workload=w.name, us_per_step_python_launch=round(plain, 2),
+               us_per_step_graph=round(graphs[1][1], 2))
+    out[f"us_per_step_graph_x{per_graph}"] = round(graphs[per_graph][1], 2)
+    out["graph_matches_eager"] = same
+    return out
 
 
 def cpu_baseline(w, inp, r_max, budget_s=10.0):

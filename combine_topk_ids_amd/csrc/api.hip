@@ -33,6 +33,8 @@ int check(const moe_problem *p) {
   if (r_max > INT32_MAX) return MOE_EOVERFLOW;
   if (r_max * static_cast<int64_t>(p->hidden) >= (int64_t{1} << 32)) return MOE_EOVERFLOW;
   if (p->n_tokens * static_cast<int64_t>(p->hidden) >= (int64_t{1} << 40)) return MOE_EOVERFLOW;
+  // one wave per (token, column slab of >= 512 values) must index within int
+  if (p->n_tokens * ((static_cast<int64_t>(p->hidden) + 511) / 512) > INT32_MAX / 4) return MOE_EOVERFLOW;
   return MOE_OK;
 }
 

@@ -14,11 +14,12 @@
 // for j = 0..k-1 in order, skipping masked slots: the same fp32 rounding
 // sequence on every element, so results do not depend on the launch shape.
 //
-// Design for gfx950.  One wave64 per token; each lane owns 8 consecutive
-// columns (one 16-byte bf16 vector) of two 512-column chunks at a time.  All
-// k row loads of a chunk pair are issued before the first FMA, so a wave
-// keeps k x 2 KiB in flight; gate weights and slots are wave-uniform scalar
-// loads.
+// Design for gfx950.  One wave64 per (token, 1024-column slab); each lane
+// owns 8 consecutive columns (one 16-byte bf16 vector) of two 512-column
+// chunks.  The token's k slots and gate weights are loaded once, one per
+// lane, and broadcast with readlane; all k row loads of the slab are issued
+// before the first FMA, so each wave makes two round trips to memory (index
+// loads, then row loads) and keeps k x 2 KiB in flight.
 #include "moe_device.hpp"
 #include "moe_kernels.hpp"
 
@@ -29,7 +30,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kBatch = 8;  // top-k slots whose loads are issued together
+constexpr int kVec = 2;     // 16-byte vectors per lane per slab
+constexpr int kBatch = 8;   // top-k slots whose loads are issued together
 
 struct CombineArgs {
   const uint16_t *y;
@@ -38,6 +40,7 @@ struct CombineArgs {
   uint16_t *out;
   int64_t n;
   int k, h;
+  int slabs;  // waves per token
 };
 
 __device__ __forceinline__ void fma8(float (&acc)[8], float w, const u32x4 v) {
@@ -63,51 +66,55 @@ __device__ __forceinline__ u32x4 pack8(const float (&a)[8]) {
 // KC > 0: k is the compile-time constant KC; KC == 0: runtime k, in batches.
 template <int KC>
 __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs g) {
-  constexpr int U = 2;  // 16-byte vectors per lane per step
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
+  const int q = blockIdx.x * kWaves + wave;  // the grid size keeps q within int
+  const int t = q / g.slabs;
   if (t >= g.n) return;
+  const int slab = q - t * g.slabs;
   const int lane = lane_id();
   const int k = KC > 0 ? KC : g.k;
   const int nvec = g.h / 8;
-  const int32_t *sl = g.slot + t * k;
-  const float *wt = g.w + t * k;
+  const int v0 = slab * kWave * kVec;
+  const int64_t pair0 = static_cast<int64_t>(t) * k;
+  const int my_slot = lane < k ? g.slot[pair0 + lane] : -1;
+  const float my_w = lane < k ? g.w[pair0 + lane] : 0.0f;
   const u32x4 *ybase = reinterpret_cast<const u32x4 *>(g.y);
-  u32x4 *dst = reinterpret_cast<u32x4 *>(g.out + t * g.h);
-  for (int v0 = 0; v0 < nvec; v0 += kWave * U) {
-    float acc[U][8];
+
+  float acc[kVec][8];
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+  for (int u = 0; u < kVec; ++u)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[u][i] = 0.0f;
-    constexpr int KB = KC > 0 ? KC : kBatch;
-    for (int j0 = 0; j0 < k; j0 += KB) {
-      u32x4 v[KB][U];
-      int s[KB];
+    for (int i = 0; i < 8; ++i) acc[u][i] = 0.0f;
+
+  constexpr int KB = KC > 0 ? KC : kBatch;
+  for (int j0 = 0; j0 < k; j0 += KB) {
+    u32x4 v[KB][kVec];
+    int s[KB];
 #pragma unroll
-      for (int jj = 0; jj < KB; ++jj) {
-        s[jj] = (KC > 0 || j0 + jj < k) ? sl[j0 + jj] : -1;
-        const int64_t row = s[jj] >= 0 ? s[jj] : 0;  // masked: harmless in-bounds read
-        const u32x4 *src = ybase + row * nvec;
+    for (int jj = 0; jj < KB; ++jj) {
+      s[jj] = (KC > 0 || j0 + jj < k) ? __builtin_amdgcn_readlane(my_slot, j0 + jj) : -1;
+      const int64_t row = s[jj] >= 0 ? s[jj] : 0;  // masked: harmless in-bounds read
+      const u32x4 *src = ybase + row * nvec;
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int idx = v0 + u * kWave + lane;
-          if (idx < nvec) v[jj][u] = __builtin_nontemporal_load(src + idx);
-        }
-      }
-#pragma unroll
-      for (int jj = 0; jj < KB; ++jj) {
-        if (s[jj] < 0) continue;
-        const float wj = wt[j0 + jj];
-#pragma unroll
-        for (int u = 0; u < U; ++u) fma8(acc[u], wj, v[jj][u]);
+      for (int u = 0; u < kVec; ++u) {
+        const int idx = v0 + u * kWave + lane;
+        if (idx < nvec) v[jj][u] = __builtin_nontemporal_load(src + idx);
       }
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int idx = v0 + u * kWave + lane;
-      if (idx < nvec) __builtin_nontemporal_store(pack8(acc[u]), dst + idx);
+    for (int jj = 0; jj < KB; ++jj) {
+      if (s[jj] < 0) continue;
+      const float wj = __builtin_bit_cast(
+          float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_w), j0 + jj));
+#pragma unroll
+      for (int u = 0; u < kVec; ++u) fma8(acc[u], wj, v[jj][u]);
     }
+  }
+  u32x4 *dst = reinterpret_cast<u32x4 *>(g.out + static_cast<int64_t>(t) * g.h);
+#pragma unroll
+  for (int u = 0; u < kVec; ++u) {
+    const int idx = v0 + u * kWave + lane;
+    if (idx < nvec) __builtin_nontemporal_store(pack8(acc[u]), dst + idx);
   }
 }
 
@@ -123,7 +130,10 @@ hipError_t launch_combine(const moe_problem &p, const moe_plan &plan, const uint
   g.n = p.n_tokens;
   g.k = p.top_k;
   g.h = p.hidden;
-  const int grid = static_cast<int>((p.n_tokens + kWaves - 1) / kWaves);
+  const int slab_cols = kWave * kVec * 8;
+  g.slabs = (p.hidden + slab_cols - 1) / slab_cols;
+  const int64_t waves = p.n_tokens * g.slabs;
+  const int grid = static_cast<int>((waves + kWaves - 1) / kWaves);
   if (grid == 0) return hipSuccess;
   switch (p.top_k) {
     case 1: combine_kernel<1><<<grid, kThreads, 0, stream>>>(g); break;

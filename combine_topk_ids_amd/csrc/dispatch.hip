@@ -14,12 +14,12 @@
 //   Formats: OCP 8-bit Floating Point (E4M3) and OCP MX v1.0 (E2M1, E8M0),
 //     with the per-1x128 amax/448 fp32 scale of the FP8 recipe.
 //
-// Design for gfx950.  Token-stationary: one wave64 owns one token, reads its
-// row once with 16-byte loads (8 bf16 per lane, 1 KiB per wave instruction),
-// encodes it once, and writes the result to each of its k packed rows, so
-// the cost does not depend on how skewed the routing is.  FP8 block maxima
-// are a 16-lane DPP row reduction (one 1x128 block = 16 lanes x 8 values);
-// MX block maxima a 4-lane quad reduction.  Pad rows are zeroed by a second
+// Design for gfx950.  Token-stationary: one wave64 owns one column slab of
+// one token, reads it once with 16-byte loads (8 bf16 per lane, 1 KiB per
+// wave instruction), encodes it once, and writes the result to each of the
+// token's k packed rows, so the cost does not depend on how skewed the
+// routing is.  FP8 block maxima are a 16-lane DPP row reduction (one 1x128
+// block = 16 lanes x 8 values); MX block maxima a 4-lane quad reduction.  Pad rows are zeroed by a second
 // range of workgroups in the same launch, the optional tail by a third.
 #include "moe_device.hpp"
 #include "moe_kernels.hpp"
@@ -47,6 +47,7 @@ struct DispatchArgs {
   int64_t row_bytes;    // payload bytes per packed row
   int64_t scale_bytes;  // scale bytes per packed row
   int k, h, e;
+  int slabs;  // waves per token
   int token_blocks, pad_blocks, tail_blocks;
   int pad_groups;  // pad-row groups of kPadRowsPerWave per expert
 };
@@ -59,135 +60,137 @@ __device__ __forceinline__ void store(V *p, V v) {
     *p = v;
 }
 
-// ---- bf16: copy the row to every destination ------------------------------
+// One wave handles one (token, column slab).  The k destination slots are
+// loaded once, one per lane, together with the slab's data, and broadcast
+// with readlane, so a wave makes a single round trip to memory before it
+// starts storing.
+__device__ __forceinline__ int lane_slot(const DispatchArgs &g, int64_t t, int lane) {
+  return lane < g.k ? g.slot[t * g.k + lane] : -1;
+}
+
+// ---- bf16: copy the slab to every destination -------------------------------
+constexpr int kBf16Vec = 4;  // 16-byte vectors per lane per slab (4 KiB a wave)
+
 template <bool NT>
-__device__ void token_bf16(const DispatchArgs &g, int64_t t) {
-  constexpr int U = 8;  // 16-byte vectors per lane in flight
+__device__ void slab_bf16(const DispatchArgs &g, int64_t t, int slab) {
   const int lane = lane_id();
   const int nvec = g.h / 8;
+  const int v0 = slab * kWave * kBf16Vec;
   const u32x4 *src = reinterpret_cast<const u32x4 *>(g.x + t * g.h);
-  const int32_t *sl = g.slot + t * g.k;
-  for (int v0 = 0; v0 < nvec; v0 += kWave * U) {
-    u32x4 buf[U];
+  const int my_slot = lane_slot(g, t, lane);
+  u32x4 buf[kBf16Vec];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+  for (int u = 0; u < kBf16Vec; ++u) {
+    const int idx = v0 + u * kWave + lane;
+    if (idx < nvec) buf[u] = __builtin_nontemporal_load(src + idx);
+  }
+  for (int j = 0; j < g.k; ++j) {
+    const int s = __builtin_amdgcn_readlane(my_slot, j);
+    if (s < 0) continue;
+    u32x4 *dst = reinterpret_cast<u32x4 *>(g.payload + static_cast<int64_t>(s) * g.row_bytes);
+#pragma unroll
+    for (int u = 0; u < kBf16Vec; ++u) {
       const int idx = v0 + u * kWave + lane;
-      if (idx < nvec) buf[u] = __builtin_nontemporal_load(src + idx);
-    }
-    for (int j = 0; j < g.k; ++j) {
-      const int s = sl[j];
-      if (s < 0) continue;
-      u32x4 *dst = reinterpret_cast<u32x4 *>(g.payload + static_cast<int64_t>(s) * g.row_bytes);
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int idx = v0 + u * kWave + lane;
-        if (idx < nvec) store<NT>(dst + idx, buf[u]);
-      }
+      if (idx < nvec) store<NT>(dst + idx, buf[u]);
     }
   }
 }
 
 // ---- FP8 E4M3, one fp32 scale per 1x128 block -------------------------------
+constexpr int kQuantChunks = 2;  // 512-element chunks per slab
+
 template <bool NT>
-__device__ void token_fp8(const DispatchArgs &g, int64_t t) {
-  constexpr int U = 4;  // 512-element chunks per batch
+__device__ void slab_fp8(const DispatchArgs &g, int64_t t, int slab) {
   const int lane = lane_id();
-  const int nchunk = (g.h + 511) / 512;
+  const int c0 = slab * kQuantChunks;
   const u32x4 *src = reinterpret_cast<const u32x4 *>(g.x + t * g.h);
-  const int32_t *sl = g.slot + t * g.k;
-  const int sblocks = g.h / 128;
-  for (int c0 = 0; c0 < nchunk; c0 += U) {
-    u32x4 raw[U];
+  const int my_slot = lane_slot(g, t, lane);
+  u32x4 raw[kQuantChunks];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+  for (int u = 0; u < kQuantChunks; ++u) {
+    const int elem = (c0 + u) * 512 + lane * 8;
+    raw[u] = elem < g.h ? __builtin_nontemporal_load(src + elem / 8) : u32x4{0u, 0u, 0u, 0u};
+  }
+  u32x2 codes[kQuantChunks];
+  float scale[kQuantChunks];
+#pragma unroll
+  for (int u = 0; u < kQuantChunks; ++u) {
+    float f[8];
+    uint4 r4;
+    r4.x = raw[u].x; r4.y = raw[u].y; r4.z = raw[u].z; r4.w = raw[u].w;
+    unpack8(r4, f);
+    uint32_t am = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) am = max(am, __float_as_uint(f[i]) & 0x7FFFFFFFu);
+    am = row16_max(am);  // one 1x128 block = one 16-lane DPP row
+    const float s = __uint_as_float(am) / 448.0f;
+    uint32_t b[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) b[i] = s == 0.0f ? 0u : e4m3_rne_sat(f[i] / s);
+    codes[u].x = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
+    codes[u].y = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
+    scale[u] = s;
+  }
+  for (int j = 0; j < g.k; ++j) {
+    const int s = __builtin_amdgcn_readlane(my_slot, j);
+    if (s < 0) continue;
+    uint8_t *prow = g.payload + static_cast<int64_t>(s) * g.row_bytes;
+    float *srow = reinterpret_cast<float *>(g.scales + static_cast<int64_t>(s) * g.scale_bytes);
+#pragma unroll
+    for (int u = 0; u < kQuantChunks; ++u) {
       const int elem = (c0 + u) * 512 + lane * 8;
-      raw[u] = elem < g.h ? __builtin_nontemporal_load(src + elem / 8) : u32x4{0u, 0u, 0u, 0u};
-    }
-    u32x2 codes[U];
-    float scale[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float f[8];
-      uint4 r4;
-      r4.x = raw[u].x; r4.y = raw[u].y; r4.z = raw[u].z; r4.w = raw[u].w;
-      unpack8(r4, f);
-      uint32_t am = 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) am = max(am, __float_as_uint(f[i]) & 0x7FFFFFFFu);
-      am = row16_max(am);
-      const float s = __uint_as_float(am) / 448.0f;
-      uint32_t b[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) b[i] = s == 0.0f ? 0u : e4m3_rne_sat(f[i] / s);
-      codes[u].x = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
-      codes[u].y = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
-      scale[u] = s;
-    }
-    for (int j = 0; j < g.k; ++j) {
-      const int s = sl[j];
-      if (s < 0) continue;
-      uint8_t *prow = g.payload + static_cast<int64_t>(s) * g.row_bytes;
-      float *srow = reinterpret_cast<float *>(g.scales + static_cast<int64_t>(s) * g.scale_bytes);
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int elem = (c0 + u) * 512 + lane * 8;
-        if (elem < g.h) {
-          store<NT>(reinterpret_cast<u32x2 *>(prow + elem), codes[u]);
-          if ((lane & 15) == 0) store<NT>(srow + elem / 128, scale[u]);
-        }
+      if (elem < g.h) {
+        store<NT>(reinterpret_cast<u32x2 *>(prow + elem), codes[u]);
+        if ((lane & 15) == 0) store<NT>(srow + elem / 128, scale[u]);
       }
     }
   }
-  (void)sblocks;
 }
 
 // ---- MX-FP4: E2M1 codes, one E8M0 scale per 32 values -----------------------
 template <bool NT>
-__device__ void token_mx(const DispatchArgs &g, int64_t t) {
-  constexpr int U = 4;
+__device__ void slab_mx(const DispatchArgs &g, int64_t t, int slab) {
   const int lane = lane_id();
-  const int nchunk = (g.h + 511) / 512;
+  const int c0 = slab * kQuantChunks;
   const u32x4 *src = reinterpret_cast<const u32x4 *>(g.x + t * g.h);
-  const int32_t *sl = g.slot + t * g.k;
-  for (int c0 = 0; c0 < nchunk; c0 += U) {
-    u32x4 raw[U];
+  const int my_slot = lane_slot(g, t, lane);
+  u32x4 raw[kQuantChunks];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+  for (int u = 0; u < kQuantChunks; ++u) {
+    const int elem = (c0 + u) * 512 + lane * 8;
+    raw[u] = elem < g.h ? __builtin_nontemporal_load(src + elem / 8) : u32x4{0u, 0u, 0u, 0u};
+  }
+  uint32_t word[kQuantChunks];
+  uint32_t sbyte[kQuantChunks];
+#pragma unroll
+  for (int u = 0; u < kQuantChunks; ++u) {
+    float f[8];
+    uint4 r4;
+    r4.x = raw[u].x; r4.y = raw[u].y; r4.z = raw[u].z; r4.w = raw[u].w;
+    unpack8(r4, f);
+    uint32_t am = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) am = max(am, __float_as_uint(f[i]) & 0x7FFFFFFFu);
+    am = quad_max(am);  // one 32-value block = one quad
+    const int X = mx_exponent(am);
+    const float mul = __uint_as_float(static_cast<uint32_t>(127 - X) << 23);  // 2^-X
+    uint32_t w = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w |= e2m1_rne_sat(f[i] * mul) << (4 * i);
+    word[u] = am == 0 ? 0u : w;
+    sbyte[u] = am == 0 ? 0u : static_cast<uint32_t>(X + 127);
+  }
+  for (int j = 0; j < g.k; ++j) {
+    const int s = __builtin_amdgcn_readlane(my_slot, j);
+    if (s < 0) continue;
+    uint8_t *prow = g.payload + static_cast<int64_t>(s) * g.row_bytes;
+    uint8_t *srow = g.scales + static_cast<int64_t>(s) * g.scale_bytes;
+#pragma unroll
+    for (int u = 0; u < kQuantChunks; ++u) {
       const int elem = (c0 + u) * 512 + lane * 8;
-      raw[u] = elem < g.h ? __builtin_nontemporal_load(src + elem / 8) : u32x4{0u, 0u, 0u, 0u};
-    }
-    uint32_t word[U];
-    uint32_t sbyte[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float f[8];
-      uint4 r4;
-      r4.x = raw[u].x; r4.y = raw[u].y; r4.z = raw[u].z; r4.w = raw[u].w;
-      unpack8(r4, f);
-      uint32_t am = 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) am = max(am, __float_as_uint(f[i]) & 0x7FFFFFFFu);
-      am = quad_max(am);
-      const int X = mx_exponent(am);
-      const float mul = __uint_as_float(static_cast<uint32_t>(127 - X) << 23);  // 2^-X
-      uint32_t w = 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) w |= e2m1_rne_sat(f[i] * mul) << (4 * i);
-      word[u] = am == 0 ? 0u : w;
-      sbyte[u] = am == 0 ? 0u : static_cast<uint32_t>(X + 127);
-    }
-    for (int j = 0; j < g.k; ++j) {
-      const int s = sl[j];
-      if (s < 0) continue;
-      uint8_t *prow = g.payload + static_cast<int64_t>(s) * g.row_bytes;
-      uint8_t *srow = g.scales + static_cast<int64_t>(s) * g.scale_bytes;
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int elem = (c0 + u) * 512 + lane * 8;
-        if (elem < g.h) {
-          store<NT>(reinterpret_cast<uint32_t *>(prow + elem / 2), word[u]);
-          if ((lane & 3) == 0) store<NT>(srow + elem / 32, static_cast<uint8_t>(sbyte[u]));
-        }
+      if (elem < g.h) {
+        store<NT>(reinterpret_cast<uint32_t *>(prow + elem / 2), word[u]);
+        if ((lane & 3) == 0) store<NT>(srow + elem / 32, static_cast<uint8_t>(sbyte[u]));
       }
     }
   }
@@ -217,11 +220,13 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(DispatchArgs g) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   int blk = blockIdx.x;
   if (blk < g.token_blocks) {
-    const int64_t t = static_cast<int64_t>(blk) * kWaves + wave;
+    const int q = blk * kWaves + wave;  // the grid size keeps q within int
+    const int t = q / g.slabs;
     if (t >= g.n) return;
-    if (FMT == MOE_FMT_BF16) token_bf16<NT>(g, t);
-    else if (FMT == MOE_FMT_FP8_E4M3_B128) token_fp8<NT>(g, t);
-    else token_mx<NT>(g, t);
+    const int slab = q - t * g.slabs;
+    if (FMT == MOE_FMT_BF16) slab_bf16<NT>(g, t, slab);
+    else if (FMT == MOE_FMT_FP8_E4M3_B128) slab_fp8<NT>(g, t, slab);
+    else slab_mx<NT>(g, t, slab);
     return;
   }
   blk -= g.token_blocks;
@@ -276,7 +281,9 @@ hipError_t launch_dispatch(const moe_problem &p, const moe_plan &plan, const uin
     g.row_bytes = p.hidden / 2;
     g.scale_bytes = p.hidden / 32;
   }
-  g.token_blocks = static_cast<int>((p.n_tokens + kWaves - 1) / kWaves);
+  const int slab_elems = p.fmt == MOE_FMT_BF16 ? kWave * kBf16Vec * 8 : kQuantChunks * 512;
+  g.slabs = (p.hidden + slab_elems - 1) / slab_elems;
+  g.token_blocks = static_cast<int>((p.n_tokens * g.slabs + kWaves - 1) / kWaves);
   g.pad_groups = (p.pad_multiple - 1 + kPadRowsPerWave - 1) / kPadRowsPerWave;
   g.pad_blocks = g.pad_groups == 0 ? 0 : (p.n_experts * g.pad_groups + kWaves - 1) / kWaves;
   if (g.pad_groups == 0) g.pad_groups = 1;  // keep the division in the kernel defined

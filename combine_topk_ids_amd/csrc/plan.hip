@@ -25,20 +25,27 @@
 //                [ntiles][E] plus the tile's fault bits.
 //   plan_assign  (one block per tile) every block re-reduces the small
 //                histogram matrix (totals and the prefix over earlier
-//                tiles), scans the padded counts over experts, block 0
-//                writes counts/offsets/table/status; then each wave walks its
-//                64-pair chunks in order, ranking equal expert IDs inside the
-//                chunk with a ballot-based match (one ballot per ID bit) and
-//                advancing a per-wave cursor per expert in LDS.
-// A plan of at most 2048 pairs (decode shapes) runs as a single block of
+//                tiles), scans the padded counts over experts, then each wave
+//                walks its 64-pair chunks in order, ranking equal expert IDs
+//                inside the chunk with a ballot-based match (one ballot per ID
+//                bit) and advancing a per-wave cursor per expert in LDS;
+//                block 0 also writes counts, offsets, table and status.
+// A plan of at most 2048 pairs (decode shapes) runs as one block of
 // plan_assign that also does the counting: one launch.
+//
+// Latency matters more than bandwidth here (the whole plan moves < 2 MB):
+// each kernel issues all of its global loads first, keeps every
+// intermediate in LDS, and issues its global stores last, so no barrier has
+// to wait for stores to drain.
 #include "moe_device.hpp"
 #include "moe_kernels.hpp"
 
 namespace moe {
 namespace {
 
-constexpr int kTilePairs = 2048;  // a multiple of kPlanThreads
+constexpr int kTilePairs = 2048;                       // multiple of kPlanThreads
+constexpr int kPairsPerThread = kTilePairs / kPlanThreads;
+constexpr int kHistBatch = 32;                         // histogram loads in flight per thread
 
 struct PlanArgs {
   const int32_t *ids;
@@ -59,42 +66,54 @@ struct PlanArgs {
 
 __device__ __forceinline__ int padded(int c, int a) { return ((c + a - 1) / a) * a; }
 
-// OR of `v` over the block (every thread must call; v holds status bits).
-__device__ uint32_t block_or(uint32_t v, uint32_t *s_word) {
-  const uint32_t w = (ballot(v & 1u) ? 1u : 0u) | (ballot(v & 2u) ? 2u : 0u) |
-                     (ballot(v & 4u) ? 4u : 0u);
-  if (lane_id() == 0 && w) atomicOr(s_word, w);
-  __syncthreads();
-  return *s_word;
+__device__ __forceinline__ uint32_t wave_or_bits(uint32_t v) {
+  return (ballot(v & 1u) ? 1u : 0u) | (ballot(v & 2u) ? 2u : 0u) | (ballot(v & 4u) ? 4u : 0u);
 }
 
-// Stage the tile's IDs in LDS, starting at the first pair of the token that
-// owns pair `begin` (so a token's earlier slots are at hand for the
-// repeated-ID check).  Returns that lead-in length (< k).
+// Load the tile's IDs into LDS, starting at the first pair of the token that
+// owns pair `begin` (so each token's earlier slots are at hand for the
+// repeated-ID check).  All loads are issued before any is used.  Returns the
+// lead-in length (< k).  The caller places a barrier before reading s_ids.
 __device__ int stage_ids(const PlanArgs &g, int64_t begin, int64_t end, int *s_ids) {
-  const int pre = static_cast<int>(begin % g.k);
-  const int64_t lo = begin - pre;
-  const int len = static_cast<int>(end - lo);
-  for (int i = threadIdx.x; i < len; i += kPlanThreads) s_ids[i] = g.ids[lo + i];
-  __syncthreads();
+  const int tid = threadIdx.x;
+  // pair indices fit in 31 bits (checked on the host)
+  const int pre = static_cast<int>(static_cast<uint32_t>(begin) % static_cast<uint32_t>(g.k));
+  const int len = static_cast<int>(end - begin);
+  int v[kPairsPerThread];
+#pragma unroll
+  for (int u = 0; u < kPairsPerThread; ++u) {
+    const int i = u * kPlanThreads + tid;
+    v[u] = i < len ? g.ids[begin + i] : -1;
+  }
+  const int lead = tid < pre ? g.ids[begin - pre + tid] : 0;
+#pragma unroll
+  for (int u = 0; u < kPairsPerThread; ++u) {
+    const int i = u * kPlanThreads + tid;
+    if (i < len) s_ids[pre + i] = v[u];
+  }
+  if (tid < pre) s_ids[tid] = lead;
   return pre;
 }
 
-// Histogram of the valid pairs of [begin, end) into s_cnt (zeroed by the
-// caller); returns this thread's BAD_ID / DUP_ID bits.
-__device__ uint32_t count_tile(const PlanArgs &g, int64_t begin, int64_t end,
-                               const int *s_ids, int pre, int *s_cnt) {
+// Histogram of the valid pairs of [begin, end) into s_cnt (zeroed); returns
+// this thread's BAD_ID / DUP_ID bits.
+__device__ uint32_t count_tile(const PlanArgs &g, int64_t begin, int64_t end, const int *s_ids,
+                               int pre, int *s_cnt) {
   uint32_t fl = 0;
   const int len = static_cast<int>(end - begin);
   const uint32_t k = static_cast<uint32_t>(g.k);
-  for (int i = threadIdx.x; i < len; i += kPlanThreads) {
+  const uint32_t j0 = static_cast<uint32_t>(pre);  // position in its token of pair `begin`
+#pragma unroll
+  for (int u = 0; u < kPairsPerThread; ++u) {
+    const int i = u * kPlanThreads + threadIdx.x;
+    if (i >= len) break;
     const int e = s_ids[pre + i];
     if (e == -1) continue;
     if (e < -1 || e >= g.e) {
       fl |= MOE_STATUS_BAD_ID;
       continue;
     }
-    const int j = static_cast<int>(static_cast<uint32_t>(begin + i) % k);
+    const int j = static_cast<int>((j0 + static_cast<uint32_t>(i)) % k);
     for (int q = pre + i - j; q < pre + i; ++q)
       if (s_ids[q] == e) fl |= MOE_STATUS_DUP_ID;
     atomicAdd(&s_cnt[e], 1);
@@ -104,33 +123,35 @@ __device__ uint32_t count_tile(const PlanArgs &g, int64_t begin, int64_t end,
 
 __global__ __launch_bounds__(kPlanThreads) void plan_count_kernel(PlanArgs g) {
   extern __shared__ int smem[];
-  int *s_cnt = smem;                  // [E]
-  int *s_ids = smem + g.e;            // [kTilePairs + kMaxTopK]
+  int *s_cnt = smem;        // [E]
+  int *s_ids = smem + g.e;  // [kTilePairs + kMaxTopK]
   __shared__ uint32_t s_fl;
-  for (int e = threadIdx.x; e < g.e; e += kPlanThreads) s_cnt[e] = 0;
-  if (threadIdx.x == 0) s_fl = 0;
   const int b = blockIdx.x;
   const int64_t begin = static_cast<int64_t>(b) * kTilePairs;
   const int64_t end = min(begin + kTilePairs, g.npairs);
-  const int pre = stage_ids(g, begin, end, s_ids);  // includes a barrier
-  uint32_t fl = count_tile(g, begin, end, s_ids, pre, s_cnt);
-  fl = block_or(fl, &s_fl);
+  const int pre = stage_ids(g, begin, end, s_ids);
+  for (int e = threadIdx.x; e < g.e; e += kPlanThreads) s_cnt[e] = 0;
+  if (threadIdx.x == 0) s_fl = 0;
+  __syncthreads();
+  const uint32_t fl = wave_or_bits(count_tile(g, begin, end, s_ids, pre, s_cnt));
+  if (lane_id() == 0 && fl) atomicOr(&s_fl, fl);
+  __syncthreads();
   int32_t *hrow = g.hist + static_cast<int64_t>(b) * g.e;
   for (int e = threadIdx.x; e < g.e; e += kPlanThreads) hrow[e] = s_cnt[e];
-  if (threadIdx.x == 0) g.tflags[b] = fl;
+  if (threadIdx.x == 0) g.tflags[b] = s_fl;
 }
 
 template <bool kSingle>
 __global__ __launch_bounds__(kPlanThreads) void plan_assign_kernel(PlanArgs g) {
   extern __shared__ int smem[];
   const int E = g.e;
-  int *s_tot = smem;               // [E]   c_e
-  int *s_pre = s_tot + E;          // [E]   pairs of e in tiles before this one
-  int *s_off = s_pre + E;          // [E+1] padded exclusive cumsum
-  int *s_cpre = s_off + E + 1;     // [E+1] unpadded exclusive cumsum
-  int *s_cur = s_cpre + E + 1;     // [kPlanWaves][E] per-wave cursors
+  int *s_tot = smem;                    // [E]   c_e
+  int *s_pre = s_tot + E;               // [E]   pairs of e in tiles before this one
+  int *s_off = s_pre + E;               // [E+1] padded exclusive cumsum
+  int *s_cpre = s_off + E + 1;          // [E+1] unpadded exclusive cumsum
+  int *s_cur = s_cpre + E + 1;          // [kPlanWaves][E] per-wave cursors
   int *s_ids = s_cur + kPlanWaves * E;  // [kTilePairs + kMaxTopK]
-  __shared__ uint32_t s_fl, s_fl2;
+  __shared__ uint32_t s_fl;
   __shared__ int s_scan[2][kPlanWaves];
 
   const int tid = threadIdx.x;
@@ -139,45 +160,63 @@ __global__ __launch_bounds__(kPlanThreads) void plan_assign_kernel(PlanArgs g) {
   const int b = blockIdx.x;
   const int64_t begin = static_cast<int64_t>(b) * kTilePairs;
   const int64_t end = min(begin + kTilePairs, g.npairs);
+  const int len = static_cast<int>(end - begin);
 
+  // ---- global loads first: the first batch of the histogram matrix, then
+  // the tile's IDs ---------------------------------------------------------
+  const int total = kSingle ? 0 : g.ntiles * E;
+  int hv[kHistBatch];
+#pragma unroll
+  for (int u = 0; u < kHistBatch; ++u) {
+    const int i = u * kPlanThreads + tid;
+    hv[u] = i < total ? g.hist[i] : 0;
+  }
+  const int pre = stage_ids(g, begin, end, s_ids);
   for (int e = tid; e < E; e += kPlanThreads) {
     s_tot[e] = 0;
     s_pre[e] = 0;
   }
   for (int i = tid; i < kPlanWaves * E; i += kPlanThreads) s_cur[i] = 0;
-  if (tid == 0) {
-    s_fl = 0;
-    s_fl2 = 0;
-  }
-  const int pre = stage_ids(g, begin, end, s_ids);  // includes a barrier
+  if (tid == 0) s_fl = 0;
+  __syncthreads();
 
-  // ---- totals c_e (and, across tiles, the prefix before this tile) -------
   uint32_t fl = 0;
   if (kSingle) {
     fl = count_tile(g, begin, end, s_ids, pre, s_tot);
   } else {
-    const int total = g.ntiles * E;
-    for (int base = 0; base < total; base += 8 * kPlanThreads) {
-      int v[8];
+    for (int base = 0; base < total; base += kHistBatch * kPlanThreads) {
+      if (base > 0) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i = base + u * kPlanThreads + tid;
-        v[u] = i < total ? g.hist[i] : 0;
+        for (int u = 0; u < kHistBatch; ++u) {
+          const int i = base + u * kPlanThreads + tid;
+          hv[u] = i < total ? g.hist[i] : 0;
+        }
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (v[u]) {
+      for (int u = 0; u < kHistBatch; ++u) {
+        if (hv[u]) {
           const int i = base + u * kPlanThreads + tid;
           const int tile = i / E;
           const int e = i - tile * E;
-          atomicAdd(&s_tot[e], v[u]);
-          if (tile < b) atomicAdd(&s_pre[e], v[u]);
+          atomicAdd(&s_tot[e], hv[u]);
+          if (tile < b) atomicAdd(&s_pre[e], hv[u]);
         }
       }
     }
     for (int i = tid; i < g.ntiles; i += kPlanThreads) fl |= g.tflags[i];
   }
-  fl = block_or(fl, &s_fl);  // barrier: s_tot / s_pre complete
+  // per-wave counts of this tile's pairs (cursor bases come later)
+  // pairs per wave: the tile split evenly over the waves in 64-pair chunks
+  const int wp = ((len + kPlanWaves * kWave - 1) / (kPlanWaves * kWave)) * kWave;
+  const int wb = wave * wp, we = min(wb + wp, len);
+  int *cur = s_cur + wave * E;
+  for (int i = wb + lane; i < we; i += kWave) {
+    const int e = s_ids[pre + i];
+    if (e >= 0 && e < E) atomicAdd(&cur[e], 1);
+  }
+  fl = wave_or_bits(fl);
+  if (lane == 0 && fl) atomicOr(&s_fl, fl);
+  __syncthreads();
 
   // ---- padded and unpadded exclusive scans over experts -----------------
   {
@@ -216,52 +255,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_assign_kernel(PlanArgs g) {
       s_off[E] = tp;
       s_cpre[E] = tc;
     }
-    __syncthreads();
-  }
-
-  // ---- block 0: counts, offsets, per-rank table, status -----------------
-  if (b == 0) {
-    for (int e = tid; e < E; e += kPlanThreads) {
-      g.counts[e] = s_tot[e];
-      g.offsets[e] = s_off[e];
-    }
-    if (tid == 0) g.offsets[E] = s_off[E];
-    const int L = E / g.ep;
-    uint32_t cap = 0;
-    for (int r = tid; r < g.ep; r += kPlanThreads) {
-      const int lo = r * L, hi = lo + L;
-      const int S = s_cpre[hi] - s_cpre[lo];
-      const int P = s_off[hi] - s_off[lo];
-      g.dest_counts[r] = S;
-      g.table[r] = static_cast<uint32_t>(S) * g.h;
-      g.table[g.ep + r] = static_cast<uint32_t>(s_cpre[lo]) * g.h;
-      g.table[2 * g.ep + r] = static_cast<uint32_t>(P) * g.h;
-      g.table[3 * g.ep + r] = static_cast<uint32_t>(s_off[lo]) * g.h;
-      if (S > g.cap) cap = MOE_STATUS_CAPACITY;
-    }
-    cap = block_or(cap, &s_fl2);
-    if (tid == 0) *g.status = fl | cap;
-  }
-
-  // ---- packed_src = -1 on pad rows (experts b, b+ntiles, ...) and tail ---
-  for (int e = b; e < E; e += g.ntiles) {
-    const int lo = s_off[e] + s_tot[e], hi = s_off[e + 1];
-    for (int r = lo + tid; r < hi; r += kPlanThreads) g.packed_src[r] = -1;
-  }
-  for (int64_t r = s_off[E] + static_cast<int64_t>(b) * kPlanThreads + tid; r < g.r_max;
-       r += static_cast<int64_t>(g.ntiles) * kPlanThreads)
-    g.packed_src[r] = -1;
-
-  // ---- stable slots: per-wave counts, wave bases, ranked walk -----------
-  const int wp = kTilePairs / kPlanWaves;  // pairs per wave, multiple of 64
-  const int len = static_cast<int>(end - begin);
-  const int wb = wave * wp, we = min(wb + wp, len);
-  int *cur = s_cur + wave * E;
-  for (int i = wb + lane; i < we; i += kWave) {
-    const int e = s_ids[pre + i];
-    if (e >= 0 && e < E) atomicAdd(&cur[e], 1);
   }
   __syncthreads();
+
+  // ---- cursor bases: offset + earlier tiles + earlier waves of this tile --
   for (int e = tid; e < E; e += kPlanThreads) {
     int run = s_off[e] + s_pre[e];
 #pragma unroll
@@ -271,7 +268,17 @@ __global__ __launch_bounds__(kPlanThreads) void plan_assign_kernel(PlanArgs g) {
       run += c;
     }
   }
+  // capacity check (block 0 only needs it; cheap everywhere)
+  const int L = E / g.ep;
+  uint32_t cap = 0;
+  for (int r = tid; r < g.ep; r += kPlanThreads)
+    if (s_cpre[(r + 1) * L] - s_cpre[r * L] > g.cap) cap = MOE_STATUS_CAPACITY;
+  cap = wave_or_bits(cap);
+  if (lane == 0 && cap) atomicOr(&s_fl, cap);
   __syncthreads();
+
+  // ---- stores only from here on -------------------------------------------
+  // stable slots: walk this wave's pairs in 64-pair chunks, in order
   const uint32_t k = static_cast<uint32_t>(g.k);
   for (int i0 = wb; i0 < we; i0 += kWave) {
     const int i = i0 + lane;
@@ -291,6 +298,43 @@ __global__ __launch_bounds__(kPlanThreads) void plan_assign_kernel(PlanArgs g) {
     }
     if (in) g.slot[begin + i] = sl;
   }
+
+  // block 0: counts, offsets, per-rank table, status
+  if (b == 0) {
+    for (int e = tid; e < E; e += kPlanThreads) {
+      g.counts[e] = s_tot[e];
+      g.offsets[e] = s_off[e];
+    }
+    if (tid == 0) {
+      g.offsets[E] = s_off[E];
+      *g.status = s_fl;
+    }
+    for (int r = tid; r < g.ep; r += kPlanThreads) {
+      const int lo = r * L, hi = lo + L;
+      const int S = s_cpre[hi] - s_cpre[lo];
+      const int P = s_off[hi] - s_off[lo];
+      g.dest_counts[r] = S;
+      g.table[r] = static_cast<uint32_t>(S) * g.h;
+      g.table[g.ep + r] = static_cast<uint32_t>(s_cpre[lo]) * g.h;
+      g.table[2 * g.ep + r] = static_cast<uint32_t>(P) * g.h;
+      g.table[3 * g.ep + r] = static_cast<uint32_t>(s_off[lo]) * g.h;
+    }
+  }
+
+  // packed_src = -1 on pad rows (an expert has at most A-1 of them: the grid
+  // strides over all E*(A-1) candidates) and on the tail rows
+  if (g.a > 1) {
+    const int per = g.a - 1;
+    const int cand = E * per;
+    for (int q = b * kPlanThreads + tid; q < cand; q += g.ntiles * kPlanThreads) {
+      const int e = q / per;
+      const int r = s_off[e] + s_tot[e] + (q - e * per);
+      if (r < s_off[e + 1]) g.packed_src[r] = -1;
+    }
+  }
+  for (int64_t r = s_off[E] + static_cast<int64_t>(b) * kPlanThreads + tid; r < g.r_max;
+       r += static_cast<int64_t>(g.ntiles) * kPlanThreads)
+    g.packed_src[r] = -1;
 }
 
 }  // namespace

@@ -117,7 +117,25 @@ def moe_workspace_bytes(p: Problem) -> int:
     return int(lib.moe_workspace_bytes(ctypes.byref(p)))
 
 
-@dataclasses.dataclass
+_SIZES: dict = {}
+
+
+def _sizes(p: Problem):
+    """(R_max, payload row bytes, scale row bytes, workspace bytes), cached per
+    problem value (the C library stays the source of these numbers)."""
+    key = (p.n_tokens, p.hidden, p.top_k, p.n_experts, p.ep, p.recv_capacity,
+           p.pad_multiple, p.fmt, p.flags)
+    v = _SIZES.get(key)
+    if v is None:
+        v = (moe_max_rows(p), moe_payload_row_bytes(p), moe_scale_row_bytes(p),
+             moe_workspace_bytes(p))
+        if len(_SIZES) > 4096:
+            _SIZES.clear()
+        _SIZES[key] = v
+    return v
+
+
+@dataclasses.dataclass(frozen=True)
 class PlanBuffers:
     """Device tensors a plan is written to, plus the plan kernels' workspace."""
     expert_counts: torch.Tensor
@@ -130,7 +148,12 @@ class PlanBuffers:
     workspace: torch.Tensor
 
     def as_struct(self) -> Plan:
-        return Plan(*(getattr(self, f).data_ptr() for f, _ in Plan._fields_))
+        """The moe_plan struct (device pointers); built once per buffer set."""
+        st = self.__dict__.get("_struct")
+        if st is None:
+            st = Plan(*(getattr(self, f).data_ptr() for f, _ in Plan._fields_))
+            self.__dict__["_struct"] = st
+        return st
 
     def read_status(self) -> int:
         """Synchronises the current stream and returns the status bits."""
@@ -180,48 +203,56 @@ def _dev(t: torch.Tensor | None, name: str, dtypes, numel: int | None = None) ->
     return t.data_ptr()
 
 
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(stream) -> int:
-    s = torch.cuda.current_stream() if stream is None else stream
-    return s.cuda_stream
+    """Raw hipStream_t of `stream`, or of torch's current stream (which is the
+    capture stream inside torch.cuda.graph)."""
+    if stream is not None:
+        return stream.cuda_stream
+    if _raw_stream is not None:
+        return _raw_stream(torch.cuda.current_device())
+    return torch.cuda.current_stream().cuda_stream
 
 
 _BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+_PAYLOAD = (torch.bfloat16, torch.int16, torch.uint16, torch.uint8, torch.float8_e4m3fn)
 
 
 def moe_dispatch_plan(p: Problem, topk_ids: torch.Tensor, plan: PlanBuffers, stream=None) -> None:
-    ids = _dev(topk_ids, "topk_ids", (torch.int32,), p.n_tokens * p.top_k)
-    _dev(plan.slot, "plan.slot", (torch.int32,), p.n_tokens * p.top_k)
-    _dev(plan.packed_src, "plan.packed_src", (torch.int32,), moe_max_rows(p))
-    _dev(plan.workspace, "plan.workspace", (torch.uint8,), moe_workspace_bytes(p))
-    pl = plan.as_struct()
-    rc = lib.moe_dispatch_plan(ctypes.byref(p), ids, ctypes.byref(pl),
+    r_max, _, _, ws = _sizes(p)
+    npairs = p.n_tokens * p.top_k
+    ids = _dev(topk_ids, "topk_ids", (torch.int32,), npairs)
+    _dev(plan.slot, "plan.slot", (torch.int32,), npairs)
+    _dev(plan.packed_src, "plan.packed_src", (torch.int32,), r_max)
+    _dev(plan.workspace, "plan.workspace", (torch.uint8,), ws)
+    rc = lib.moe_dispatch_plan(ctypes.byref(p), ids, ctypes.byref(plan.as_struct()),
                                plan.workspace.data_ptr(), _stream(stream))
     _checked(rc, "moe_dispatch_plan")
 
 
 def moe_dispatch(p: Problem, plan: PlanBuffers, hidden: torch.Tensor, payload: torch.Tensor,
                  scales: torch.Tensor | None, stream=None) -> None:
-    r_max = moe_max_rows(p)
+    r_max, pb, sb, _ = _sizes(p)
     x = _dev(hidden, "hidden", _BF16, p.n_tokens * p.hidden)
-    pb = moe_payload_row_bytes(p)
-    sb = moe_scale_row_bytes(p)
     if payload.numel() * payload.element_size() < r_max * pb:
         raise ValueError("payload is smaller than R_max rows")
     if scales is not None and scales.numel() * scales.element_size() < r_max * sb:
         raise ValueError("scales is smaller than R_max rows")
-    pay = _dev(payload, "payload", (torch.bfloat16, torch.int16, torch.uint16, torch.uint8,
-                                    torch.float8_e4m3fn))
+    pay = _dev(payload, "payload", _PAYLOAD)
     sc = _dev(scales, "scales", (torch.float32, torch.uint8))
-    pl = plan.as_struct()
-    rc = lib.moe_dispatch(ctypes.byref(p), ctypes.byref(pl), x, pay, sc or None, _stream(stream))
+    rc = lib.moe_dispatch(ctypes.byref(p), ctypes.byref(plan.as_struct()), x, pay, sc or None,
+                          _stream(stream))
     _checked(rc, "moe_dispatch")
 
 
 def moe_combine(p: Problem, plan: PlanBuffers, expert_out: torch.Tensor,
                 topk_weights: torch.Tensor, out: torch.Tensor, stream=None) -> None:
-    y = _dev(expert_out, "expert_out", _BF16, moe_max_rows(p) * p.hidden)
+    r_max = _sizes(p)[0]
+    y = _dev(expert_out, "expert_out", _BF16, r_max * p.hidden)
     w = _dev(topk_weights, "topk_weights", (torch.float32,), p.n_tokens * p.top_k)
     o = _dev(out, "out", _BF16, p.n_tokens * p.hidden)
-    pl = plan.as_struct()
-    rc = lib.moe_combine(ctypes.byref(p), ctypes.byref(pl), y, w, o, _stream(stream))
+    rc = lib.moe_combine(ctypes.byref(p), ctypes.byref(plan.as_struct()), y, w, o,
+                         _stream(stream))
     _checked(rc, "moe_combine")
