@@ -74,13 +74,21 @@ __device__ __forceinline__ uint32_t row16_max(uint32_t v) {
   return v;
 }
 
+// Inclusive prefix sum over the 64 lanes: four row shifts (1, 2, 4, 8) scan
+// each 16-lane row, then row_bcast:15 / row_bcast:31 carry row totals into
+// the rows above.  Lanes shifted in from outside a row read 0.
+template <int CTRL, int ROWMASK, bool BOUND_ZERO>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWMASK, 0xF, BOUND_ZERO);
+}
+
 __device__ __forceinline__ int wave_incl_scan(int v) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int u = __shfl_up(v, d, kWave);
-    if (lane >= d) v += u;
-  }
+  v += dpp_i<0x111, 0xF, true>(v);   // row_shr:1
+  v += dpp_i<0x112, 0xF, true>(v);   // row_shr:2
+  v += dpp_i<0x114, 0xF, true>(v);   // row_shr:4
+  v += dpp_i<0x118, 0xF, true>(v);   // row_shr:8
+  v += dpp_i<0x142, 0xA, false>(v);  // row_bcast:15 -> rows 1 and 3
+  v += dpp_i<0x143, 0xC, false>(v);  // row_bcast:31 -> rows 2 and 3
   return v;
 }
 

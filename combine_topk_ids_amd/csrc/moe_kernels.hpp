@@ -10,17 +10,17 @@ namespace moe {
 
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 64;
-constexpr int kPlanThreads = 256;          // 4 waves
+constexpr int kPlanThreads = 512;          // 8 waves per plan block
 constexpr int kPlanWaves = kPlanThreads / 64;
-constexpr int64_t kSingleBlockPairs = 4096;  // plans this small run in one block
-constexpr int kMaxTiles = 64;              // tiles of the two-kernel plan
 
 // How the (token, k) pairs are split into tiles for the plan kernels.
 struct PlanGeom {
   int64_t npairs;      // N * k
-  int64_t tile_pairs;  // pairs per tile (a multiple of kPlanThreads)
-  int ntiles;          // ceil(npairs / tile_pairs), >= 1
-  bool single;         // one block does count, scan and assignment
+  int tile_tokens;     // whole tokens per tile (at most 2048 pairs)
+  int64_t tile_pairs;  // tile_tokens * k
+  int ntiles;          // ceil(N / tile_tokens), >= 1
+  int subs;            // 512-pair sub-tiles per count tile (assign blocks)
+  bool single;         // one count tile: no separate counting kernel
   int key_bits;        // bits needed for an expert id (ceil(log2 E))
 };
 

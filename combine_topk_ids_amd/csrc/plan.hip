@@ -17,51 +17,62 @@
 //     per-expert histogram read as an [ep_size, E_local] count matrix.
 //   Mojo shmem ep_comm module -- block_prefix_sum (block-wide scan).
 //
-// Design for gfx950.  The pairs t*k+j are cut into tiles of 2048.  Slots
-// must follow flat pair order inside each expert whatever order atomics land
-// in, so every position comes from counts and scans, never from an atomic's
-// return value:
-//   plan_count   (one block per tile) histogram of the tile in LDS -> HBM
-//                [ntiles][E] plus the tile's fault bits.
-//   plan_assign  (one block per tile) every block re-reduces the small
-//                histogram matrix (totals and the prefix over earlier
-//                tiles), scans the padded counts over experts, then each wave
-//                walks its 64-pair chunks in order, ranking equal expert IDs
-//                inside the chunk with a ballot-based match (one ballot per ID
-//                bit) and advancing a per-wave cursor per expert in LDS;
+// Design for gfx950.  Slots must follow flat pair order (t*k + j) inside
+// each expert whatever order atomics land in, so every position comes from
+// counts and scans, never from an atomic's return value.  Pairs are cut
+// into count tiles of at most 2048 pairs (whole tokens) and each count tile
+// into sub-tiles of 512 pairs, one 64-pair chunk per wave of a 512-thread
+// block:
+//   plan_count   (one block per count tile) histogram of the tile -> HBM
+//                [ntiles][E], plus the tile's fault bits.
+//   plan_assign  (one block per sub-tile) sums the histogram columns (each
+//                expert's total and its count in earlier count tiles),
+//                counts the pairs of its own count tile that precede the
+//                sub-tile, scans the padded counts over experts, gives every
+//                wave a base row per expert, and ranks each pair among the
+//                equal IDs of its chunk with ballots (one ballot per ID bit);
 //                block 0 also writes counts, offsets, table and status.
-// A plan of at most 2048 pairs (decode shapes) runs as one block of
-// plan_assign that also does the counting: one launch.
+// Plans of at most 2048 pairs (decode shapes) skip plan_count: the whole
+// problem is one count tile that every plan_assign block counts itself.
 //
 // Latency matters more than bandwidth here (the whole plan moves < 2 MB):
-// each kernel issues all of its global loads first, keeps every
-// intermediate in LDS, and issues its global stores last, so no barrier has
-// to wait for stores to drain.
+// each kernel issues its global loads first, keeps every intermediate in LDS
+// or registers, and issues its global stores last, so no barrier waits for
+// stores to drain; no slot depends on another slot, so there is no serial
+// chain.
 #include "moe_device.hpp"
 #include "moe_kernels.hpp"
 
 namespace moe {
 namespace {
 
-constexpr int kTilePairs = 2048;                       // multiple of kPlanThreads
-constexpr int kPairsPerThread = kTilePairs / kPlanThreads;
-constexpr int kHistBatch = 32;                         // histogram loads in flight per thread
+constexpr int kThreads = kPlanThreads;                  // 8 waves
+constexpr int kWaves = kPlanWaves;
+constexpr int kTilePairs = 2048;                        // count tile, whole tokens
+constexpr int kSubPairs = kThreads;                     // sub-tile: one chunk per wave
+constexpr int kPairsPerThread = kTilePairs / kThreads;  // staging loads per thread
+constexpr int kHistBatch = 16;                          // column loads in flight
+static_assert(kMaxExperts <= 2 * kThreads, "the expert scan gives each thread two experts");
 
 struct PlanArgs {
   const int32_t *ids;
+  int64_t n;          // tokens
   int64_t npairs;
   int64_t r_max;
   int64_t cap;
   uint32_t h;
   int k, e, ep, a;
-  int ntiles;
+  int tile_tokens;    // tokens per count tile
+  int ntiles;         // count tiles
+  int subs;           // sub-tiles per count tile
+  int nblocks;        // plan_assign blocks = ntiles * subs
   int key_bits;
   int32_t *counts, *offsets, *dest_counts;
   uint32_t *table;
   int32_t *slot, *packed_src;
   uint32_t *status;
-  int32_t *hist;     // workspace [ntiles][E]
-  uint32_t *tflags;  // workspace [ntiles]
+  int32_t *hist;      // workspace [ntiles][E]
+  uint32_t *tflags;   // workspace [ntiles]
 };
 
 __device__ __forceinline__ int padded(int c, int a) { return ((c + a - 1) / a) * a; }
@@ -70,238 +81,302 @@ __device__ __forceinline__ uint32_t wave_or_bits(uint32_t v) {
   return (ballot(v & 1u) ? 1u : 0u) | (ballot(v & 2u) ? 2u : 0u) | (ballot(v & 4u) ? 4u : 0u);
 }
 
-// Load the tile's IDs into LDS, starting at the first pair of the token that
-// owns pair `begin` (so each token's earlier slots are at hand for the
-// repeated-ID check).  All loads are issued before any is used.  Returns the
-// lead-in length (< k).  The caller places a barrier before reading s_ids.
-__device__ int stage_ids(const PlanArgs &g, int64_t begin, int64_t end, int *s_ids) {
-  const int tid = threadIdx.x;
-  // pair indices fit in 31 bits (checked on the host)
-  const int pre = static_cast<int>(static_cast<uint32_t>(begin) % static_cast<uint32_t>(g.k));
-  const int len = static_cast<int>(end - begin);
+struct Tile {
+  int64_t tok0;   // first token
+  int ntok;       // tokens in the tile
+  int64_t pair0;  // first pair = tok0 * k
+  int len;        // pairs = ntok * k
+};
+
+__device__ __forceinline__ Tile tile_of(const PlanArgs &g, int c, int k) {
+  Tile t;
+  t.tok0 = static_cast<int64_t>(c) * g.tile_tokens;
+  t.ntok = static_cast<int>(min(static_cast<int64_t>(g.tile_tokens), g.n - t.tok0));
+  if (t.ntok < 0) t.ntok = 0;
+  t.pair0 = t.tok0 * k;
+  t.len = t.ntok * k;
+  return t;
+}
+
+// Coalesced load of the first `len` IDs of a tile into LDS (all loads issued
+// first).  The caller places a barrier before s_ids is read.
+__device__ __forceinline__ void stage_ids(const PlanArgs &g, int64_t pair0, int len, int *s_ids) {
   int v[kPairsPerThread];
 #pragma unroll
   for (int u = 0; u < kPairsPerThread; ++u) {
-    const int i = u * kPlanThreads + tid;
-    v[u] = i < len ? g.ids[begin + i] : -1;
+    const int i = u * kThreads + threadIdx.x;
+    v[u] = i < len ? g.ids[pair0 + i] : -1;
   }
-  const int lead = tid < pre ? g.ids[begin - pre + tid] : 0;
 #pragma unroll
   for (int u = 0; u < kPairsPerThread; ++u) {
-    const int i = u * kPlanThreads + tid;
-    if (i < len) s_ids[pre + i] = v[u];
+    const int i = u * kThreads + threadIdx.x;
+    if (i < len) s_ids[i] = v[u];
   }
-  if (tid < pre) s_ids[tid] = lead;
-  return pre;
 }
 
-// Histogram of the valid pairs of [begin, end) into s_cnt (zeroed); returns
-// this thread's BAD_ID / DUP_ID bits.
-__device__ uint32_t count_tile(const PlanArgs &g, int64_t begin, int64_t end, const int *s_ids,
-                               int pre, int *s_cnt) {
+// Histogram of a tile's valid pairs into s_cnt, one thread per token, and
+// (if s_before) of those with tile-relative index < before into s_before;
+// returns this thread's BAD_ID / DUP_ID bits.  With a compile-time k the
+// token's IDs sit in registers for the repeated-ID check.
+template <int KC>
+__device__ uint32_t count_tokens(const PlanArgs &g, const Tile &t, const int *s_ids, int *s_cnt,
+                                 int *s_before, int before) {
   uint32_t fl = 0;
-  const int len = static_cast<int>(end - begin);
-  const uint32_t k = static_cast<uint32_t>(g.k);
-  const uint32_t j0 = static_cast<uint32_t>(pre);  // position in its token of pair `begin`
+  const int E = g.e;
+  const int k = KC > 0 ? KC : g.k;
+  for (int tl = threadIdx.x; tl < t.ntok; tl += kThreads) {
+    if (KC > 0) {
+      int e[KC > 0 ? KC : 1];
 #pragma unroll
-  for (int u = 0; u < kPairsPerThread; ++u) {
-    const int i = u * kPlanThreads + threadIdx.x;
-    if (i >= len) break;
-    const int e = s_ids[pre + i];
-    if (e == -1) continue;
-    if (e < -1 || e >= g.e) {
-      fl |= MOE_STATUS_BAD_ID;
-      continue;
+      for (int j = 0; j < KC; ++j) e[j] = s_ids[tl * KC + j];
+#pragma unroll
+      for (int j = 0; j < KC; ++j) {
+        if (e[j] == -1) continue;
+        if (e[j] < -1 || e[j] >= E) {
+          fl |= MOE_STATUS_BAD_ID;
+          continue;
+        }
+#pragma unroll
+        for (int jj = 0; jj < j; ++jj)
+          if (e[jj] == e[j]) fl |= MOE_STATUS_DUP_ID;
+        atomicAdd(&s_cnt[e[j]], 1);
+        if (s_before && tl * KC + j < before) atomicAdd(&s_before[e[j]], 1);
+      }
+    } else {
+      const int *row = s_ids + tl * k;
+      for (int j = 0; j < k; ++j) {
+        const int e = row[j];
+        if (e == -1) continue;
+        if (e < -1 || e >= E) {
+          fl |= MOE_STATUS_BAD_ID;
+          continue;
+        }
+        for (int jj = 0; jj < j; ++jj)
+          if (row[jj] == e) fl |= MOE_STATUS_DUP_ID;
+        atomicAdd(&s_cnt[e], 1);
+        if (s_before && tl * k + j < before) atomicAdd(&s_before[e], 1);
+      }
     }
-    const int j = static_cast<int>((j0 + static_cast<uint32_t>(i)) % k);
-    for (int q = pre + i - j; q < pre + i; ++q)
-      if (s_ids[q] == e) fl |= MOE_STATUS_DUP_ID;
-    atomicAdd(&s_cnt[e], 1);
   }
   return fl;
 }
 
-__global__ __launch_bounds__(kPlanThreads) void plan_count_kernel(PlanArgs g) {
+template <int KC>
+__global__ __launch_bounds__(kThreads) void plan_count_kernel(PlanArgs g) {
   extern __shared__ int smem[];
   int *s_cnt = smem;        // [E]
-  int *s_ids = smem + g.e;  // [kTilePairs + kMaxTopK]
+  int *s_ids = smem + g.e;  // [kTilePairs]
   __shared__ uint32_t s_fl;
-  const int b = blockIdx.x;
-  const int64_t begin = static_cast<int64_t>(b) * kTilePairs;
-  const int64_t end = min(begin + kTilePairs, g.npairs);
-  const int pre = stage_ids(g, begin, end, s_ids);
-  for (int e = threadIdx.x; e < g.e; e += kPlanThreads) s_cnt[e] = 0;
+  const int k = KC > 0 ? KC : g.k;
+  const int c = blockIdx.x;
+  const Tile t = tile_of(g, c, k);
+  stage_ids(g, t.pair0, t.len, s_ids);
+  for (int e = threadIdx.x; e < g.e; e += kThreads) s_cnt[e] = 0;
   if (threadIdx.x == 0) s_fl = 0;
   __syncthreads();
-  const uint32_t fl = wave_or_bits(count_tile(g, begin, end, s_ids, pre, s_cnt));
+  const uint32_t fl = wave_or_bits(count_tokens<KC>(g, t, s_ids, s_cnt, nullptr, 0));
   if (lane_id() == 0 && fl) atomicOr(&s_fl, fl);
   __syncthreads();
-  int32_t *hrow = g.hist + static_cast<int64_t>(b) * g.e;
-  for (int e = threadIdx.x; e < g.e; e += kPlanThreads) hrow[e] = s_cnt[e];
-  if (threadIdx.x == 0) g.tflags[b] = s_fl;
+  int32_t *hrow = g.hist + static_cast<int64_t>(c) * g.e;
+  for (int e = threadIdx.x; e < g.e; e += kThreads) hrow[e] = s_cnt[e];
+  if (threadIdx.x == 0) g.tflags[c] = s_fl;
 }
 
-template <bool kSingle>
-__global__ __launch_bounds__(kPlanThreads) void plan_assign_kernel(PlanArgs g) {
+// kFused: the whole problem is one count tile, counted here by every block.
+template <int KC, bool kFused>
+__global__ __launch_bounds__(kThreads) void plan_assign_kernel(PlanArgs g) {
   extern __shared__ int smem[];
   const int E = g.e;
-  int *s_tot = smem;                    // [E]   c_e
-  int *s_pre = s_tot + E;               // [E]   pairs of e in tiles before this one
-  int *s_off = s_pre + E;               // [E+1] padded exclusive cumsum
-  int *s_cpre = s_off + E + 1;          // [E+1] unpadded exclusive cumsum
-  int *s_cur = s_cpre + E + 1;          // [kPlanWaves][E] per-wave cursors
-  int *s_ids = s_cur + kPlanWaves * E;  // [kTilePairs + kMaxTopK]
+  int *s_tot = smem;                 // [E]   c_e
+  int *s_pre = s_tot + E;            // [E]   pairs of e before this sub-tile
+  int *s_off = s_pre + E;            // [E+1] padded exclusive cumsum
+  int *s_cpre = s_off + E + 1;       // [E+1] unpadded exclusive cumsum
+  int *s_cur = s_cpre + E + 1;       // [kWaves][E] per-wave counts, then bases
+  int *s_ids = s_cur + kWaves * E;   // [kTilePairs]
+  int *s_red = s_ids + kTilePairs;   // [2][kThreads] partial column sums
   __shared__ uint32_t s_fl;
-  __shared__ int s_scan[2][kPlanWaves];
+  __shared__ int s_scan[2][kWaves];
 
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int k = KC > 0 ? KC : g.k;
   const int b = blockIdx.x;
-  const int64_t begin = static_cast<int64_t>(b) * kTilePairs;
-  const int64_t end = min(begin + kTilePairs, g.npairs);
-  const int len = static_cast<int>(end - begin);
+  const int c = b / g.subs;                       // count tile
+  const int sub0 = (b - c * g.subs) * kSubPairs;  // sub-tile start inside it
+  const Tile t = tile_of(g, c, k);
+  const int sub_len = max(0, min(kSubPairs, t.len - sub0));
 
-  // ---- global loads first: the first batch of the histogram matrix, then
-  // the tile's IDs ---------------------------------------------------------
-  const int total = kSingle ? 0 : g.ntiles * E;
-  int hv[kHistBatch];
+  // ---- global loads: histogram columns first, then the tile's IDs -------
+  // Experts are taken in passes of up to kThreads; inside a pass, `tpe`
+  // threads share an expert and each sums every tpe-th count tile.
+  const int e_pass = min(E, kThreads);
+  const int tpe = kThreads / e_pass;
+  const int grp = tid / e_pass, e_loc = tid - grp * e_pass;
+  int col_tot = 0, col_pre = 0;
+  if (!kFused && grp < tpe) {
+    for (int t0 = grp; t0 < g.ntiles; t0 += kHistBatch * tpe) {
+      int v[kHistBatch];
 #pragma unroll
-  for (int u = 0; u < kHistBatch; ++u) {
-    const int i = u * kPlanThreads + tid;
-    hv[u] = i < total ? g.hist[i] : 0;
-  }
-  const int pre = stage_ids(g, begin, end, s_ids);
-  for (int e = tid; e < E; e += kPlanThreads) {
-    s_tot[e] = 0;
-    s_pre[e] = 0;
-  }
-  for (int i = tid; i < kPlanWaves * E; i += kPlanThreads) s_cur[i] = 0;
-  if (tid == 0) s_fl = 0;
-  __syncthreads();
-
-  uint32_t fl = 0;
-  if (kSingle) {
-    fl = count_tile(g, begin, end, s_ids, pre, s_tot);
-  } else {
-    for (int base = 0; base < total; base += kHistBatch * kPlanThreads) {
-      if (base > 0) {
-#pragma unroll
-        for (int u = 0; u < kHistBatch; ++u) {
-          const int i = base + u * kPlanThreads + tid;
-          hv[u] = i < total ? g.hist[i] : 0;
-        }
+      for (int u = 0; u < kHistBatch; ++u) {
+        const int tt = t0 + u * tpe;
+        v[u] = tt < g.ntiles ? g.hist[static_cast<int64_t>(tt) * E + e_loc] : 0;
       }
 #pragma unroll
       for (int u = 0; u < kHistBatch; ++u) {
-        if (hv[u]) {
-          const int i = base + u * kPlanThreads + tid;
-          const int tile = i / E;
-          const int e = i - tile * E;
-          atomicAdd(&s_tot[e], hv[u]);
-          if (tile < b) atomicAdd(&s_pre[e], hv[u]);
-        }
+        col_tot += v[u];
+        col_pre += (t0 + u * tpe < c) ? v[u] : 0;
       }
     }
-    for (int i = tid; i < g.ntiles; i += kPlanThreads) fl |= g.tflags[i];
   }
-  // per-wave counts of this tile's pairs (cursor bases come later)
-  // pairs per wave: the tile split evenly over the waves in 64-pair chunks
-  const int wp = ((len + kPlanWaves * kWave - 1) / (kPlanWaves * kWave)) * kWave;
-  const int wb = wave * wp, we = min(wb + wp, len);
+  uint32_t fl = 0;
+  if (!kFused)
+    for (int i = tid; i < g.ntiles; i += kThreads) fl |= g.tflags[i];
+  // fused: the whole tile (for totals); otherwise up to the sub-tile's end
+  stage_ids(g, t.pair0, kFused ? t.len : sub0 + sub_len, s_ids);
+  for (int e = tid; e < E; e += kThreads) {
+    s_tot[e] = 0;
+    s_pre[e] = 0;
+  }
+  for (int i = tid; i < kWaves * E; i += kThreads) s_cur[i] = 0;
+  if (tid == 0) s_fl = 0;
+  if (!kFused) {
+    s_red[tid] = grp < tpe ? col_tot : 0;
+    s_red[kThreads + tid] = grp < tpe ? col_pre : 0;
+  }
+  __syncthreads();
+
+  // ---- c_e totals and counts of the pairs before this sub-tile -----------
+  if (kFused) {
+    fl = count_tokens<KC>(g, t, s_ids, s_tot, s_pre, sub0);
+  } else {
+    // pairs of this count tile ahead of the sub-tile
+#pragma unroll
+    for (int u = 0; u < kPairsPerThread; ++u) {
+      const int i = u * kThreads + tid;
+      if (i < sub0) {
+        const int e = s_ids[i];
+        if (e >= 0 && e < E) atomicAdd(&s_pre[e], 1);
+      }
+    }
+    for (int pass = 0; pass * e_pass < E; ++pass) {
+      if (pass > 0) {  // E > kThreads: sum the columns of the next experts
+        __syncthreads();
+        const int e = pass * e_pass + e_loc;
+        int ct = 0, cp = 0;
+        if (grp < tpe && e < E)
+          for (int tt = grp; tt < g.ntiles; tt += tpe) {
+            const int v = g.hist[static_cast<int64_t>(tt) * E + e];
+            ct += v;
+            cp += tt < c ? v : 0;
+          }
+        s_red[tid] = ct;
+        s_red[kThreads + tid] = cp;
+        __syncthreads();
+      }
+      if (tid < e_pass && pass * e_pass + tid < E) {
+        int ct = 0, cp = 0;
+        for (int q = 0; q < tpe; ++q) {
+          ct += s_red[q * e_pass + tid];
+          cp += s_red[kThreads + q * e_pass + tid];
+        }
+        s_tot[pass * e_pass + tid] = ct;
+        atomicAdd(&s_pre[pass * e_pass + tid], cp);
+      }
+    }
+  }
+  // this wave's chunk: IDs into registers, per-wave counts into LDS
+  const int i_loc = sub0 + wave * kWave + lane;  // tile-relative pair index
+  const bool in = wave * kWave + lane < sub_len;
+  const int ev = in ? s_ids[i_loc] : -1;
+  const bool valid = ev >= 0 && ev < E;
   int *cur = s_cur + wave * E;
-  for (int i = wb + lane; i < we; i += kWave) {
-    const int e = s_ids[pre + i];
-    if (e >= 0 && e < E) atomicAdd(&cur[e], 1);
-  }
+  if (valid) atomicAdd(&cur[ev], 1);
   fl = wave_or_bits(fl);
   if (lane == 0 && fl) atomicOr(&s_fl, fl);
   __syncthreads();
 
   // ---- padded and unpadded exclusive scans over experts -----------------
+  // thread tid owns experts 2*tid and 2*tid+1 (E <= 1024 = 2 * kThreads)
   {
-    const int per = (E + kPlanThreads - 1) / kPlanThreads;
-    const int e0 = min(tid * per, E), e1 = min(e0 + per, E);
-    int sp = 0, sc = 0;
-    for (int e = e0; e < e1; ++e) {
-      const int c = s_tot[e];
-      sc += c;
-      sp += padded(c, g.a);
-    }
-    const int ip = wave_incl_scan(sp), ic = wave_incl_scan(sc);
+    const int e0 = 2 * tid;
+    const int c0 = e0 < E ? s_tot[e0] : 0;
+    const int c1 = e0 + 1 < E ? s_tot[e0 + 1] : 0;
+    const int p0 = padded(c0, g.a), p1 = padded(c1, g.a);
+    const int ip = wave_incl_scan(p0 + p1), ic = wave_incl_scan(c0 + c1);
     if (lane == kWave - 1) {
       s_scan[0][wave] = ip;
       s_scan[1][wave] = ic;
     }
     __syncthreads();
-    int xp = ip - sp, xc = ic - sc;
-    for (int w = 0; w < wave; ++w) {
-      xp += s_scan[0][w];
-      xc += s_scan[1][w];
+    int xp = ip - (p0 + p1), xc = ic - (c0 + c1);
+    int tp = 0, tc = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const int sp = s_scan[0][w], sc = s_scan[1][w];
+      xp += w < wave ? sp : 0;
+      xc += w < wave ? sc : 0;
+      tp += sp;
+      tc += sc;
     }
-    for (int e = e0; e < e1; ++e) {
-      const int c = s_tot[e];
-      s_off[e] = xp;
-      s_cpre[e] = xc;
-      xp += padded(c, g.a);
-      xc += c;
+    if (e0 < E) {
+      s_off[e0] = xp;
+      s_cpre[e0] = xc;
+    }
+    if (e0 + 1 < E) {
+      s_off[e0 + 1] = xp + p0;
+      s_cpre[e0 + 1] = xc + c0;
     }
     if (tid == 0) {
-      int tp = 0, tc = 0;
-      for (int w = 0; w < kPlanWaves; ++w) {
-        tp += s_scan[0][w];
-        tc += s_scan[1][w];
-      }
       s_off[E] = tp;
       s_cpre[E] = tc;
     }
   }
   __syncthreads();
 
-  // ---- cursor bases: offset + earlier tiles + earlier waves of this tile --
-  for (int e = tid; e < E; e += kPlanThreads) {
+  // ---- per-wave base rows: offset + earlier pairs + earlier waves --------
+  // one thread per expert column: read the wave counts, write the bases
+  for (int e = tid; e < E; e += kThreads) {
+    int cw[kWaves];
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) cw[w] = s_cur[w * E + e];
     int run = s_off[e] + s_pre[e];
 #pragma unroll
-    for (int w = 0; w < kPlanWaves; ++w) {
-      const int c = s_cur[w * E + e];
+    for (int w = 0; w < kWaves; ++w) {
       s_cur[w * E + e] = run;
-      run += c;
+      run += cw[w];
     }
   }
-  // capacity check (block 0 only needs it; cheap everywhere)
   const int L = E / g.ep;
   uint32_t cap = 0;
-  for (int r = tid; r < g.ep; r += kPlanThreads)
+  for (int r = tid; r < g.ep; r += kThreads)
     if (s_cpre[(r + 1) * L] - s_cpre[r * L] > g.cap) cap = MOE_STATUS_CAPACITY;
   cap = wave_or_bits(cap);
   if (lane == 0 && cap) atomicOr(&s_fl, cap);
+  // rank among the equal IDs of this chunk: one ballot per ID bit, a lane
+  // keeping the lanes whose bit matches its own
+  uint64_t m = ballot(valid);
+  for (int bt = 0; bt < g.key_bits; ++bt) {
+    const bool set = (ev >> bt) & 1;
+    const uint64_t ones = ballot(set);
+    m &= set ? ones : ~ones;
+  }
+  const int rank = lanes_below(m);
   __syncthreads();
 
   // ---- stores only from here on -------------------------------------------
-  // stable slots: walk this wave's pairs in 64-pair chunks, in order
-  const uint32_t k = static_cast<uint32_t>(g.k);
-  for (int i0 = wb; i0 < we; i0 += kWave) {
-    const int i = i0 + lane;
-    const bool in = i < we;
-    const int e = in ? s_ids[pre + i] : -1;
-    const bool valid = in && e >= 0 && e < E;
+  if (in) {
     int sl = -1;
-    const uint64_t act = ballot(valid);
     if (valid) {
-      const uint64_t m = match_any(static_cast<uint32_t>(e), g.key_bits, act);
-      const int r = lanes_below(m);
-      const int base = cur[e];
-      sl = base + r;
-      if (r == 0) cur[e] = base + __popcll(m);
-      const uint32_t p = static_cast<uint32_t>(begin + i);
-      g.packed_src[sl] = static_cast<int32_t>(p / k);
+      sl = cur[ev] + rank;
+      g.packed_src[sl] = static_cast<int32_t>(t.tok0 + i_loc / k);
     }
-    if (in) g.slot[begin + i] = sl;
+    g.slot[t.pair0 + i_loc] = sl;
   }
 
   // block 0: counts, offsets, per-rank table, status
   if (b == 0) {
-    for (int e = tid; e < E; e += kPlanThreads) {
+    for (int e = tid; e < E; e += kThreads) {
       g.counts[e] = s_tot[e];
       g.offsets[e] = s_off[e];
     }
@@ -309,7 +384,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_assign_kernel(PlanArgs g) {
       g.offsets[E] = s_off[E];
       *g.status = s_fl;
     }
-    for (int r = tid; r < g.ep; r += kPlanThreads) {
+    for (int r = tid; r < g.ep; r += kThreads) {
       const int lo = r * L, hi = lo + L;
       const int S = s_cpre[hi] - s_cpre[lo];
       const int P = s_off[hi] - s_off[lo];
@@ -326,15 +401,28 @@ __global__ __launch_bounds__(kPlanThreads) void plan_assign_kernel(PlanArgs g) {
   if (g.a > 1) {
     const int per = g.a - 1;
     const int cand = E * per;
-    for (int q = b * kPlanThreads + tid; q < cand; q += g.ntiles * kPlanThreads) {
+    for (int q = b * kThreads + tid; q < cand; q += g.nblocks * kThreads) {
       const int e = q / per;
       const int r = s_off[e] + s_tot[e] + (q - e * per);
       if (r < s_off[e + 1]) g.packed_src[r] = -1;
     }
   }
-  for (int64_t r = s_off[E] + static_cast<int64_t>(b) * kPlanThreads + tid; r < g.r_max;
-       r += static_cast<int64_t>(g.ntiles) * kPlanThreads)
+  for (int64_t r = s_off[E] + static_cast<int64_t>(b) * kThreads + tid; r < g.r_max;
+       r += static_cast<int64_t>(g.nblocks) * kThreads)
     g.packed_src[r] = -1;
+}
+
+template <int KC>
+void launch_k(const PlanArgs &g, bool fused, int e, hipStream_t stream) {
+  const size_t assign_lds =
+      (static_cast<size_t>(4 + kWaves) * e + 2 + kTilePairs + 2 * kThreads) * sizeof(int);
+  if (fused) {
+    plan_assign_kernel<KC, true><<<g.nblocks, kThreads, assign_lds, stream>>>(g);
+  } else {
+    const size_t count_lds = (static_cast<size_t>(e) + kTilePairs) * sizeof(int);
+    plan_count_kernel<KC><<<g.ntiles, kThreads, count_lds, stream>>>(g);
+    plan_assign_kernel<KC, false><<<g.nblocks, kThreads, assign_lds, stream>>>(g);
+  }
 }
 
 }  // namespace
@@ -342,9 +430,14 @@ __global__ __launch_bounds__(kPlanThreads) void plan_assign_kernel(PlanArgs g) {
 PlanGeom plan_geometry(const moe_problem &p) {
   PlanGeom geo;
   geo.npairs = p.n_tokens * p.top_k;
-  geo.tile_pairs = kTilePairs;
-  geo.ntiles = geo.npairs == 0 ? 1 : static_cast<int>((geo.npairs + kTilePairs - 1) / kTilePairs);
+  geo.tile_tokens = max(1, kTilePairs / p.top_k);
+  geo.tile_pairs = static_cast<int64_t>(geo.tile_tokens) * p.top_k;
+  geo.ntiles = p.n_tokens == 0 ? 1
+                               : static_cast<int>((p.n_tokens + geo.tile_tokens - 1) / geo.tile_tokens);
   geo.single = geo.ntiles == 1;
+  // sub-tiles per count tile: every tile but the last holds tile_pairs pairs
+  const int64_t span = geo.single ? geo.npairs : geo.tile_pairs;
+  geo.subs = span > kSubPairs ? static_cast<int>((span + kSubPairs - 1) / kSubPairs) : 1;
   int bits = 0;
   while ((1 << bits) < p.n_experts) ++bits;
   geo.key_bits = bits;
@@ -363,6 +456,7 @@ hipError_t launch_plan(const moe_problem &p, const int32_t *ids, const moe_plan 
   const PlanGeom geo = plan_geometry(p);
   PlanArgs g;
   g.ids = ids;
+  g.n = p.n_tokens;
   g.npairs = geo.npairs;
   g.r_max = p.n_tokens * p.top_k + static_cast<int64_t>(p.n_experts) * (p.pad_multiple - 1);
   g.cap = p.recv_capacity;
@@ -371,7 +465,10 @@ hipError_t launch_plan(const moe_problem &p, const int32_t *ids, const moe_plan 
   g.e = p.n_experts;
   g.ep = p.ep;
   g.a = p.pad_multiple;
+  g.tile_tokens = geo.tile_tokens;
   g.ntiles = geo.ntiles;
+  g.subs = geo.subs;
+  g.nblocks = geo.ntiles * geo.subs;
   g.key_bits = geo.key_bits;
   g.counts = plan.expert_counts;
   g.offsets = plan.expert_offsets;
@@ -383,14 +480,13 @@ hipError_t launch_plan(const moe_problem &p, const int32_t *ids, const moe_plan 
   g.hist = static_cast<int32_t *>(workspace);
   g.tflags = geo.single ? nullptr
                         : reinterpret_cast<uint32_t *>(g.hist + static_cast<int64_t>(geo.ntiles) * p.n_experts);
-  const size_t ids_lds = (kTilePairs + kMaxTopK) * sizeof(int);
-  const size_t assign_lds = (8 * static_cast<size_t>(p.n_experts) + 2) * sizeof(int) + ids_lds;
-  if (geo.single) {
-    plan_assign_kernel<true><<<1, kPlanThreads, assign_lds, stream>>>(g);
-  } else {
-    const size_t count_lds = static_cast<size_t>(p.n_experts) * sizeof(int) + ids_lds;
-    plan_count_kernel<<<geo.ntiles, kPlanThreads, count_lds, stream>>>(g);
-    plan_assign_kernel<false><<<geo.ntiles, kPlanThreads, assign_lds, stream>>>(g);
+  switch (p.top_k) {
+    case 1: launch_k<1>(g, geo.single, p.n_experts, stream); break;
+    case 2: launch_k<2>(g, geo.single, p.n_experts, stream); break;
+    case 4: launch_k<4>(g, geo.single, p.n_experts, stream); break;
+    case 6: launch_k<6>(g, geo.single, p.n_experts, stream); break;
+    case 8: launch_k<8>(g, geo.single, p.n_experts, stream); break;
+    default: launch_k<0>(g, geo.single, p.n_experts, stream); break;
   }
   return hipGetLastError();
 }
