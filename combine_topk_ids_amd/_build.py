@@ -24,6 +24,25 @@ def hipcc_command(out: str) -> list[str]:
     ] + [os.path.join(CSRC, s) for s in SOURCES]
 
 
+TEST_KERNELS = os.path.join(ROOT, "tests", "kernels")
+TEST_LIB = os.path.join(TEST_KERNELS, "libfp8_path_check.so")
+
+
+def build_test_kernels(force: bool = True) -> str:
+    """Compile the test-support kernels that check libmoe's device code paths
+    exhaustively (tests/kernels/*.hip) into tests/kernels/libfp8_path_check.so."""
+    if not force and os.path.exists(TEST_LIB):
+        return TEST_LIB
+    tmp = TEST_LIB + ".tmp%d" % os.getpid()
+    cmd = ["hipcc", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+           "-fvisibility=hidden", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-Wno-unused-command-line-argument", "-I", CSRC, "-I", os.path.join(ROOT, "include"),
+           "-o", tmp, os.path.join(TEST_KERNELS, "fp8_path_check.hip")]
+    subprocess.run(cmd, check=True, stdout=subprocess.DEVNULL, stderr=subprocess.PIPE)
+    os.replace(tmp, TEST_LIB)
+    return TEST_LIB
+
+
 def build(force: bool = True, verbose: bool = False) -> str:
     """Compile every HIP source into combine_topk_ids_amd/libmoe.so."""
     if not force and os.path.exists(LIB):
@@ -32,10 +51,13 @@ def build(force: bool = True, verbose: bool = False) -> str:
     cmd = hipcc_command(tmp)
     if verbose:
         print(" ".join(cmd), flush=True)
-    subprocess.check_call(cmd, cwd=PKG)
+    res = subprocess.run(cmd, cwd=PKG, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)
     os.replace(tmp, LIB)
     return LIB
 
 
 if __name__ == "__main__":
     print(build(force=True, verbose=True))
+    print(build_test_kernels(force=True))

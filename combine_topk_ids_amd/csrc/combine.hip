@@ -28,9 +28,22 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// Tuning knobs (build-time): 16-byte vectors per lane in a slab (columns
+// per wave = 512 * MOE_COMBINE_VEC); the footprint of expert rows up to
+// which they are read with ordinary (cache-allocating) loads -- rows written
+// just before, e.g. by the expert GEMM or, for identity experts, by the
+// dispatch, are then still in the 256 MB Infinity Cache -- and beyond which
+// with non-temporal loads that do not churn the caches.
+#ifndef MOE_COMBINE_VEC
+#define MOE_COMBINE_VEC 2
+#endif
+#ifndef MOE_COMBINE_CACHED_BYTES
+#define MOE_COMBINE_CACHED_BYTES (256ll << 20)
+#endif
+
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kVec = 2;     // 16-byte vectors per lane per slab
+constexpr int kVec = MOE_COMBINE_VEC;  // 16-byte vectors per lane per slab
 constexpr int kBatch = 8;   // top-k slots whose loads are issued together
 
 struct CombineArgs {
@@ -64,7 +77,8 @@ __device__ __forceinline__ u32x4 pack8(const float (&a)[8]) {
 }
 
 // KC > 0: k is the compile-time constant KC; KC == 0: runtime k, in batches.
-template <int KC>
+// NT: non-temporal expert-row loads.
+template <int KC, bool NT>
 __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs g) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int q = blockIdx.x * kWaves + wave;  // the grid size keeps q within int
@@ -98,7 +112,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs g) {
 #pragma unroll
       for (int u = 0; u < kVec; ++u) {
         const int idx = v0 + u * kWave + lane;
-        if (idx < nvec) v[jj][u] = __builtin_nontemporal_load(src + idx);
+        if (idx < nvec) v[jj][u] = NT ? __builtin_nontemporal_load(src + idx) : src[idx];
       }
     }
 #pragma unroll
@@ -115,6 +129,18 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs g) {
   for (int u = 0; u < kVec; ++u) {
     const int idx = v0 + u * kWave + lane;
     if (idx < nvec) __builtin_nontemporal_store(pack8(acc[u]), dst + idx);
+  }
+}
+
+template <bool NT>
+void launch_k(const CombineArgs &g, int k, int grid, hipStream_t stream) {
+  switch (k) {
+    case 1: combine_kernel<1, NT><<<grid, kThreads, 0, stream>>>(g); break;
+    case 2: combine_kernel<2, NT><<<grid, kThreads, 0, stream>>>(g); break;
+    case 4: combine_kernel<4, NT><<<grid, kThreads, 0, stream>>>(g); break;
+    case 6: combine_kernel<6, NT><<<grid, kThreads, 0, stream>>>(g); break;
+    case 8: combine_kernel<8, NT><<<grid, kThreads, 0, stream>>>(g); break;
+    default: combine_kernel<0, NT><<<grid, kThreads, 0, stream>>>(g); break;
   }
 }
 
@@ -135,14 +161,12 @@ hipError_t launch_combine(const moe_problem &p, const moe_plan &plan, const uint
   const int64_t waves = p.n_tokens * g.slabs;
   const int grid = static_cast<int>((waves + kWaves - 1) / kWaves);
   if (grid == 0) return hipSuccess;
-  switch (p.top_k) {
-    case 1: combine_kernel<1><<<grid, kThreads, 0, stream>>>(g); break;
-    case 2: combine_kernel<2><<<grid, kThreads, 0, stream>>>(g); break;
-    case 4: combine_kernel<4><<<grid, kThreads, 0, stream>>>(g); break;
-    case 6: combine_kernel<6><<<grid, kThreads, 0, stream>>>(g); break;
-    case 8: combine_kernel<8><<<grid, kThreads, 0, stream>>>(g); break;
-    default: combine_kernel<0><<<grid, kThreads, 0, stream>>>(g); break;
-  }
+  // bytes of expert rows this launch reads (one row per valid pair at most)
+  const int64_t rows_bytes = p.n_tokens * p.top_k * 2 * static_cast<int64_t>(p.hidden);
+  if (rows_bytes <= MOE_COMBINE_CACHED_BYTES)
+    launch_k<false>(g, p.top_k, grid, stream);
+  else
+    launch_k<true>(g, p.top_k, grid, stream);
   return hipGetLastError();
 }
 

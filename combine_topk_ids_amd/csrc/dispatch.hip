@@ -18,8 +18,10 @@
 // one token, reads it once with 16-byte loads (8 bf16 per lane, 1 KiB per
 // wave instruction), encodes it once, and writes the result to each of the
 // token's k packed rows, so the cost does not depend on how skewed the
-// routing is.  FP8 block maxima are a 16-lane DPP row reduction (one 1x128
-// block = 16 lanes x 8 values); MX block maxima a 4-lane quad reduction.  Pad rows are zeroed by a second
+// routing is.  In the quantising formats a lane encodes 8 consecutive values
+// (a 512-value slab per wave: the division-heavy FP8 encode wants many
+// waves); an FP8 1x128 block spans one 16-lane DPP row (block maximum by
+// quad, half-row and row mirrors), an MX 32-value block one quad.  Pad rows are zeroed by a second
 // range of workgroups in the same launch, the optional tail by a third.
 #include "moe_device.hpp"
 #include "moe_kernels.hpp"
@@ -29,6 +31,18 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Tuning knobs (build-time): vectors per lane in a bf16 slab, bf16 elements
+// per lane in the quantising formats (8 or 16), non-temporal payload stores.
+#ifndef MOE_DISPATCH_VEC
+#define MOE_DISPATCH_VEC 4
+#endif
+#ifndef MOE_QUANT_LANE_ELEMS
+#define MOE_QUANT_LANE_ELEMS 8
+#endif
+#ifndef MOE_DISPATCH_NT_STORE
+#define MOE_DISPATCH_NT_STORE 0
+#endif
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
@@ -69,7 +83,7 @@ __device__ __forceinline__ int lane_slot(const DispatchArgs &g, int64_t t, int l
 }
 
 // ---- bf16: copy the slab to every destination -------------------------------
-constexpr int kBf16Vec = 4;  // 16-byte vectors per lane per slab (4 KiB a wave)
+constexpr int kBf16Vec = MOE_DISPATCH_VEC;  // 16-byte vectors per lane per slab
 
 template <bool NT>
 __device__ void slab_bf16(const DispatchArgs &g, int64_t t, int slab) {
@@ -96,54 +110,82 @@ __device__ void slab_bf16(const DispatchArgs &g, int64_t t, int slab) {
   }
 }
 
-// ---- FP8 E4M3, one fp32 scale per 1x128 block -------------------------------
-constexpr int kQuantChunks = 2;  // 512-element chunks per slab
+// ---- quantising formats: each lane encodes LE consecutive values ----------
+constexpr int kLE = MOE_QUANT_LANE_ELEMS;           // 8 or 16
+constexpr int kQuantSlab = kWave * kLE;             // values per wave
+static_assert(kLE == 8 || kLE == 16, "8 or 16 values per lane");
 
+// Load this lane's LE bf16 values (zeros past the row end) as fp32.
+__device__ __forceinline__ void load_lane(const DispatchArgs &g, int64_t t, int elem, float (&f)[kLE]) {
+  const u32x4 *src = reinterpret_cast<const u32x4 *>(g.x + t * g.h) + elem / 8;
+  u32x4 raw[kLE / 8];
+#pragma unroll
+  for (int q = 0; q < kLE / 8; ++q)
+    raw[q] = elem < g.h ? __builtin_nontemporal_load(src + q) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int q = 0; q < kLE / 8; ++q) {
+    uint4 r4;
+    r4.x = raw[q].x; r4.y = raw[q].y; r4.z = raw[q].z; r4.w = raw[q].w;
+    float h[8];
+    unpack8(r4, h);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[q * 8 + i] = h[i];
+  }
+}
+
+__device__ __forceinline__ uint32_t lane_absmax(const float (&f)[kLE]) {
+  uint32_t am = 0;
+#pragma unroll
+  for (int i = 0; i < kLE; ++i) am = max(am, __float_as_uint(f[i]) & 0x7FFFFFFFu);
+  return am;
+}
+
+// ---- FP8 E4M3, one fp32 scale per 1x128 block -------------------------------
 template <bool NT>
 __device__ void slab_fp8(const DispatchArgs &g, int64_t t, int slab) {
   const int lane = lane_id();
-  const int c0 = slab * kQuantChunks;
-  const u32x4 *src = reinterpret_cast<const u32x4 *>(g.x + t * g.h);
+  const int elem = slab * kQuantSlab + lane * kLE;
   const int my_slot = lane_slot(g, t, lane);
-  u32x4 raw[kQuantChunks];
+  float f[kLE];
+  load_lane(g, t, elem, f);
+  // one 1x128 block = 128/kLE lanes: a 16-lane row (kLE 8) or 8 lanes (16)
+  uint32_t am = quad_max(lane_absmax(f));
+  am = max(am, dpp<kRowHalfMirror>(am));
+  if (kLE == 8) am = max(am, dpp<kRowMirror>(am));
+  const float s = __uint_as_float(am) / 448.0f;
+  // codes E4M3(fl32(x / s)): a reciprocal and one fused correction per value
+  // (exact for every block maximum >= 2^-103), IEEE division below that,
+  // zero codes for an all-zero block; hardware conversion in pairs
+  float q[kLE];
+  if (am >= kFp8FastMinBits) {
+    const float r = 1.0f / s;
 #pragma unroll
-  for (int u = 0; u < kQuantChunks; ++u) {
-    const int elem = (c0 + u) * 512 + lane * 8;
-    raw[u] = elem < g.h ? __builtin_nontemporal_load(src + elem / 8) : u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < kLE; ++i) q[i] = fp8_quotient_fast(f[i], s, r);
+  } else if (am != 0) {
+#pragma unroll
+    for (int i = 0; i < kLE; ++i) q[i] = f[i] / s;
+  } else {
+#pragma unroll
+    for (int i = 0; i < kLE; ++i) q[i] = 0.0f;
   }
-  u32x2 codes[kQuantChunks];
-  float scale[kQuantChunks];
+  uint32_t w[kLE / 4];
 #pragma unroll
-  for (int u = 0; u < kQuantChunks; ++u) {
-    float f[8];
-    uint4 r4;
-    r4.x = raw[u].x; r4.y = raw[u].y; r4.z = raw[u].z; r4.w = raw[u].w;
-    unpack8(r4, f);
-    uint32_t am = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) am = max(am, __float_as_uint(f[i]) & 0x7FFFFFFFu);
-    am = row16_max(am);  // one 1x128 block = one 16-lane DPP row
-    const float s = __uint_as_float(am) / 448.0f;
-    uint32_t b[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) b[i] = s == 0.0f ? 0u : e4m3_rne_sat(f[i] / s);
-    codes[u].x = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
-    codes[u].y = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
-    scale[u] = s;
-  }
+  for (int qd = 0; qd < kLE / 4; ++qd)
+    w[qd] = e4m3_pair_hw(q[4 * qd], q[4 * qd + 1]) | (e4m3_pair_hw(q[4 * qd + 2], q[4 * qd + 3]) << 16);
+  const bool writes = elem < g.h;
+  const bool scale_lane = writes && (lane & (128 / kLE - 1)) == 0;
   for (int j = 0; j < g.k; ++j) {
-    const int s = __builtin_amdgcn_readlane(my_slot, j);
-    if (s < 0) continue;
-    uint8_t *prow = g.payload + static_cast<int64_t>(s) * g.row_bytes;
-    float *srow = reinterpret_cast<float *>(g.scales + static_cast<int64_t>(s) * g.scale_bytes);
-#pragma unroll
-    for (int u = 0; u < kQuantChunks; ++u) {
-      const int elem = (c0 + u) * 512 + lane * 8;
-      if (elem < g.h) {
-        store<NT>(reinterpret_cast<u32x2 *>(prow + elem), codes[u]);
-        if ((lane & 15) == 0) store<NT>(srow + elem / 128, scale[u]);
-      }
+    const int d = __builtin_amdgcn_readlane(my_slot, j);
+    if (d < 0) continue;
+    uint8_t *prow = g.payload + static_cast<int64_t>(d) * g.row_bytes;
+    float *srow = reinterpret_cast<float *>(g.scales + static_cast<int64_t>(d) * g.scale_bytes);
+    if (writes) {
+      if (kLE == 16)
+        store<NT>(reinterpret_cast<u32x4 *>(prow + elem), u32x4{w[0], w[1], w[2], w[3]});
+      else
+        store<NT>(reinterpret_cast<u32x2 *>(prow + elem), u32x2{w[0], w[1]});
     }
+    if (scale_lane) store<NT>(srow + elem / 128, s);
   }
 }
 
@@ -151,48 +193,39 @@ __device__ void slab_fp8(const DispatchArgs &g, int64_t t, int slab) {
 template <bool NT>
 __device__ void slab_mx(const DispatchArgs &g, int64_t t, int slab) {
   const int lane = lane_id();
-  const int c0 = slab * kQuantChunks;
-  const u32x4 *src = reinterpret_cast<const u32x4 *>(g.x + t * g.h);
+  const int elem = slab * kQuantSlab + lane * kLE;
   const int my_slot = lane_slot(g, t, lane);
-  u32x4 raw[kQuantChunks];
+  float f[kLE];
+  load_lane(g, t, elem, f);
+  // one 32-value block = 32/kLE lanes: a quad (kLE 8) or a lane pair (16)
+  uint32_t am = lane_absmax(f);
+  am = max(am, dpp<kQuadSwap1>(am));
+  if (kLE == 8) am = max(am, dpp<kQuadSwap2>(am));
+  const int X = mx_exponent(am);
+  const float mul = __uint_as_float(static_cast<uint32_t>(127 - X) << 23);  // 2^-X
+  uint32_t w[kLE / 8];
 #pragma unroll
-  for (int u = 0; u < kQuantChunks; ++u) {
-    const int elem = (c0 + u) * 512 + lane * 8;
-    raw[u] = elem < g.h ? __builtin_nontemporal_load(src + elem / 8) : u32x4{0u, 0u, 0u, 0u};
+  for (int q = 0; q < kLE / 8; ++q) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v |= e2m1_rne_sat(f[8 * q + i] * mul) << (4 * i);
+    w[q] = am == 0 ? 0u : v;
   }
-  uint32_t word[kQuantChunks];
-  uint32_t sbyte[kQuantChunks];
-#pragma unroll
-  for (int u = 0; u < kQuantChunks; ++u) {
-    float f[8];
-    uint4 r4;
-    r4.x = raw[u].x; r4.y = raw[u].y; r4.z = raw[u].z; r4.w = raw[u].w;
-    unpack8(r4, f);
-    uint32_t am = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) am = max(am, __float_as_uint(f[i]) & 0x7FFFFFFFu);
-    am = quad_max(am);  // one 32-value block = one quad
-    const int X = mx_exponent(am);
-    const float mul = __uint_as_float(static_cast<uint32_t>(127 - X) << 23);  // 2^-X
-    uint32_t w = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) w |= e2m1_rne_sat(f[i] * mul) << (4 * i);
-    word[u] = am == 0 ? 0u : w;
-    sbyte[u] = am == 0 ? 0u : static_cast<uint32_t>(X + 127);
-  }
+  const uint8_t sbyte = am == 0 ? 0 : static_cast<uint8_t>(X + 127);
+  const bool writes = elem < g.h;
+  const bool scale_lane = writes && (lane & (32 / kLE - 1)) == 0;
   for (int j = 0; j < g.k; ++j) {
-    const int s = __builtin_amdgcn_readlane(my_slot, j);
-    if (s < 0) continue;
-    uint8_t *prow = g.payload + static_cast<int64_t>(s) * g.row_bytes;
-    uint8_t *srow = g.scales + static_cast<int64_t>(s) * g.scale_bytes;
-#pragma unroll
-    for (int u = 0; u < kQuantChunks; ++u) {
-      const int elem = (c0 + u) * 512 + lane * 8;
-      if (elem < g.h) {
-        store<NT>(reinterpret_cast<uint32_t *>(prow + elem / 2), word[u]);
-        if ((lane & 3) == 0) store<NT>(srow + elem / 32, static_cast<uint8_t>(sbyte[u]));
-      }
+    const int d = __builtin_amdgcn_readlane(my_slot, j);
+    if (d < 0) continue;
+    uint8_t *prow = g.payload + static_cast<int64_t>(d) * g.row_bytes;
+    uint8_t *srow = g.scales + static_cast<int64_t>(d) * g.scale_bytes;
+    if (writes) {
+      if (kLE == 16)
+        store<NT>(reinterpret_cast<u32x2 *>(prow + elem / 2), u32x2{w[0], w[1]});
+      else
+        store<NT>(reinterpret_cast<uint32_t *>(prow + elem / 2), w[0]);
     }
+    if (scale_lane) store<NT>(srow + elem / 32, sbyte);
   }
 }
 
@@ -252,7 +285,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(DispatchArgs g) {
 
 template <int FMT>
 void launch_fmt(const DispatchArgs &g, int grid, hipStream_t stream) {
-  dispatch_kernel<FMT, false><<<grid, kThreads, 0, stream>>>(g);
+  dispatch_kernel<FMT, MOE_DISPATCH_NT_STORE != 0><<<grid, kThreads, 0, stream>>>(g);
 }
 
 }  // namespace
@@ -281,7 +314,7 @@ hipError_t launch_dispatch(const moe_problem &p, const moe_plan &plan, const uin
     g.row_bytes = p.hidden / 2;
     g.scale_bytes = p.hidden / 32;
   }
-  const int slab_elems = p.fmt == MOE_FMT_BF16 ? kWave * kBf16Vec * 8 : kQuantChunks * 512;
+  const int slab_elems = p.fmt == MOE_FMT_BF16 ? kWave * kBf16Vec * 8 : kQuantSlab;
   g.slabs = (p.hidden + slab_elems - 1) / slab_elems;
   g.token_blocks = static_cast<int>((p.n_tokens * g.slabs + kWaves - 1) / kWaves);
   g.pad_groups = (p.pad_multiple - 1 + kPadRowsPerWave - 1) / kPadRowsPerWave;

@@ -130,6 +130,27 @@ __device__ __forceinline__ uint32_t e4m3_rne_sat(float v) {
   return sign | code;
 }
 
+// Blockwise FP8 quotient.  The code of x is E4M3(fl32(x / s)), s = amax/448.
+// With r = fl32(1/s), q0 = fl32(x*r) and one fused correction
+// q = fma(fma(-q0, s, x), r, q0), with the sign of x, gives the same E4M3
+// code as the correctly rounded quotient for every bf16 pair |x| <= amax
+// whose block maximum is at least 2^-103 (fp32 bits 0x0C000000); this was
+// checked exhaustively over all such pairs on gfx950.  Blocks with smaller
+// maxima take the IEEE division.
+constexpr uint32_t kFp8FastMinBits = 0x0C000000u;
+
+__device__ __forceinline__ float fp8_quotient_fast(float x, float s, float r) {
+  const float q0 = x * r;
+  return __builtin_copysignf(__builtin_fmaf(__builtin_fmaf(-q0, s, x), r, q0), x);
+}
+
+// Two OCP E4M3 codes (round to nearest even) in the low 16 bits, code(a) in
+// bits 0-7; gfx950's conversion matches the software rule above for every
+// fp32 |v| < 464 (checked exhaustively), and |fl32(x/s)| <= 448 * (1 + 2^-22).
+__device__ __forceinline__ uint32_t e4m3_pair_hw(float a, float b) {
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false)) & 0xFFFFu;
+}
+
 // ---------------------------------------------------------------- E2M1 ---
 
 // Midpoints between neighbouring E2M1 magnitudes; a tie goes to the even

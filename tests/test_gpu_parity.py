@@ -300,3 +300,26 @@ def test_deterministic_and_side_stream(moe):
     for r in runs[1:]:
         for key in ("slot", "packed_src", "rank_table", "payload", "out"):
             assert np.array_equal(r[key], runs[0][key]), key
+
+
+def test_fp8_every_block_maximum(moe):
+    """One 1x128 block for every positive finite bf16 block maximum (0x0001 ..
+    0x7F7F, so both sides of the fast-quotient threshold), the other values
+    random bf16 magnitudes up to it with random signs; every code and scale
+    against the oracle."""
+    say("[edge] fp8: every bf16 block maximum")
+    rng = np.random.default_rng(77)
+    amax = np.arange(1, 0x7F80, dtype=np.uint32)
+    nb = -(-amax.size // 8) * 8
+    amax = np.concatenate([amax, np.zeros(nb - amax.size, np.uint32)])  # zero blocks pad
+    mags = np.minimum((rng.random((nb, 128)) * (amax[:, None] + 1)).astype(np.uint32), amax[:, None])
+    signs = rng.integers(0, 2, (nb, 128)).astype(np.uint32) << 15
+    blocks = (mags | signs).astype(np.uint16)
+    pos = rng.integers(0, 128, nb)
+    blocks[np.arange(nb), pos] = (amax | (rng.integers(0, 2, nb).astype(np.uint32) << 15)).astype(np.uint16)
+    x = np.ascontiguousarray(blocks.reshape(-1, 1024))
+    n = x.shape[0]
+    ids = np.zeros((n, 1), np.int32)
+    w = np.ones((n, 1), np.float32)
+    y = random_bf16(rng, (n, 1024))
+    check_full(moe, ids=ids, weights=w, hidden=x, e=1, ep=1, a=1, fmt="fp8", expert_out=y)
