@@ -43,6 +43,9 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #ifndef MOE_DISPATCH_NT_STORE
 #define MOE_DISPATCH_NT_STORE 0
 #endif
+#ifndef MOE_QUANT_CHUNKS
+#define MOE_QUANT_CHUNKS 1
+#endif
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
@@ -112,7 +115,8 @@ __device__ void slab_bf16(const DispatchArgs &g, int64_t t, int slab) {
 
 // ---- quantising formats: each lane encodes LE consecutive values ----------
 constexpr int kLE = MOE_QUANT_LANE_ELEMS;           // 8 or 16
-constexpr int kQuantSlab = kWave * kLE;             // values per wave
+constexpr int kQC = MOE_QUANT_CHUNKS;               // chunks of kWave*kLE per wave
+constexpr int kQuantSlab = kWave * kLE * kQC;       // values per wave
 static_assert(kLE == 8 || kLE == 16, "8 or 16 values per lane");
 
 // Load this lane's LE bf16 values (zeros past the row end) as fp32.
@@ -144,48 +148,55 @@ __device__ __forceinline__ uint32_t lane_absmax(const float (&f)[kLE]) {
 template <bool NT>
 __device__ void slab_fp8(const DispatchArgs &g, int64_t t, int slab) {
   const int lane = lane_id();
-  const int elem = slab * kQuantSlab + lane * kLE;
   const int my_slot = lane_slot(g, t, lane);
-  float f[kLE];
-  load_lane(g, t, elem, f);
-  // one 1x128 block = 128/kLE lanes: a 16-lane row (kLE 8) or 8 lanes (16)
-  uint32_t am = quad_max(lane_absmax(f));
-  am = max(am, dpp<kRowHalfMirror>(am));
-  if (kLE == 8) am = max(am, dpp<kRowMirror>(am));
-  const float s = __uint_as_float(am) / 448.0f;
-  // codes E4M3(fl32(x / s)): a reciprocal and one fused correction per value
-  // (exact for every block maximum >= 2^-103), IEEE division below that,
-  // zero codes for an all-zero block; hardware conversion in pairs
-  float q[kLE];
-  if (am >= kFp8FastMinBits) {
-    const float r = 1.0f / s;
+  float f[kQC][kLE];
 #pragma unroll
-    for (int i = 0; i < kLE; ++i) q[i] = fp8_quotient_fast(f[i], s, r);
-  } else if (am != 0) {
+  for (int c = 0; c < kQC; ++c) load_lane(g, t, slab * kQuantSlab + c * kWave * kLE + lane * kLE, f[c]);
+  uint32_t w[kQC][kLE / 4];
+  float sc[kQC];
 #pragma unroll
-    for (int i = 0; i < kLE; ++i) q[i] = f[i] / s;
-  } else {
+  for (int c = 0; c < kQC; ++c) {
+    // one 1x128 block = 128/kLE lanes: a 16-lane row (kLE 8) or 8 lanes (16)
+    uint32_t am = quad_max(lane_absmax(f[c]));
+    am = max(am, dpp<kRowHalfMirror>(am));
+    if (kLE == 8) am = max(am, dpp<kRowMirror>(am));
+    const float s = __uint_as_float(am) / 448.0f;
+    // codes E4M3(fl32(x / s)): a reciprocal and one fused correction per value
+    // (exact for every block maximum >= 2^-103), IEEE division below that,
+    // zero codes for an all-zero block; hardware conversion in pairs
+    float q[kLE];
+    if (am >= kFp8FastMinBits) {
+      const float r = 1.0f / s;
 #pragma unroll
-    for (int i = 0; i < kLE; ++i) q[i] = 0.0f;
+      for (int i = 0; i < kLE; ++i) q[i] = fp8_quotient_fast(f[c][i], s, r);
+    } else if (am != 0) {
+#pragma unroll
+      for (int i = 0; i < kLE; ++i) q[i] = f[c][i] / s;
+    } else {
+#pragma unroll
+      for (int i = 0; i < kLE; ++i) q[i] = 0.0f;
+    }
+#pragma unroll
+    for (int qd = 0; qd < kLE / 4; ++qd)
+      w[c][qd] = e4m3_pair_hw(q[4 * qd], q[4 * qd + 1]) | (e4m3_pair_hw(q[4 * qd + 2], q[4 * qd + 3]) << 16);
+    sc[c] = s;
   }
-  uint32_t w[kLE / 4];
-#pragma unroll
-  for (int qd = 0; qd < kLE / 4; ++qd)
-    w[qd] = e4m3_pair_hw(q[4 * qd], q[4 * qd + 1]) | (e4m3_pair_hw(q[4 * qd + 2], q[4 * qd + 3]) << 16);
-  const bool writes = elem < g.h;
-  const bool scale_lane = writes && (lane & (128 / kLE - 1)) == 0;
   for (int j = 0; j < g.k; ++j) {
     const int d = __builtin_amdgcn_readlane(my_slot, j);
     if (d < 0) continue;
     uint8_t *prow = g.payload + static_cast<int64_t>(d) * g.row_bytes;
     float *srow = reinterpret_cast<float *>(g.scales + static_cast<int64_t>(d) * g.scale_bytes);
-    if (writes) {
-      if (kLE == 16)
-        store<NT>(reinterpret_cast<u32x4 *>(prow + elem), u32x4{w[0], w[1], w[2], w[3]});
-      else
-        store<NT>(reinterpret_cast<u32x2 *>(prow + elem), u32x2{w[0], w[1]});
+#pragma unroll
+    for (int c = 0; c < kQC; ++c) {
+      const int elem = slab * kQuantSlab + c * kWave * kLE + lane * kLE;
+      if (elem < g.h) {
+        if (kLE == 16)
+          store<NT>(reinterpret_cast<u32x4 *>(prow + elem), u32x4{w[c][0], w[c][1], w[c][2], w[c][3]});
+        else
+          store<NT>(reinterpret_cast<u32x2 *>(prow + elem), u32x2{w[c][0], w[c][1]});
+        if ((lane & (128 / kLE - 1)) == 0) store<NT>(srow + elem / 128, sc[c]);
+      }
     }
-    if (scale_lane) store<NT>(srow + elem / 128, s);
   }
 }
 
@@ -193,39 +204,45 @@ __device__ void slab_fp8(const DispatchArgs &g, int64_t t, int slab) {
 template <bool NT>
 __device__ void slab_mx(const DispatchArgs &g, int64_t t, int slab) {
   const int lane = lane_id();
-  const int elem = slab * kQuantSlab + lane * kLE;
   const int my_slot = lane_slot(g, t, lane);
-  float f[kLE];
-  load_lane(g, t, elem, f);
-  // one 32-value block = 32/kLE lanes: a quad (kLE 8) or a lane pair (16)
-  uint32_t am = lane_absmax(f);
-  am = max(am, dpp<kQuadSwap1>(am));
-  if (kLE == 8) am = max(am, dpp<kQuadSwap2>(am));
-  const int X = mx_exponent(am);
-  const float mul = __uint_as_float(static_cast<uint32_t>(127 - X) << 23);  // 2^-X
-  uint32_t w[kLE / 8];
+  float f[kQC][kLE];
 #pragma unroll
-  for (int q = 0; q < kLE / 8; ++q) {
-    uint32_t v = 0;
+  for (int c = 0; c < kQC; ++c) load_lane(g, t, slab * kQuantSlab + c * kWave * kLE + lane * kLE, f[c]);
+  uint32_t w[kQC][kLE / 8];
+  uint8_t sbyte[kQC];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v |= e2m1_rne_sat(f[8 * q + i] * mul) << (4 * i);
-    w[q] = am == 0 ? 0u : v;
+  for (int c = 0; c < kQC; ++c) {
+    // one 32-value block = 32/kLE lanes: a quad (kLE 8) or a lane pair (16)
+    uint32_t am = lane_absmax(f[c]);
+    am = max(am, dpp<kQuadSwap1>(am));
+    if (kLE == 8) am = max(am, dpp<kQuadSwap2>(am));
+    const int X = mx_exponent(am);
+    const float mul = __uint_as_float(static_cast<uint32_t>(127 - X) << 23);  // 2^-X
+#pragma unroll
+    for (int qd = 0; qd < kLE / 8; ++qd) {
+      uint32_t v = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v |= e2m1_rne_sat(f[c][8 * qd + i] * mul) << (4 * i);
+      w[c][qd] = am == 0 ? 0u : v;
+    }
+    sbyte[c] = am == 0 ? 0 : static_cast<uint8_t>(X + 127);
   }
-  const uint8_t sbyte = am == 0 ? 0 : static_cast<uint8_t>(X + 127);
-  const bool writes = elem < g.h;
-  const bool scale_lane = writes && (lane & (32 / kLE - 1)) == 0;
   for (int j = 0; j < g.k; ++j) {
     const int d = __builtin_amdgcn_readlane(my_slot, j);
     if (d < 0) continue;
     uint8_t *prow = g.payload + static_cast<int64_t>(d) * g.row_bytes;
     uint8_t *srow = g.scales + static_cast<int64_t>(d) * g.scale_bytes;
-    if (writes) {
-      if (kLE == 16)
-        store<NT>(reinterpret_cast<u32x2 *>(prow + elem / 2), u32x2{w[0], w[1]});
-      else
-        store<NT>(reinterpret_cast<uint32_t *>(prow + elem / 2), w[0]);
+#pragma unroll
+    for (int c = 0; c < kQC; ++c) {
+      const int elem = slab * kQuantSlab + c * kWave * kLE + lane * kLE;
+      if (elem < g.h) {
+        if (kLE == 16)
+          store<NT>(reinterpret_cast<u32x2 *>(prow + elem / 2), u32x2{w[c][0], w[c][1]});
+        else
+          store<NT>(reinterpret_cast<uint32_t *>(prow + elem / 2), w[c][0]);
+        if ((lane & (32 / kLE - 1)) == 0) store<NT>(srow + elem / 32, sbyte[c]);
+      }
     }
-    if (scale_lane) store<NT>(srow + elem / 32, sbyte);
   }
 }
 
