@@ -265,11 +265,25 @@ __device__ void zero_row(const DispatchArgs &g, int64_t r) {
   }
 }
 
+// Workgroups are handed to the 8 XCDs round-robin (block b runs on XCD
+// b % 8), each XCD with its own L2.  Renumbering the token range so that
+// consecutive logical blocks share an XCD keeps all waves of a token on one
+// L2, where the partial-line writes of its scale rows (16 bytes per wave and
+// copy) merge before they reach memory.
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ int xcd_local_block(int b, int nblocks) {
+  const int per = nblocks / kXcds, extra = nblocks % kXcds;
+  const int x = b % kXcds, pos = b / kXcds;
+  return x * per + min(x, extra) + pos;
+}
+
 template <int FMT, bool NT>
 __global__ __launch_bounds__(kThreads) void dispatch_kernel(DispatchArgs g) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   int blk = blockIdx.x;
   if (blk < g.token_blocks) {
+    if (FMT != MOE_FMT_BF16) blk = xcd_local_block(blk, g.token_blocks);
     const int q = blk * kWaves + wave;  // the grid size keeps q within int
     const int t = q / g.slabs;
     if (t >= g.n) return;

@@ -323,3 +323,50 @@ def test_fp8_every_block_maximum(moe):
     w = np.ones((n, 1), np.float32)
     y = random_bf16(rng, (n, 1024))
     check_full(moe, ids=ids, weights=w, hidden=x, e=1, ep=1, a=1, fmt="fp8", expert_out=y)
+
+
+def test_graph_capture_replays_match_eager(moe):
+    """The three calls captured in one HIP graph and replayed several times,
+    with eager work and synchronisation between replays: every replay must
+    reproduce the eager outputs (the plan clears nothing with memset nodes)."""
+    say("[graph] capture plan + dispatch + combine, replay 4 times")
+    w = WORKLOADS["decode_mxfp4_n128"]
+    r_max = oracle.max_rows(w.n, w.k, w.e, w.a)
+    inp = make_inputs(w, seed=3, expert_rows=r_max)
+    p = moe.problem(w.n, w.h, w.k, w.e, w.ep, pad_multiple=w.a, fmt=w.fmt, zero_tail=True)
+    plan = moe.alloc_plan(p)
+    payload, scales = moe.alloc_payload(p)
+    x = to_dev_bf16(inp["hidden"])
+    ids = torch.from_numpy(inp["ids"]).cuda()
+    wts = torch.from_numpy(inp["weights"]).cuda()
+    y = to_dev_bf16(inp["expert_out"])
+    out = torch.empty((w.n, w.h), dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        moe.moe_dispatch_plan(p, ids, plan)
+        moe.moe_dispatch(p, plan, x, payload, scales)
+        moe.moe_combine(p, plan, y, wts, out)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (plan.slot, plan.packed_src, payload, scales, out)]
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    with torch.cuda.graph(g):
+        step()
+    for it in range(4):
+        for t in (plan.slot, plan.packed_src, out):
+            t.fill_(-3)
+        payload.view(torch.uint8).fill_(0xEE)
+        scales.fill_(0xEE)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(ref, (plan.slot, plan.packed_src, payload, scales, out)):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), it
+    pl = oracle.plan(inp["ids"], w.e, w.ep, w.a, w.capacity, w.h)
+    assert np.array_equal(plan.slot.cpu().numpy(), pl["slot"])
