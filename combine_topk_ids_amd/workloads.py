@@ -15,6 +15,10 @@ this order):
 3. expert outputs ``[rows, H]`` (only workloads with non-identity experts):
    N(0, 1) in float32, rounded to bf16.
 
+Workloads with ``ranks`` > 1 stand for that many simulated ranks holding N
+tokens each; their logits, hidden rows and expert outputs are drawn the same
+way for all ``ranks * N`` tokens at once (rank s owns tokens s*N .. s*N+N-1).
+
 Top-k: the k largest logits per token, ties to the lower expert index, IDs in
 descending-logit order.  Gate weights: softmax over all E logits in float64,
 keep the top-k probabilities, renormalise them to sum 1, cast to float32.
@@ -39,22 +43,34 @@ class Workload:
     fmt: str          # "bf16" | "fp8" | "mxfp4"
     routing: str      # "softmax" | "zipf"
     experts: str      # "identity" (expert output = dispatched rows) | "random"
-    recv_capacity: int | None = None  # None: dropless N * min(k, E/EP)
+    recv_capacity: int | None = None  # None: dropless (all tokens) * min(k, E/EP)
+    ranks: int = 1    # simulated source ranks, N tokens each (exchange workloads: EP)
 
     @property
     def l(self) -> int:
         return self.e // self.ep
 
     @property
+    def tokens(self) -> int:
+        """Tokens over all simulated source ranks."""
+        return self.n * self.ranks
+
+    @property
+    def exchange(self) -> bool:
+        return self.ranks > 1
+
+    @property
     def capacity(self) -> int:
         if self.recv_capacity is not None:
             return self.recv_capacity
-        return self.n * min(self.k, self.l)
+        return self.tokens * min(self.k, self.l)
 
     def describe(self) -> str:
-        return (f"N={self.n} H={self.h} E={self.e} k={self.k} EP={self.ep} "
+        head = f"{self.ranks} ranks x " if self.exchange else ""
+        tail = f", C={self.capacity} rows per receive buffer" if self.exchange else ""
+        return (f"{head}N={self.n} H={self.h} E={self.e} k={self.k} EP={self.ep} "
                 f"A={self.a} {self.fmt} {self.routing} routing, "
-                f"{self.experts} experts")
+                f"{self.experts} experts{tail}")
 
 
 WORKLOADS = {
@@ -76,6 +92,19 @@ WORKLOADS = {
         # decode-sized MX-FP4 dispatch
         Workload("decode_mxfp4_n128", n=128, h=7168, e=256, k=8, ep=8, a=1,
                  fmt="mxfp4", routing="softmax", experts="random"),
+        # exchange across 8 simulated ranks of the uniform prefill share;
+        # receive buffers of 1.25 * N * k rows (the mean receive is N * k)
+        Workload("exchange_bf16_ep8_n4096", n=4096, h=4096, e=64, k=6, ep=8,
+                 a=1, fmt="bf16", routing="softmax", experts="identity",
+                 recv_capacity=30720, ranks=8),
+        # exchange of FP8 rows across 4 simulated ranks
+        Workload("exchange_fp8_ep4_n2048", n=2048, h=7168, e=256, k=8, ep=4,
+                 a=1, fmt="fp8", routing="softmax", experts="random",
+                 recv_capacity=20480, ranks=4),
+        # decode-sized exchange across 8 simulated ranks
+        Workload("exchange_mxfp4_ep8_n128", n=128, h=7168, e=256, k=8, ep=8,
+                 a=1, fmt="mxfp4", routing="softmax", experts="random",
+                 recv_capacity=1280, ranks=8),
     ]
 }
 
@@ -87,13 +116,14 @@ def to_bf16_bits(a: np.ndarray) -> np.ndarray:
 
 
 def router(rng: np.random.Generator, w: Workload):
-    """Draw logits and return (topk_ids int32 [N,k], weights float32 [N,k])."""
+    """Draw logits and return (topk_ids int32 [T,k], weights float32 [T,k]),
+    T = ranks * N tokens."""
     if w.routing == "softmax":
-        logits = rng.standard_normal((w.n, w.e), dtype=np.float32)
+        logits = rng.standard_normal((w.tokens, w.e), dtype=np.float32)
     elif w.routing == "zipf":
         pop = (np.arange(1, w.e + 1, dtype=np.float64)) ** -1.2
         pop /= pop.sum()
-        noise = rng.standard_normal((w.n, w.e), dtype=np.float32)
+        noise = rng.standard_normal((w.tokens, w.e), dtype=np.float32)
         logits = (np.log(pop)[None, :] + 0.5 * noise.astype(np.float64))
         logits = logits.astype(np.float32)
     else:
@@ -112,13 +142,13 @@ def router(rng: np.random.Generator, w: Workload):
 def make_inputs(w: Workload, seed: int = 0, expert_rows: int | None = None):
     """All inputs of one workload.
 
-    Returns a dict with ``ids`` (int32 [N,k]), ``weights`` (float32 [N,k]),
-    ``hidden`` (uint16 bf16 bits [N,H]) and, for random experts,
+    Returns a dict with ``ids`` (int32 [T,k]), ``weights`` (float32 [T,k]),
+    ``hidden`` (uint16 bf16 bits [T,H]), T = ranks * N, and, for random experts,
     ``expert_out`` (uint16 bf16 bits [expert_rows, H]).
     """
     rng = np.random.Generator(np.random.PCG64(seed))
     ids, weights = router(rng, w)
-    hidden = to_bf16_bits(rng.standard_normal((w.n, w.h), dtype=np.float32))
+    hidden = to_bf16_bits(rng.standard_normal((w.tokens, w.h), dtype=np.float32))
     out = dict(ids=ids, weights=weights, hidden=hidden)
     if w.experts == "random":
         if expert_rows is None:

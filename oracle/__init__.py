@@ -55,6 +55,8 @@ def _load():
         lib.oracle_max_rows.argtypes = [i64, i32, i32, i32]
         lib.oracle_plan.restype = None
         lib.oracle_plan.argtypes = [i64, i32, i32, i32, i32, i64, i64] + [p] * 8
+        lib.oracle_exchange_plan.restype = None
+        lib.oracle_exchange_plan.argtypes = [i64, i32, i32, i32, i64, i64] + [p] * 9
         lib.oracle_encode_row.restype = None
         lib.oracle_encode_row.argtypes = [i32, i64, p, p, p]
         lib.oracle_dispatch.restype = None
@@ -122,6 +124,48 @@ def plan(ids: np.ndarray, n_experts: int, ep: int, pad_multiple: int,
     out["r_used"] = int(out["expert_offsets"][e])
     out["status"] = int(out["status"][0])
     return out
+
+
+def exchange_plan(ids: np.ndarray, n_experts: int, recv_capacity: int,
+                  hidden: int) -> dict:
+    """Receive-side plan for EP simulated ranks.
+
+    ``ids`` is ``int32 [EP, N, k]``: rank s routes its own N tokens.  Returns
+    the count matrix each rank sends, per-rank send counts, what each rank
+    receives per source and local expert, the (4, EP) table of every rank,
+    and the receive row of every pair (``d * C + i`` into the stacked receive
+    buffers ``[EP, C]``) with its inverse ``recv_src`` (``s * N + t``).
+    """
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    ep, n, k = ids.shape
+    e = n_experts
+    cap = recv_capacity
+    out = dict(
+        expert_counts=np.zeros((ep, e), np.int32),
+        send_counts=np.zeros((ep, ep), np.int32),
+        recv_expert_counts=np.zeros((ep, ep, e // ep), np.int32),
+        recv_rows=np.zeros(ep, np.int32),
+        rank_table=np.zeros((ep, 4, ep), np.uint32),
+        recv_slot=np.zeros((ep, n, k), np.int32),
+        recv_src=np.zeros((ep, cap), np.int32),
+        status=np.zeros(ep, np.uint32),
+    )
+    _load().oracle_exchange_plan(n, k, e, ep, cap, hidden, _ptr(ids),
+                                 _ptr(out["expert_counts"]), _ptr(out["send_counts"]),
+                                 _ptr(out["recv_expert_counts"]), _ptr(out["recv_rows"]),
+                                 _ptr(out["rank_table"]), _ptr(out["recv_slot"]),
+                                 _ptr(out["recv_src"]), _ptr(out["status"]))
+    return out
+
+
+def exchange_dispatch(fmt: str, x: np.ndarray, xp: dict, payload=None, scales=None):
+    """Every receive buffer, whole: row ``d*C + i`` holds the encoded row of
+    global token ``recv_src[d, i]`` of the stacked ``x [EP*N, H]``, or zero
+    bytes.  Returns ``(payload [EP*C, ...], scales [EP*C, ...] or None)``."""
+    ep, cap = xp["recv_src"].shape
+    src = np.ascontiguousarray(xp["recv_src"].reshape(-1))
+    pl = dict(packed_src=src, r_max=ep * cap, r_used=ep * cap)
+    return dispatch(fmt, x, pl, zero_tail=True, payload=payload, scales=scales)
 
 
 def encode_rows(fmt: str, x: np.ndarray):

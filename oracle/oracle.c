@@ -35,6 +35,21 @@
  *             - OCP 8-bit Floating Point Specification (E4M3 with no
  *               infinities, max 448) and OCP Microscaling Formats v1.0 (E2M1
  *               element, E8M0 shared scale, X = floor(log2 amax) - emax).
+ *   exchange  EP simulated ranks, each with its own N tokens: the count
+ *             matrix each rank sends, the receive counts and displacements,
+ *             and for every destination rank a receive buffer of C rows that
+ *             holds, source rank by source rank, the rows each source sends
+ *             it (in that source's packed order), then zero rows.
+ *             - NKI permute_a2av API reference: description (the receive
+ *               layout is the packed cumsum of recv_counts; the table's rows
+ *               2-3 are receive counts and displacements) and :return: (C
+ *               rows, source-major packed rows followed by deterministic zero
+ *               padding).
+ *             - DeepSpeed v0.19.4 function index, page 15: SplitPlan entries
+ *               (one all-to-all of the [ep_size, E_local] count matrix; the
+ *               rows a rank receives from it).
+ *             - Mojo ep.dispatch_async.block.scaled.nv struct: recv_count_ptrs
+ *               (tokens received per expert).
  *   combine   out[t] = bf16(sum_j w[t,j] * Y[slot[t,j]]) accumulated in fp32
  *             in j order, one fused multiply-add per term.
  *             - DeepSpeed v0.19.4 function index, page 15: the combine entry
@@ -46,7 +61,8 @@
  * Readings where the pages are silent (expert e lives on rank e / L; rows are
  * ordered expert-major, then token, then k; invalid IDs are masked and
  * flagged; duplicates are dispatched and flagged; zero blocks get zero codes
- * and zero scales; signs of zero are kept) are listed with the design notes.
+ * and zero scales; signs of zero are kept; rows a receive buffer cannot hold
+ * are dropped and flagged) are listed with the design notes.
  *
  * Build: gcc -O2 -std=c99 -fPIC -shared -ffp-contract=off -o liboracle.so
  *        oracle.c -lm     (no fast-math: IEEE division and fmaf are required)
@@ -243,6 +259,114 @@ void oracle_plan(int64_t n, int k, int e_cnt, int ep, int a, int64_t cap,
     }
   }
   *status = st;
+}
+
+/* ------------------------------------------------------------ exchange --- */
+
+/* X1..X5 for EP simulated ranks; rank s owns tokens s*n .. s*n+n-1 of the
+ * stacked arrays.  Arrays: ids[ep][n][k]; expert_counts[ep][E] (row s is the
+ * count matrix rank s sends, viewed as [EP][L]); send_counts[ep][ep] ([s][d]:
+ * rows s sends to d); recv_expert_counts[ep][ep][L] ([d][s][l]: rows d
+ * receives from s for its local expert l); recv_rows[ep] (rows offered to
+ * each receive buffer); table[ep][4][ep] (rank r: row 0 send counts, 1 send
+ * displacements, 2 receive counts, 3 receive displacements, in elements);
+ * recv_slot[ep][n][k] (receive row d*cap + i of each pair, -1 if masked,
+ * invalid or dropped); recv_src[ep][cap] (global source token s*n + t of each
+ * receive row, -1 in the zero tail); status[ep]. */
+void oracle_exchange_plan(int64_t n, int k, int e_cnt, int ep, int64_t cap,
+                          int64_t h, const int32_t *ids, int32_t *expert_counts,
+                          int32_t *send_counts, int32_t *recv_expert_counts,
+                          int32_t *recv_rows, uint32_t *table,
+                          int32_t *recv_slot, int32_t *recv_src,
+                          uint32_t *status) {
+  int l = e_cnt / ep;
+
+  /* X1: every rank validates and counts its own pairs in flat order. */
+  for (int s = 0; s < ep; s++) {
+    const int32_t *sid = ids + (int64_t)s * n * k;
+    int32_t *cnt = expert_counts + (int64_t)s * e_cnt;
+    uint32_t st = 0;
+    for (int x = 0; x < e_cnt; x++) cnt[x] = 0;
+    for (int64_t t = 0; t < n; t++) {
+      for (int j = 0; j < k; j++) {
+        int32_t e = sid[t * k + j];
+        if (e == -1) continue;
+        if (e < -1 || e >= e_cnt) {
+          st |= ORC_BAD_ID;
+          continue;
+        }
+        for (int jj = 0; jj < j; jj++)
+          if (sid[t * k + jj] == e) st |= ORC_DUP_ID;
+        cnt[e] += 1;
+      }
+    }
+    status[s] = st;
+  }
+
+  /* X2: rows rank s sends to rank d = its pairs for d's L experts. */
+  for (int s = 0; s < ep; s++) {
+    for (int d = 0; d < ep; d++) {
+      int64_t c = 0;
+      for (int x = d * l; x < (d + 1) * l; x++) c += expert_counts[(int64_t)s * e_cnt + x];
+      send_counts[(int64_t)s * ep + d] = (int32_t)c;
+    }
+  }
+
+  /* X3: the counts all-to-all.  Rank d receives, from every rank s, the
+   * part of s's count matrix that covers d's experts. */
+  for (int d = 0; d < ep; d++) {
+    int64_t total = 0;
+    for (int s = 0; s < ep; s++) {
+      for (int x = 0; x < l; x++)
+        recv_expert_counts[((int64_t)d * ep + s) * l + x] =
+            expert_counts[(int64_t)s * e_cnt + d * l + x];
+      total += send_counts[(int64_t)s * ep + d];
+    }
+    recv_rows[d] = (int32_t)total;
+    if (total > cap) status[d] |= ORC_CAPACITY;
+  }
+
+  /* X4: each rank's table; receive displacements are the packed cumsum of
+   * its receive counts, source by source. */
+  for (int r = 0; r < ep; r++) {
+    uint32_t *tr = table + (int64_t)r * 4 * ep;
+    uint32_t sd = 0, rd = 0;
+    for (int q = 0; q < ep; q++) {
+      uint32_t sc = (uint32_t)((int64_t)send_counts[(int64_t)r * ep + q] * h);
+      uint32_t rc = (uint32_t)((int64_t)send_counts[(int64_t)q * ep + r] * h);
+      tr[0 * ep + q] = sc;
+      tr[1 * ep + q] = sd;
+      tr[2 * ep + q] = rc;
+      tr[3 * ep + q] = rd;
+      sd += sc;
+      rd += rc;
+    }
+  }
+
+  /* X5: fill each receive buffer: sources in rank order; within a source,
+   * its own packed order (its experts for d in turn, then token, then k).
+   * The first cap rows are kept, later ones dropped; the rest of the buffer
+   * is zero rows (recv_src -1). */
+  for (int64_t i = 0; i < (int64_t)ep * n * k; i++) recv_slot[i] = -1;
+  for (int d = 0; d < ep; d++) {
+    int64_t next = 0;
+    for (int s = 0; s < ep; s++) {
+      const int32_t *sid = ids + (int64_t)s * n * k;
+      for (int x = d * l; x < (d + 1) * l; x++) {
+        for (int64_t t = 0; t < n; t++) {
+          for (int j = 0; j < k; j++) {
+            if (sid[t * k + j] != x) continue;
+            if (next < cap) {
+              recv_slot[((int64_t)s * n + t) * k + j] = (int32_t)((int64_t)d * cap + next);
+              recv_src[(int64_t)d * cap + next] = (int32_t)((int64_t)s * n + t);
+            }
+            next++;
+          }
+        }
+      }
+    }
+    for (int64_t i = next; i < cap; i++) recv_src[(int64_t)d * cap + i] = -1;
+  }
 }
 
 /* ------------------------------------------------------------ encoders --- */
