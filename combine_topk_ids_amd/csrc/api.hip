@@ -38,6 +38,22 @@ int check(const moe_problem *p) {
   return MOE_OK;
 }
 
+// The exchange: EP ranks of N tokens in one launch, receive buffers of C rows.
+int check_exchange(const moe_problem *p) {
+  const int rc = check(p);
+  if (rc != MOE_OK) return rc;
+  if (p->pad_multiple != 1) return MOE_EINVAL;
+  const int64_t ranks = p->ep;
+  const int64_t tokens = p->n_tokens * ranks;  // < 2^31 * 1024: no overflow
+  // global pair and token indices, receive rows: int32; table: uint32 elements
+  if (tokens > INT32_MAX / p->top_k) return MOE_EOVERFLOW;
+  if (p->recv_capacity > INT32_MAX / ranks) return MOE_EOVERFLOW;
+  if (tokens * p->top_k * static_cast<int64_t>(p->hidden) >= (int64_t{1} << 32)) return MOE_EOVERFLOW;
+  if (tokens * static_cast<int64_t>(p->hidden) >= (int64_t{1} << 40)) return MOE_EOVERFLOW;
+  if (tokens * ((static_cast<int64_t>(p->hidden) + 511) / 512) > INT32_MAX / 4) return MOE_EOVERFLOW;
+  return MOE_OK;
+}
+
 int launched(hipError_t err) { return err == hipSuccess ? MOE_OK : MOE_EHIP; }
 
 }  // namespace
@@ -115,6 +131,59 @@ MOE_API int moe_combine(const moe_problem *p, const moe_plan *plan, const uint16
   if (!aligned(expert_out, 16) || !aligned(out, 16) || !aligned(topk_weights, 4) || !aligned(plan->slot, 4))
     return MOE_EALIGN;
   return launched(moe::launch_combine(*p, *plan, expert_out, topk_weights, out, static_cast<hipStream_t>(stream)));
+}
+
+MOE_API int moe_check_exchange(const moe_problem *p) { return check_exchange(p); }
+
+MOE_API size_t moe_exchange_workspace_bytes(const moe_problem *p) {
+  if (check_exchange(p) != MOE_OK) return 0;
+  return moe::exchange_workspace_bytes(*p);
+}
+
+MOE_API int moe_exchange_plan(const moe_problem *p, const int32_t *topk_ids, const moe_exchange *x,
+                              void *workspace, void *stream) {
+  const int rc = check_exchange(p);
+  if (rc != MOE_OK) return rc;
+  if (!x || !x->expert_counts || !x->send_counts || !x->recv_expert_counts || !x->recv_rows ||
+      !x->rank_table || !x->status || !workspace)
+    return MOE_EINVAL;
+  const int64_t pairs = p->n_tokens * p->ep * p->top_k;
+  if (pairs > 0 && (!topk_ids || !x->recv_slot)) return MOE_EINVAL;
+  if (p->recv_capacity > 0 && !x->recv_src) return MOE_EINVAL;
+  if (!aligned(topk_ids, 4) || !aligned(x->expert_counts, 4) || !aligned(x->send_counts, 4) ||
+      !aligned(x->recv_expert_counts, 4) || !aligned(x->recv_rows, 4) || !aligned(x->rank_table, 4) ||
+      !aligned(x->recv_slot, 4) || !aligned(x->recv_src, 4) || !aligned(x->status, 4) ||
+      !aligned(workspace, 256))
+    return MOE_EALIGN;
+  return launched(moe::launch_exchange_plan(*p, topk_ids, *x, workspace, static_cast<hipStream_t>(stream)));
+}
+
+MOE_API int moe_exchange_dispatch(const moe_problem *p, const moe_exchange *x, const uint16_t *hidden,
+                                  void *recv_payload, void *recv_scales, void *stream) {
+  const int rc = check_exchange(p);
+  if (rc != MOE_OK) return rc;
+  if (!x || !x->recv_rows) return MOE_EINVAL;
+  if (p->n_tokens > 0 && (!hidden || !x->recv_slot)) return MOE_EINVAL;
+  const bool quant = p->fmt != MOE_FMT_BF16;
+  if (p->recv_capacity > 0 && (!recv_payload || (quant && !recv_scales))) return MOE_EINVAL;
+  if (!quant && recv_scales) return MOE_EINVAL;
+  if (!aligned(hidden, 16) || !aligned(recv_payload, 16) || !aligned(x->recv_slot, 4) ||
+      !aligned(x->recv_rows, 4) || (p->fmt == MOE_FMT_FP8_E4M3_B128 && !aligned(recv_scales, 4)))
+    return MOE_EALIGN;
+  return launched(moe::launch_exchange_dispatch(*p, *x, hidden, recv_payload, recv_scales,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+MOE_API int moe_exchange_combine(const moe_problem *p, const moe_exchange *x, const uint16_t *expert_out,
+                                 const float *topk_weights, uint16_t *out, void *stream) {
+  const int rc = check_exchange(p);
+  if (rc != MOE_OK) return rc;
+  if (!x) return MOE_EINVAL;
+  if (p->n_tokens > 0 && (!expert_out || !topk_weights || !out || !x->recv_slot)) return MOE_EINVAL;
+  if (!aligned(expert_out, 16) || !aligned(out, 16) || !aligned(topk_weights, 4) || !aligned(x->recv_slot, 4))
+    return MOE_EALIGN;
+  return launched(moe::launch_exchange_combine(*p, *x, expert_out, topk_weights, out,
+                                               static_cast<hipStream_t>(stream)));
 }
 
 MOE_API const char *moe_strerror(int code) {

@@ -30,6 +30,29 @@ size_t plan_workspace_bytes(const moe_problem &p);
 hipError_t launch_plan(const moe_problem &p, const int32_t *ids, const moe_plan &plan,
                        void *workspace, hipStream_t stream);
 
+// Distance, in elements, between consecutive ranks' arrays of a batch of
+// plans made in one launch (one rank per blockIdx.y).
+struct PlanStrides {
+  int64_t pairs = 0;      // topk_ids and slot
+  int64_t rows = 0;       // packed_src
+  int64_t workspace = 0;  // plan workspace, in int32 elements
+  int counts = 0, offsets = 0, dest = 0, table = 0;
+};
+
+// `ranks` independent plans of problem p (each over its own N tokens).
+hipError_t launch_plan_ranks(const moe_problem &p, int ranks, const int32_t *ids,
+                             const moe_plan &plan, const PlanStrides &st, void *workspace,
+                             hipStream_t stream);
+
+// Exchange across p.ep simulated ranks (rank s owns tokens s*N .. s*N+N-1).
+size_t exchange_workspace_bytes(const moe_problem &p);
+hipError_t launch_exchange_plan(const moe_problem &p, const int32_t *ids, const moe_exchange &x,
+                                void *workspace, hipStream_t stream);
+hipError_t launch_exchange_dispatch(const moe_problem &p, const moe_exchange &x, const uint16_t *hidden,
+                                    void *payload, void *scales, hipStream_t stream);
+hipError_t launch_exchange_combine(const moe_problem &p, const moe_exchange &x, const uint16_t *expert_out,
+                                   const float *weights, uint16_t *out, hipStream_t stream);
+
 hipError_t launch_dispatch(const moe_problem &p, const moe_plan &plan, const uint16_t *hidden,
                            void *payload, void *scales, hipStream_t stream);
 

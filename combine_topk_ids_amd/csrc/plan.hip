@@ -73,7 +73,31 @@ struct PlanArgs {
   uint32_t *status;
   int32_t *hist;      // workspace [ntiles][E]
   uint32_t *tflags;   // workspace [ntiles]
+  // Batched plans (one per simulated rank, blockIdx.y = rank): distance
+  // between consecutive ranks' arrays, in elements.  Unused with one rank.
+  int64_t st_pairs;   // ids, slot
+  int64_t st_rows;    // packed_src
+  int64_t st_ws;      // hist and tflags
+  int st_counts, st_offsets, st_dest, st_table;
 };
+
+// Point every per-rank array at this block's rank.
+__device__ __forceinline__ void select_rank(PlanArgs &g) {
+  const int r = blockIdx.y;
+  if (r == 0) return;
+  g.ids += r * g.st_pairs;
+  g.slot += r * g.st_pairs;
+  g.packed_src += r * g.st_rows;
+  g.counts += static_cast<int64_t>(r) * g.st_counts;
+  g.offsets += static_cast<int64_t>(r) * g.st_offsets;
+  g.dest_counts += static_cast<int64_t>(r) * g.st_dest;
+  g.table += static_cast<int64_t>(r) * g.st_table;
+  g.status += r;
+  if (g.hist) {
+    g.hist += r * g.st_ws;
+    g.tflags += r * g.st_ws;
+  }
+}
 
 __device__ __forceinline__ int padded(int c, int a) { return ((c + a - 1) / a) * a; }
 
@@ -163,6 +187,7 @@ __device__ uint32_t count_tokens(const PlanArgs &g, const Tile &t, const int *s_
 
 template <int KC>
 __global__ __launch_bounds__(kThreads) void plan_count_kernel(PlanArgs g) {
+  select_rank(g);
   extern __shared__ int smem[];
   int *s_cnt = smem;        // [E]
   int *s_ids = smem + g.e;  // [kTilePairs]
@@ -185,6 +210,7 @@ __global__ __launch_bounds__(kThreads) void plan_count_kernel(PlanArgs g) {
 // kFused: the whole problem is one count tile, counted here by every block.
 template <int KC, bool kFused>
 __global__ __launch_bounds__(kThreads) void plan_assign_kernel(PlanArgs g) {
+  select_rank(g);
   extern __shared__ int smem[];
   const int E = g.e;
   int *s_tot = smem;                 // [E]   c_e
@@ -413,15 +439,15 @@ __global__ __launch_bounds__(kThreads) void plan_assign_kernel(PlanArgs g) {
 }
 
 template <int KC>
-void launch_k(const PlanArgs &g, bool fused, int e, hipStream_t stream) {
+void launch_k(const PlanArgs &g, bool fused, int e, int ranks, hipStream_t stream) {
   const size_t assign_lds =
       (static_cast<size_t>(4 + kWaves) * e + 2 + kTilePairs + 2 * kThreads) * sizeof(int);
   if (fused) {
-    plan_assign_kernel<KC, true><<<g.nblocks, kThreads, assign_lds, stream>>>(g);
+    plan_assign_kernel<KC, true><<<dim3(g.nblocks, ranks), kThreads, assign_lds, stream>>>(g);
   } else {
     const size_t count_lds = (static_cast<size_t>(e) + kTilePairs) * sizeof(int);
-    plan_count_kernel<KC><<<g.ntiles, kThreads, count_lds, stream>>>(g);
-    plan_assign_kernel<KC, false><<<g.nblocks, kThreads, assign_lds, stream>>>(g);
+    plan_count_kernel<KC><<<dim3(g.ntiles, ranks), kThreads, count_lds, stream>>>(g);
+    plan_assign_kernel<KC, false><<<dim3(g.nblocks, ranks), kThreads, assign_lds, stream>>>(g);
   }
 }
 
@@ -451,8 +477,9 @@ size_t plan_workspace_bytes(const moe_problem &p) {
   return (bytes + 255) & ~static_cast<size_t>(255);
 }
 
-hipError_t launch_plan(const moe_problem &p, const int32_t *ids, const moe_plan &plan,
-                       void *workspace, hipStream_t stream) {
+hipError_t launch_plan_ranks(const moe_problem &p, int ranks, const int32_t *ids,
+                             const moe_plan &plan, const PlanStrides &st, void *workspace,
+                             hipStream_t stream) {
   const PlanGeom geo = plan_geometry(p);
   PlanArgs g;
   g.ids = ids;
@@ -477,18 +504,30 @@ hipError_t launch_plan(const moe_problem &p, const int32_t *ids, const moe_plan 
   g.slot = plan.slot;
   g.packed_src = plan.packed_src;
   g.status = plan.status;
-  g.hist = static_cast<int32_t *>(workspace);
+  g.hist = geo.single ? nullptr : static_cast<int32_t *>(workspace);
   g.tflags = geo.single ? nullptr
                         : reinterpret_cast<uint32_t *>(g.hist + static_cast<int64_t>(geo.ntiles) * p.n_experts);
+  g.st_pairs = st.pairs;
+  g.st_rows = st.rows;
+  g.st_ws = st.workspace;
+  g.st_counts = st.counts;
+  g.st_offsets = st.offsets;
+  g.st_dest = st.dest;
+  g.st_table = st.table;
   switch (p.top_k) {
-    case 1: launch_k<1>(g, geo.single, p.n_experts, stream); break;
-    case 2: launch_k<2>(g, geo.single, p.n_experts, stream); break;
-    case 4: launch_k<4>(g, geo.single, p.n_experts, stream); break;
-    case 6: launch_k<6>(g, geo.single, p.n_experts, stream); break;
-    case 8: launch_k<8>(g, geo.single, p.n_experts, stream); break;
-    default: launch_k<0>(g, geo.single, p.n_experts, stream); break;
+    case 1: launch_k<1>(g, geo.single, p.n_experts, ranks, stream); break;
+    case 2: launch_k<2>(g, geo.single, p.n_experts, ranks, stream); break;
+    case 4: launch_k<4>(g, geo.single, p.n_experts, ranks, stream); break;
+    case 6: launch_k<6>(g, geo.single, p.n_experts, ranks, stream); break;
+    case 8: launch_k<8>(g, geo.single, p.n_experts, ranks, stream); break;
+    default: launch_k<0>(g, geo.single, p.n_experts, ranks, stream); break;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_plan(const moe_problem &p, const int32_t *ids, const moe_plan &plan,
+                       void *workspace, hipStream_t stream) {
+  return launch_plan_ranks(p, 1, ids, plan, PlanStrides{}, workspace, stream);
 }
 
 }  // namespace moe

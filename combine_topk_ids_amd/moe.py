@@ -27,7 +27,9 @@ FLAG_ZERO_TAIL = 1
 # every symbol include/moe.h declares
 EXPORTS = ("moe_check_problem", "moe_max_rows", "moe_payload_row_bytes",
            "moe_scale_row_bytes", "moe_workspace_bytes", "moe_dispatch_plan",
-           "moe_dispatch", "moe_combine", "moe_strerror")
+           "moe_dispatch", "moe_combine", "moe_check_exchange",
+           "moe_exchange_workspace_bytes", "moe_exchange_plan", "moe_exchange_dispatch",
+           "moe_exchange_combine", "moe_strerror")
 
 
 class MoeError(RuntimeError):
@@ -50,6 +52,12 @@ class Plan(ctypes.Structure):
         "packed_src", "status")]
 
 
+class Exchange(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in (
+        "expert_counts", "send_counts", "recv_expert_counts", "recv_rows", "rank_table",
+        "recv_slot", "recv_src", "status")]
+
+
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
@@ -66,6 +74,11 @@ def _load() -> ctypes.CDLL:
         "moe_dispatch_plan": (ctypes.c_int, [P, V, ctypes.POINTER(Plan), V, V]),
         "moe_dispatch": (ctypes.c_int, [P, ctypes.POINTER(Plan), V, V, V, V]),
         "moe_combine": (ctypes.c_int, [P, ctypes.POINTER(Plan), V, V, V, V]),
+        "moe_check_exchange": (ctypes.c_int, [P]),
+        "moe_exchange_workspace_bytes": (ctypes.c_size_t, [P]),
+        "moe_exchange_plan": (ctypes.c_int, [P, V, ctypes.POINTER(Exchange), V, V]),
+        "moe_exchange_dispatch": (ctypes.c_int, [P, ctypes.POINTER(Exchange), V, V, V, V]),
+        "moe_exchange_combine": (ctypes.c_int, [P, ctypes.POINTER(Exchange), V, V, V, V]),
         "moe_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     }
     for name, (res, args) in sig.items():
@@ -256,3 +269,105 @@ def moe_combine(p: Problem, plan: PlanBuffers, expert_out: torch.Tensor,
     rc = lib.moe_combine(ctypes.byref(p), ctypes.byref(plan.as_struct()), y, w, o,
                          _stream(stream))
     _checked(rc, "moe_combine")
+
+
+# ---- exchange across EP simulated ranks ---------------------------------------
+
+def moe_check_exchange(p: Problem) -> int:
+    return int(lib.moe_check_exchange(ctypes.byref(p)))
+
+
+def moe_exchange_workspace_bytes(p: Problem) -> int:
+    return int(lib.moe_exchange_workspace_bytes(ctypes.byref(p)))
+
+
+@dataclasses.dataclass(frozen=True)
+class ExchangeBuffers:
+    """Device tensors an exchange plan is written to, plus its workspace."""
+    expert_counts: torch.Tensor
+    send_counts: torch.Tensor
+    recv_expert_counts: torch.Tensor
+    recv_rows: torch.Tensor
+    rank_table: torch.Tensor
+    recv_slot: torch.Tensor
+    recv_src: torch.Tensor
+    status: torch.Tensor
+    workspace: torch.Tensor
+
+    def as_struct(self) -> Exchange:
+        st = self.__dict__.get("_struct")
+        if st is None:
+            st = Exchange(*(getattr(self, f).data_ptr() for f, _ in Exchange._fields_))
+            self.__dict__["_struct"] = st
+        return st
+
+
+def alloc_exchange(p: Problem, device="cuda") -> ExchangeBuffers:
+    """Buffers of an exchange over p.ep ranks of p.n_tokens tokens each."""
+    ep, e = p.ep, p.n_experts
+    i32 = dict(dtype=torch.int32, device=device)
+    ws = moe_exchange_workspace_bytes(p)
+    if ws == 0:
+        raise MoeError(moe_check_exchange(p), "alloc_exchange")
+    return ExchangeBuffers(
+        expert_counts=torch.empty((ep, e), **i32),
+        send_counts=torch.empty((ep, ep), **i32),
+        recv_expert_counts=torch.empty((ep, ep, e // ep), **i32),
+        recv_rows=torch.empty(ep, **i32),
+        rank_table=torch.empty((ep, 4, ep), **i32),  # uint32 bits in int32 storage
+        recv_slot=torch.empty((ep, p.n_tokens, p.top_k), **i32),
+        recv_src=torch.empty((ep, max(p.recv_capacity, 1)), **i32),
+        status=torch.empty(ep, **i32),
+        workspace=torch.empty(ws, dtype=torch.uint8, device=device),
+    )
+
+
+def alloc_recv_payload(p: Problem, device="cuda"):
+    """(payload, scales) device tensors of EP * C receive rows for p.fmt."""
+    rows = p.ep * p.recv_capacity
+    h = p.hidden
+    if p.fmt == FMT["bf16"]:
+        return torch.empty((rows, h), dtype=torch.bfloat16, device=device), None
+    if p.fmt == FMT["fp8"]:
+        return (torch.empty((rows, h), dtype=torch.uint8, device=device),
+                torch.empty((rows, h // 128), dtype=torch.float32, device=device))
+    return (torch.empty((rows, h // 2), dtype=torch.uint8, device=device),
+            torch.empty((rows, h // 32), dtype=torch.uint8, device=device))
+
+
+def moe_exchange_plan(p: Problem, topk_ids: torch.Tensor, x: ExchangeBuffers, stream=None) -> None:
+    tokens = p.ep * p.n_tokens
+    ids = _dev(topk_ids, "topk_ids", (torch.int32,), tokens * p.top_k)
+    _dev(x.recv_slot, "recv_slot", (torch.int32,), tokens * p.top_k)
+    _dev(x.recv_src, "recv_src", (torch.int32,), p.ep * p.recv_capacity)
+    _dev(x.workspace, "workspace", (torch.uint8,), moe_exchange_workspace_bytes(p))
+    rc = lib.moe_exchange_plan(ctypes.byref(p), ids, ctypes.byref(x.as_struct()),
+                               x.workspace.data_ptr(), _stream(stream))
+    _checked(rc, "moe_exchange_plan")
+
+
+def moe_exchange_dispatch(p: Problem, x: ExchangeBuffers, hidden: torch.Tensor,
+                          payload: torch.Tensor, scales: torch.Tensor | None, stream=None) -> None:
+    _, pb, sb, _ = _sizes(p)
+    rows = p.ep * p.recv_capacity
+    h = _dev(hidden, "hidden", _BF16, p.ep * p.n_tokens * p.hidden)
+    if payload.numel() * payload.element_size() < rows * pb:
+        raise ValueError("payload is smaller than EP * C rows")
+    if scales is not None and scales.numel() * scales.element_size() < rows * sb:
+        raise ValueError("scales is smaller than EP * C rows")
+    pay = _dev(payload, "payload", _PAYLOAD)
+    sc = _dev(scales, "scales", (torch.float32, torch.uint8))
+    rc = lib.moe_exchange_dispatch(ctypes.byref(p), ctypes.byref(x.as_struct()), h, pay,
+                                   sc or None, _stream(stream))
+    _checked(rc, "moe_exchange_dispatch")
+
+
+def moe_exchange_combine(p: Problem, x: ExchangeBuffers, expert_out: torch.Tensor,
+                         topk_weights: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+    tokens = p.ep * p.n_tokens
+    y = _dev(expert_out, "expert_out", _BF16, p.ep * p.recv_capacity * p.hidden)
+    w = _dev(topk_weights, "topk_weights", (torch.float32,), tokens * p.top_k)
+    o = _dev(out, "out", _BF16, tokens * p.hidden)
+    rc = lib.moe_exchange_combine(ctypes.byref(p), ctypes.byref(x.as_struct()), y, w, o,
+                                  _stream(stream))
+    _checked(rc, "moe_exchange_combine")

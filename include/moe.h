@@ -183,6 +183,96 @@ MOE_API int moe_combine(const moe_problem *p, const moe_plan *plan,
                         const uint16_t *expert_out, const float *topk_weights,
                         uint16_t *out, void *stream);
 
+/* ---- exchange across EP simulated ranks ----------------------------------
+ *
+ * One GPU holds the shares of all EP ranks of an expert-parallel group: rank
+ * s owns tokens s*N .. s*N+N-1 of stacked arrays ([EP][N][k], [EP][N][H]).
+ * Each rank routes its own tokens; the exchange itself is simulated by
+ * writing every rank's rows straight into the receive buffer of their
+ * destination rank (expert e lives on rank e / L, L = E/EP).  A receive
+ * buffer has C = recv_capacity rows: the rows of source rank 0, then of rank
+ * 1, ..., each source's rows in its own packed order (expert, then token,
+ * then k), then zero rows up to C.  Rows that would land at or past C are
+ * dropped (their pairs get receive row -1, so combine skips them) and flag
+ * MOE_STATUS_CAPACITY on the receiving rank.
+ *
+ * Problem fields: n_tokens = N per rank; ep = EP ranks, each both a source
+ * and a destination; recv_capacity = C rows per receive buffer;
+ * pad_multiple must be 1 (a source-major receive buffer has no per-expert
+ * padding); flags may hold MOE_FLAG_ZERO_TAIL but the zero rows are always
+ * written.  Also needed: EP*N*k*H < 2^32 (the table counts elements in
+ * uint32) and EP*C < 2^31 (receive rows are int32).
+ *
+ * Passages: NKI permute_a2av API reference, description (the receive layout
+ * is the packed cumsum of recv_counts; table rows 2-3 hold receive counts
+ * and displacements) and :return: ([C, H], source-major packed rows followed
+ * by deterministic zero padding); DeepSpeed v0.19.4 function index, page
+ * 15, SplitPlan entries (one all-to-all of the [ep_size, E_local] count
+ * matrix; the rows a rank receives from it); Mojo
+ * ep.dispatch_async.block.scaled.nv struct, recv_count_ptrs (tokens
+ * received per expert). */
+typedef struct moe_exchange {
+  int32_t *expert_counts;      /* [EP][E] pairs rank s routes to expert e; row
+                                  s, viewed as [EP][L], is the count matrix
+                                  rank s sends in the counts all-to-all      */
+  int32_t *send_counts;        /* [EP][EP] [s][d]: rows rank s sends rank d  */
+  int32_t *recv_expert_counts; /* [EP][EP][L] [d][s][l]: rows rank d receives
+                                  from rank s for its local expert l (what
+                                  the counts all-to-all delivers to d)       */
+  int32_t *recv_rows;          /* [EP] rows offered to each receive buffer,
+                                  the sum over s of send_counts[s][d]; more
+                                  than C flags CAPACITY                      */
+  uint32_t *rank_table;        /* [EP][4][EP] each rank's table, in elements
+                                  (rows * H): 0 send counts, 1 send
+                                  displacements (in the rank's own packed
+                                  order), 2 receive counts from each source,
+                                  3 receive displacements (exclusive cumsum
+                                  of row 2)                                  */
+  int32_t *recv_slot;          /* [EP][N][k] receive row d*C + i of pair
+                                  (s, t, j): row i of rank d's buffer; -1 if
+                                  masked, invalid or dropped                 */
+  int32_t *recv_src;           /* [EP][C] global token s*N + t that each
+                                  receive row holds, -1 for the zero rows    */
+  uint32_t *status;            /* [EP] per rank: BAD_ID / DUP_ID for the IDs
+                                  it routes, CAPACITY for its own buffer     */
+} moe_exchange;
+
+/* MOE_OK if p describes a valid exchange (see above), else the error code
+ * the exchange entry points would return for it. */
+MOE_API int moe_check_exchange(const moe_problem *p);
+
+/* Device scratch bytes moe_exchange_plan needs (always > 0 for a valid
+ * problem; 0 for an invalid one).  256-byte aligned, caller-owned, no
+ * initialisation needed, dead once the plan's kernels have run. */
+MOE_API size_t moe_exchange_workspace_bytes(const moe_problem *p);
+
+/* Exchange plan from topk_ids (device int32 [EP][N][k], -1 = masked): fills
+ * every array of *x.  Deterministic (no output depends on the order in
+ * which atomic operations land). */
+MOE_API int moe_exchange_plan(const moe_problem *p, const int32_t *topk_ids,
+                              const moe_exchange *x, void *workspace,
+                              void *stream);
+
+/* Fill every receive buffer: hidden (device bf16 bits [EP][N][H]) is read
+ * once per token; each kept pair writes encode(hidden[s][t]) to receive row
+ * x->recv_slot[s][t][j] of recv_payload ([EP][C] rows of the format's
+ * payload row) and recv_scales ([EP][C] scale rows; NULL for bf16); every
+ * other row of every buffer is written as zero bytes.  Reads recv_slot and
+ * recv_rows of an exchange plan made for the same problem. */
+MOE_API int moe_exchange_dispatch(const moe_problem *p, const moe_exchange *x,
+                                  const uint16_t *hidden, void *recv_payload,
+                                  void *recv_scales, void *stream);
+
+/* Reverse exchange and combine: out[s][t][c] = bf16_rne( fp32 fused
+ * multiply-add chain over j = 0..k-1 in order, from +0, of
+ * topk_weights[s][t][j] * expert_out[recv_slot[s][t][j]][c] ), skipping
+ * receive rows < 0.  expert_out: device bf16 bits [EP][C][H];
+ * topk_weights: device float [EP][N][k]; out: device bf16 bits [EP][N][H]. */
+MOE_API int moe_exchange_combine(const moe_problem *p, const moe_exchange *x,
+                                 const uint16_t *expert_out,
+                                 const float *topk_weights, uint16_t *out,
+                                 void *stream);
+
 /* Static text for a return code. */
 MOE_API const char *moe_strerror(int code);
 

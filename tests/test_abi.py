@@ -121,3 +121,49 @@ def test_workspace_required_only_for_multi_tile_plans(moe):
 def test_strerror(moe):
     for c in (0, -1, -2, -3, -4, 7):
         assert isinstance(moe.strerror(c), str) and moe.strerror(c)
+
+
+# ---- exchange across EP simulated ranks --------------------------------------
+
+def test_exchange_checks(moe):
+    ok = moe.problem(4096, 4096, 6, 64, 8, recv_capacity=30720)
+    assert moe.moe_check_exchange(ok) == 0
+    assert moe.moe_exchange_workspace_bytes(ok) % 256 == 0
+    assert moe.moe_exchange_workspace_bytes(ok) > 0
+    # source-major receive buffers carry no per-expert padding
+    assert moe.moe_check_exchange(moe.problem(64, 256, 2, 8, 4, recv_capacity=64,
+                                              pad_multiple=2)) == -1
+    # EP * C receive rows must fit int32
+    assert moe.moe_check_exchange(moe.problem(64, 256, 2, 8, 4, recv_capacity=1 << 30)) == -3
+    # EP * N * k * H must fit the uint32 element table
+    assert moe.moe_check_exchange(moe.problem(16384, 4096, 8, 64, 8, recv_capacity=1)) == -3
+    # a problem the single-rank checks reject is rejected here too
+    bad = moe.problem(64, 12, 2, 8, 4, recv_capacity=8)
+    assert moe.moe_check_exchange(bad) == -1
+    assert moe.moe_exchange_workspace_bytes(bad) == 0
+    x = moe.Exchange()
+    for p, code in ((bad, -1), (moe.problem(64, 256, 2, 8, 4, recv_capacity=8, pad_multiple=3), -1)):
+        assert moe.lib.moe_exchange_plan(ctypes.byref(p), None, ctypes.byref(x), None, None) == code
+        assert moe.lib.moe_exchange_dispatch(ctypes.byref(p), ctypes.byref(x), None, None, None,
+                                             None) == code
+        assert moe.lib.moe_exchange_combine(ctypes.byref(p), ctypes.byref(x), None, None, None,
+                                            None) == code
+
+
+def test_exchange_null_and_misaligned_pointers_rejected(moe):
+    p = moe.problem(64, 256, 2, 8, 4, recv_capacity=64)
+    fake = 1 << 20
+    full = moe.Exchange(*([fake] * 8))
+    part = moe.Exchange(*([fake] * 7 + [0]))  # no status array
+    ref = ctypes.byref
+    assert moe.lib.moe_exchange_plan(ref(p), fake, ref(part), fake, None) == -1
+    assert moe.lib.moe_exchange_plan(ref(p), fake, ref(full), None, None) == -1   # no workspace
+    assert moe.lib.moe_exchange_plan(ref(p), None, ref(full), fake, None) == -1   # no ids
+    assert moe.lib.moe_exchange_plan(ref(p), fake, ref(full), fake + 64, None) == -2
+    assert moe.lib.moe_exchange_plan(ref(p), fake + 1, ref(full), fake, None) == -2
+    assert moe.lib.moe_exchange_dispatch(ref(p), ref(full), fake, fake, fake, None) == -1
+    assert moe.lib.moe_exchange_dispatch(ref(p), ref(full), fake + 8, fake, None, None) == -2
+    p8 = moe.problem(64, 256, 2, 8, 4, recv_capacity=64, fmt="fp8")
+    assert moe.lib.moe_exchange_dispatch(ref(p8), ref(full), fake, fake, None, None) == -1
+    assert moe.lib.moe_exchange_combine(ref(p), ref(full), fake, fake, fake + 2, None) == -2
+    assert moe.lib.moe_exchange_combine(ref(p), ref(full), fake, None, fake, None) == -1

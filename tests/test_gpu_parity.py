@@ -5,8 +5,6 @@ fp32 scales, E2M1 nibbles, E8M0 bytes) and on pad/tail rows; combine within
 one bf16 ulp (and, by construction of both sides, bit-exact).  Inputs come
 from the seeded generators only; expected values only from ``oracle``.
 """
-import os
-import sys
 
 import numpy as np
 import pytest
@@ -18,12 +16,7 @@ from combine_topk_ids_amd.workloads import (WORKLOADS, make_inputs, random_bf16,
 
 pytestmark = pytest.mark.gpu
 
-SENTINEL = 0x5A
-
-
-def say(msg):
-    print(msg, flush=True)
-    sys.stdout.flush()
+from gpu_helpers import SENTINEL, assert_combine_close, say, to_dev_bf16, u16
 
 
 @pytest.fixture(scope="module")
@@ -31,14 +24,6 @@ def moe():
     assert torch.cuda.is_available(), "GPU tests need a GPU"
     import combine_topk_ids_amd.moe as m
     return m
-
-
-def u16(t):
-    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
-
-
-def to_dev_bf16(a):
-    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
 
 
 def run_path(moe, *, ids, weights, hidden, e, ep, a, fmt, cap=None, expert_out=None,
@@ -91,17 +76,6 @@ def assert_plan_equal(got, ref):
                 "packed_src"):
         assert np.array_equal(got[key], ref[key]), key
     assert got["status"] == ref["status"]
-
-
-def assert_combine_close(got, ref):
-    g = got.astype(np.int32)
-    r = ref.astype(np.int32)
-    # distance in bf16 ulps on the sign-magnitude ordering
-    def ordered(v):
-        return np.where(v & 0x8000, -(v & 0x7FFF), v & 0x7FFF)
-    d = np.abs(ordered(g) - ordered(r))
-    assert d.max(initial=0) <= 1, f"max ulp diff {d.max()}"
-    return int((d != 0).sum())
 
 
 def payload_bytes_ref(fmt, x, pl, zero_tail):
