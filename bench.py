@@ -46,13 +46,28 @@ def row_bytes(fmt, h):
 
 
 def step_bytes(w, r_used, r_max):
-    """Algorithmic bytes of one step (each array read or written once)."""
-    nk = w.n * w.k
-    plan = 4 * nk + 4 * nk + 4 * r_max                     # ids, slot, packed_src
-    dispatch = 2 * w.n * w.h + r_used * row_bytes(w.fmt, w.h)  # read x once, write live+pad rows
-    combine = 4 * nk + 4 * nk + 2 * w.h * nk + 2 * w.n * w.h   # slot, w, k rows of y, out
+    """Algorithmic bytes of one step (each array read or written once).
+
+    One buffer: r_used = R_used rows (live + pad), r_max = R_max.  Exchange:
+    r_used = receive rows in use over all buffers, r_max = EP * C; the
+    dispatch writes every receive row (live rows, then zero rows)."""
+    t = w.tokens
+    nk = t * w.k
+    if w.exchange:
+        plan = 4 * nk + 4 * nk + 4 * r_max                       # ids, recv_slot, recv_src
+        dispatch = 2 * t * w.h + r_max * row_bytes(w.fmt, w.h)   # read x once, write all rows
+        combine = 4 * nk + 4 * nk + 2 * w.h * r_used + 2 * t * w.h  # slot, w, kept rows, out
+    else:
+        plan = 4 * nk + 4 * nk + 4 * r_max                     # ids, slot, packed_src
+        dispatch = 2 * t * w.h + r_used * row_bytes(w.fmt, w.h)  # read x once, write live+pad rows
+        combine = 4 * nk + 4 * nk + 2 * w.h * nk + 2 * t * w.h   # slot, w, k rows of y, out
     return dict(plan=plan, dispatch=dispatch, combine=combine,
                 total=plan + dispatch + combine)
+
+
+def buffer_rows(w):
+    """Rows of the packed buffer (R_max) or of all receive buffers (EP * C)."""
+    return w.ep * w.capacity if w.exchange else w.n * w.k + w.e * (w.a - 1)
 
 
 def traffic_from_profile(workload, kernel):
@@ -118,6 +133,55 @@ class Path:
         return int(self.sets[0]["plan"].expert_offsets[-1].item())
 
 
+class ExchangePath:
+    """Device buffers and the three calls of one step of the exchange across
+    EP simulated ranks (exchange plan, dispatch into the receive buffers,
+    reverse combine)."""
+
+    def __init__(self, moe, torch, w, inp, copies):
+        self.moe, self.torch, self.w = moe, torch, w
+        self.p = moe.problem(w.n, w.h, w.k, w.e, w.ep, recv_capacity=w.capacity, fmt=w.fmt)
+        dev = "cuda"
+        x = torch.from_numpy(inp["hidden"].view(np.int16)).to(dev).view(torch.bfloat16)
+        ids = torch.from_numpy(inp["ids"].reshape(w.ranks, w.n, w.k)).to(dev)
+        wts = torch.from_numpy(inp["weights"]).to(dev)
+        y = None
+        if "expert_out" in inp:
+            y = torch.from_numpy(inp["expert_out"].view(np.int16)).to(dev).view(torch.bfloat16)
+        self.sets = []
+        for c in range(copies):
+            xb = moe.alloc_exchange(self.p, dev)
+            payload, scales = moe.alloc_recv_payload(self.p, dev)
+            payload.view(torch.uint8).zero_()
+            if scales is not None:
+                scales.zero_()
+            self.sets.append(dict(
+                x=x if c == 0 else x.clone(), ids=ids if c == 0 else ids.clone(),
+                w=wts if c == 0 else wts.clone(),
+                y=(y if c == 0 else y.clone()) if y is not None else payload,
+                xb=xb, payload=payload, scales=scales,
+                out=torch.empty((w.tokens, w.h), dtype=torch.bfloat16, device=dev)))
+
+    def step(self, i, ev=None):
+        s = self.sets[i % len(self.sets)]
+        m, p = self.moe, self.p
+        if ev is not None:
+            ev[0].record()
+        m.moe_exchange_plan(p, s["ids"], s["xb"])
+        if ev is not None:
+            ev[1].record()
+        m.moe_exchange_dispatch(p, s["xb"], s["x"], s["payload"], s["scales"])
+        if ev is not None:
+            ev[2].record()
+        m.moe_exchange_combine(p, s["xb"], s["y"], s["w"], s["out"])
+        if ev is not None:
+            ev[3].record()
+
+    def r_used(self):
+        rows = self.sets[0]["xb"].recv_rows.clamp(max=self.w.capacity)
+        return int(rows.sum().item())
+
+
 def time_steps(torch, path, steps, warmup):
     for i in range(warmup):
         path.step(i)
@@ -174,7 +238,7 @@ def decode_latency(moe, torch, w, inp, iters=200, per_graph=16):
     back-to-back calls from Python (host-bound: each call costs a few µs of
     Python and ctypes), one HIP graph per step, and one HIP graph holding
     `per_graph` steps (closest to the GPU's own time per step)."""
-    path = Path(moe, torch, w, inp, copies=1)
+    path = (ExchangePath if w.exchange else Path)(moe, torch, w, inp, copies=1)
     for i in range(20):
         path.step(0)
     torch.cuda.synchronize()
@@ -219,6 +283,8 @@ def cpu_baseline(w, inp, budget_s=10.0, pass_s=2.0):
     about budget_s of CPU time; GB/s with the same algorithmic byte formula."""
     import oracle
     oracle.build(force=False)
+    if w.exchange:
+        return cpu_baseline_exchange(w, inp, budget_s, pass_s)
 
     def one_pass(m):
         ids, wts, x = inp["ids"][:m], inp["weights"][:m], inp["hidden"][:m]
@@ -248,6 +314,47 @@ def cpu_baseline(w, inp, budget_s=10.0, pass_s=2.0):
                        "single thread")
 
 
+def cpu_baseline_exchange(w, inp, budget_s, pass_s):
+    """The CPU oracle's exchange (plan, receive buffers, reverse combine) on
+    the first M tokens of every rank, with C scaled by M / N."""
+    import oracle
+    ids3 = inp["ids"].reshape(w.ranks, w.n, w.k)
+    x3 = inp["hidden"].reshape(w.ranks, w.n, w.h)
+    w3 = inp["weights"].reshape(w.ranks, w.n, w.k)
+
+    def one_pass(m):
+        cap = -(-w.capacity * m // w.n)
+        ids = np.ascontiguousarray(ids3[:, :m])
+        x = np.ascontiguousarray(x3[:, :m].reshape(-1, w.h))
+        wts = np.ascontiguousarray(w3[:, :m].reshape(-1, w.k))
+        t0 = time.process_time()
+        xp = oracle.exchange_plan(ids, w.e, cap, w.h)
+        pay, _ = oracle.exchange_dispatch(w.fmt, x, xp)
+        y = pay.view(np.uint16).reshape(w.ep * cap, -1) if "expert_out" not in inp \
+            else inp["expert_out"]
+        oracle.combine(xp["recv_slot"].reshape(-1, w.k), wts, y)
+        dt = time.process_time() - t0
+        sub = dataclasses.replace(w, n=m, recv_capacity=cap)
+        used = int(np.minimum(xp["recv_rows"], cap).sum())
+        return dt, step_bytes(sub, used, w.ep * cap)["total"]
+
+    m = min(w.n, 16)
+    dt, _ = one_pass(m)
+    m = int(min(w.n, max(1, m * pass_s / max(dt, 1e-6))))
+    runs, total_bytes, t_total = 0, 0, 0.0
+    while t_total < budget_s and runs < 50:
+        dt, nbytes = one_pass(m)
+        t_total += dt
+        total_bytes += nbytes
+        runs += 1
+    return dict(value=round(total_bytes / t_total / 1e9, 3), unit="GB/s", cores=1,
+                kind="oracle",
+                sample=f"{runs} passes of the exchange plan, receive buffers and combine over "
+                       f"the first {m} of {w.n} tokens of each of {w.ranks} ranks of {w.name} "
+                       f"({w.describe()}; C scaled to {-(-w.capacity * m // w.n)}), "
+                       f"{t_total:.1f} s CPU, single thread")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -257,6 +364,8 @@ def main():
     ap.add_argument("--copies", type=int, default=0, help="buffer sets rotated over (0: auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--decode-workload", default="decode_mxfp4_n128",
+                    help="workload whose µs per step is reported under 'decode'")
     ap.add_argument("--no-copy-ref", action="store_true")
     args = ap.parse_args()
 
@@ -273,12 +382,12 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     w = WORKLOADS[args.workload]
     log(f"[bench] workload {w.name}: {w.describe()}")
-    r_max = w.n * w.k + w.e * (w.a - 1)
+    r_max = buffer_rows(w)
     inp = make_inputs(w, seed=0, expert_rows=r_max)
-    set_bytes = (w.n * w.h * 2 * 2 + r_max * row_bytes(w.fmt, w.h)
+    set_bytes = (w.tokens * w.h * 2 * 2 + r_max * row_bytes(w.fmt, w.h)
                  + (r_max * w.h * 2 if "expert_out" in inp else 0))
     copies = args.copies or max(2, min(8, -(-(768 << 20) // max(set_bytes, 1)) + 1))
-    path = Path(moe, torch, w, inp, copies)
+    path = (ExchangePath if w.exchange else Path)(moe, torch, w, inp, copies)
     log(f"[bench] {copies} buffer sets of {set_bytes / 1e6:.1f} MB rotated")
 
     ms, wall = time_steps(torch, path, args.steps, args.warmup)
@@ -304,8 +413,8 @@ def main():
         extra["stream_ref_gbps"] = round(stream_reference(torch), 1)
         log(f"[bench] 1 GiB read + 1 GiB write streaming kernel: {extra['stream_ref_gbps']} GB/s")
     if not args.no_decode:
-        dw = WORKLOADS["decode_mxfp4_n128"]
-        dinp = make_inputs(dw, seed=0, expert_rows=dw.n * dw.k + dw.e * (dw.a - 1))
+        dw = WORKLOADS[args.decode_workload]
+        dinp = make_inputs(dw, seed=0, expert_rows=buffer_rows(dw))
         extra["decode"] = decode_latency(moe, torch, dw, dinp)
         log(f"[bench] decode: {extra['decode']}")
 
@@ -314,6 +423,13 @@ def main():
         cpu = cpu_baseline(w, inp)
         log(f"[bench] cpu baseline: {cpu}")
 
+    config = {"workload": w.name, "tokens": w.n, "hidden": w.h, "experts": w.e,
+              "top_k": w.k, "ep_ranks_simulated": w.ep, "pad_multiple": w.a,
+              "format": w.fmt, "routing": w.routing, "r_used": ru, "r_max": r_max,
+              "buffer_sets": copies}
+    if w.exchange:
+        config.update(source_ranks=w.ranks, recv_capacity=w.capacity,
+                      path="exchange: source-major receive buffers of C rows per rank")
     rec = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -327,10 +443,7 @@ def main():
         "vs_baseline": None,
         "dtype": w.fmt if w.fmt != "mxfp4" else "mxfp4",
         "data": "synthetic",
-        "config": {"workload": w.name, "tokens": w.n, "hidden": w.h, "experts": w.e,
-                   "top_k": w.k, "ep_ranks_simulated": w.ep, "pad_multiple": w.a,
-                   "format": w.fmt, "routing": w.routing, "r_used": ru, "r_max": r_max,
-                   "buffer_sets": copies},
+        "config": config,
         "frac_of_peak": round(value / PEAK_HBM_GBPS, 4),
         "bytes_per_step": b,
         "kernel_us": {k: round(v * 1e3, 2) for k, v in kt.items()},

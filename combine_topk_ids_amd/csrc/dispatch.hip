@@ -51,11 +51,25 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #ifndef MOE_QUANT_CHUNKS
 #define MOE_QUANT_CHUNKS 1
 #endif
+// Zero rows after the used part of each segment: workgroups for them, their
+// place in the grid (first or last), non-temporal stores.  Non-temporal
+// tail stores measured faster (receive-buffer tails: 400 vs 436 us at 8
+// ranks x 4096 tokens); on per-expert pad rows they slowed the combine that
+// follows, so pad rows keep ordinary stores.
+#ifndef MOE_TAIL_BLOCKS
+#define MOE_TAIL_BLOCKS 512
+#endif
+#ifndef MOE_TAIL_FIRST
+#define MOE_TAIL_FIRST 0
+#endif
+#ifndef MOE_TAIL_NT
+#define MOE_TAIL_NT 1
+#endif
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kPadRowsPerWave = 4;
-constexpr int kTailBlocks = 512;
+constexpr int kTailBlocks = MOE_TAIL_BLOCKS;
 
 struct DispatchArgs {
   const uint16_t *x;
@@ -290,10 +304,29 @@ __device__ __forceinline__ int xcd_local_block(int b, int nblocks) {
   return x * per + min(x, extra) + pos;
 }
 
+// zero rows after the used part of every segment, by `blk` of tail_blocks
+template <bool NT>
+__device__ void zero_tails(const DispatchArgs &g, int blk, int wave) {
+  const int64_t stride = static_cast<int64_t>(g.tail_blocks) * kWaves;
+  for (int d = 0; d < g.nseg; ++d) {
+    const int64_t used = min(static_cast<int64_t>(g.seg_used[d]), g.seg_rows);
+    const int64_t base = d * g.seg_rows;
+    for (int64_t r = used + static_cast<int64_t>(blk) * kWaves + wave; r < g.seg_rows; r += stride)
+      zero_row<NT>(g, base + r);
+  }
+}
+
 template <int FMT, bool NT>
 __global__ __launch_bounds__(kThreads) void dispatch_kernel(DispatchArgs g) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   int blk = blockIdx.x;
+  if (MOE_TAIL_FIRST) {
+    if (blk < g.tail_blocks) {
+      zero_tails<NT || MOE_TAIL_NT>(g, blk, wave);
+      return;
+    }
+    blk -= g.tail_blocks;
+  }
   if (blk < g.token_blocks) {
     if (FMT != MOE_FMT_BF16) blk = xcd_local_block(blk, g.token_blocks);
     const int q = blk * kWaves + wave;  // the grid size keeps q within int
@@ -319,14 +352,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(DispatchArgs g) {
     return;
   }
   blk -= g.pad_blocks;
-  // zero rows after the used part of every segment
-  const int64_t stride = static_cast<int64_t>(g.tail_blocks) * kWaves;
-  for (int d = 0; d < g.nseg; ++d) {
-    const int64_t used = min(static_cast<int64_t>(g.seg_used[d]), g.seg_rows);
-    const int64_t base = d * g.seg_rows;
-    for (int64_t r = used + static_cast<int64_t>(blk) * kWaves + wave; r < g.seg_rows; r += stride)
-      zero_row<NT>(g, base + r);
-  }
+  if (!MOE_TAIL_FIRST) zero_tails<NT || MOE_TAIL_NT>(g, blk, wave);
 }
 
 template <int FMT>

@@ -18,15 +18,15 @@
 //      blockIdx.y = rank, A = 1, no send-side capacity): counts per expert,
 //      send counts per destination, send displacements (table rows 0-1),
 //      and the pair's row in the rank's own packed order;
-//   2. exchange_scan (thread per destination d): walks the sources in order
-//      over the send-count matrix column of d: rows of d's buffer that come
-//      before source s, the receive counts and displacements (table rows
-//      2-3), the rows offered to d, CAPACITY, and what the counts
-//      all-to-all delivers to d (its slice of every source's count matrix);
-//   3. exchange_remap (blocks of pairs per source, blockIdx.y = source):
-//      receive row = d*C + (rows before source s in d's buffer) + (send row
-//      - start of the source's segment for d), kept if below C; writes the
-//      inverse map recv_src, and -1 over each buffer's zero rows.
+//   2. exchange_remap, one launch of two block ranges:
+//      - blocks of pairs per source s (blockIdx.y = s): receive row = d*C +
+//        (rows of d's buffer from sources before s) + (send row - start of
+//        s's segment for d), kept if below C; the inverse map recv_src;
+//      - blocks per destination d (blockIdx.y = d): the receive counts from
+//        every source and their packed cumsum (table rows 2-3), the rows
+//        offered to d, CAPACITY, what the counts all-to-all delivers to d
+//        (its slice of every source's count matrix), and -1 over recv_src
+//        past the rows in use.
 // A pair's position inside its source's segment is the single-rank plan's,
 // so the order inside a receive buffer is (source, expert, token, k) without
 // any sort across ranks, and no output depends on atomic order.
@@ -48,7 +48,6 @@ struct ExchangeArgs {
   const int32_t *counts;        // [R][E]
   const int32_t *send_counts;   // [R][R]
   const int32_t *offsets;       // [R][E+1] each rank's expert offsets (A = 1)
-  int32_t *pre;                 // [R][R] ([s][d]) rows of d's buffer before source s
   int32_t *recv_expert_counts;  // [R][R][L]
   int32_t *recv_rows;           // [R]
   uint32_t *table;              // [R][4][R]
@@ -59,36 +58,54 @@ struct ExchangeArgs {
   int64_t cap;                  // C
   uint32_t h;
   int k, e, r, l;
-  int pair_blocks, tail_blocks;
+  int pair_blocks, dest_blocks;
 };
 
-__global__ __launch_bounds__(kThreads) void exchange_scan_kernel(ExchangeArgs g) {
-  const int d = blockIdx.x * kThreads + threadIdx.x;
-  if (d >= g.r) return;
-  const int R = g.r;
-  uint32_t *tab = g.table + static_cast<int64_t>(d) * 4 * R;
-  int64_t run = 0;
-  for (int s = 0; s < R; ++s) {
-    const int c = g.send_counts[static_cast<int64_t>(s) * R + d];
-    g.pre[static_cast<int64_t>(s) * R + d] = static_cast<int32_t>(run);
-    tab[2 * R + s] = static_cast<uint32_t>(c) * g.h;
-    tab[3 * R + s] = static_cast<uint32_t>(run) * g.h;  // < 2^32: checked on the host
-    run += c;
+// Exclusive prefix sum of v[0..n) in LDS (n <= 4 * kThreads), in place;
+// returns the total.  Each thread scans 4 consecutive entries, then a DPP
+// wave scan and one partial per wave carry the sums across.
+__device__ int block_excl_scan4(int *v, int n, int *s_wave) {
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = tid / kWave;
+  int x[4], sum = 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int i = 4 * tid + u;
+    x[u] = i < n ? v[i] : 0;
+    sum += x[u];
   }
-  g.recv_rows[d] = static_cast<int32_t>(run);
-  if (run > g.cap) g.status[d] |= MOE_STATUS_CAPACITY;
-  // the counts all-to-all: d's slice of every source's count matrix
-  int32_t *rec = g.recv_expert_counts + static_cast<int64_t>(d) * R * g.l;
-  for (int s = 0; s < R; ++s)
-    for (int x = 0; x < g.l; ++x)
-      rec[s * g.l + x] = g.counts[static_cast<int64_t>(s) * g.e + d * g.l + x];
+  const int incl = wave_incl_scan(sum);
+  if (lane == kWave - 1) s_wave[wave] = incl;
+  __syncthreads();
+  int run = incl - sum, total = 0;
+#pragma unroll
+  for (int w = 0; w < kThreads / kWave; ++w) {
+    run += w < wave ? s_wave[w] : 0;
+    total += s_wave[w];
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int i = 4 * tid + u;
+    if (i < n) v[i] = run;
+    run += x[u];
+  }
+  __syncthreads();
+  return total;
 }
 
+// grid (pair_blocks + dest_blocks, R).  Blocks x < pair_blocks map the pairs
+// of source rank s = blockIdx.y to receive rows; the others serve
+// destination rank d = blockIdx.y: its metadata (first such block) and the
+// -1 entries of recv_src past the rows in use.
 __global__ __launch_bounds__(kThreads) void exchange_remap_kernel(ExchangeArgs g) {
-  const int s = blockIdx.y;
+  const int y = blockIdx.y;
   const int tid = threadIdx.x;
+  const int R = g.r;
+  __shared__ int s_v[kMaxExperts];  // per rank; EP <= E <= 1024
+  __shared__ int s_wave[kThreads / kWave];
   if (static_cast<int>(blockIdx.x) < g.pair_blocks) {
-    __shared__ int s_base[kMaxExperts];  // per destination; EP <= E <= 1024
+    const int s = y;
     const int64_t p0 = static_cast<int64_t>(blockIdx.x) * kPairsPerBlock;
     const int32_t *ids = g.ids + s * g.npairs;
     int32_t *slot = g.slot + s * g.npairs;
@@ -100,18 +117,20 @@ __global__ __launch_bounds__(kThreads) void exchange_remap_kernel(ExchangeArgs g
       sl[u] = in ? slot[p] : -1;
       ev[u] = in ? ids[p] : 0;
     }
-    // receive row i = send row + (rows before s in d's buffer) - (start of
-    // s's segment for d in its own packed order)
-    for (int d = tid; d < g.r; d += kThreads)
-      s_base[d] = g.pre[static_cast<int64_t>(s) * g.r + d] -
-                  g.offsets[static_cast<int64_t>(s) * (g.e + 1) + d * g.l];
+    // receive row i = send row + (rows of d's buffer from sources before s)
+    // - (start of s's segment for d in its own packed order)
+    for (int d = tid; d < R; d += kThreads) {
+      int before = 0;
+      for (int q = 0; q < s; ++q) before += g.send_counts[static_cast<int64_t>(q) * R + d];
+      s_v[d] = before - g.offsets[static_cast<int64_t>(s) * (g.e + 1) + d * g.l];
+    }
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < kPairsPerThread; ++u) {
       if (sl[u] < 0) continue;  // masked or invalid: stays -1
       const int64_t p = p0 + u * kThreads + tid;
       const int d = ev[u] / g.l;  // a routed pair's ID lies in [0, E)
-      const int64_t i = static_cast<int64_t>(sl[u]) + s_base[d];
+      const int64_t i = static_cast<int64_t>(sl[u]) + s_v[d];
       if (i < g.cap) {
         const int64_t row = d * g.cap + i;  // < EP*C < 2^31: checked on the host
         g.recv_src[row] = static_cast<int32_t>(s * g.n + p / g.k);
@@ -122,22 +141,49 @@ __global__ __launch_bounds__(kThreads) void exchange_remap_kernel(ExchangeArgs g
     }
     return;
   }
-  // zero rows of receive buffer d = blockIdx.y
-  const int d = s;
-  const int64_t used = min(static_cast<int64_t>(g.recv_rows[d]), g.cap);
+  // destination d: receive counts from every source, their packed cumsum
+  const int d = y;
+  const int xb = blockIdx.x - g.pair_blocks;
+  for (int q = tid; q < R; q += kThreads) s_v[q] = g.send_counts[static_cast<int64_t>(q) * R + d];
+  __syncthreads();
+  int cnt[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) cnt[u] = 4 * tid + u < R ? s_v[4 * tid + u] : 0;
+  const int64_t total = block_excl_scan4(s_v, R, s_wave);  // s_v: displacements
+  if (xb == 0) {
+    uint32_t *tab = g.table + static_cast<int64_t>(d) * 4 * R;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int q = 4 * tid + u;
+      if (q < R) {
+        tab[2 * R + q] = static_cast<uint32_t>(cnt[u]) * g.h;
+        tab[3 * R + q] = static_cast<uint32_t>(s_v[q]) * g.h;  // < 2^32: checked on the host
+      }
+    }
+    if (tid == 0) {
+      g.recv_rows[d] = static_cast<int32_t>(total);
+      if (total > g.cap) g.status[d] |= MOE_STATUS_CAPACITY;
+    }
+    // the counts all-to-all: d's slice of every source's count matrix
+    int32_t *rec = g.recv_expert_counts + static_cast<int64_t>(d) * R * g.l;
+    for (int i = tid; i < R * g.l; i += kThreads) {
+      const int q = i / g.l, x = i - q * g.l;
+      rec[i] = g.counts[static_cast<int64_t>(q) * g.e + d * g.l + x];
+    }
+  }
+  // recv_src = -1 past the rows in use
+  const int64_t used = min(total, g.cap);
   int32_t *src = g.recv_src + d * g.cap;
-  const int64_t stride = static_cast<int64_t>(g.tail_blocks) * kThreads;
-  for (int64_t i = used + static_cast<int64_t>(blockIdx.x - g.pair_blocks) * kThreads + tid; i < g.cap;
-       i += stride)
-    src[i] = -1;
+  const int64_t stride = static_cast<int64_t>(g.dest_blocks) * kThreads;
+  for (int64_t i = used + static_cast<int64_t>(xb) * kThreads + tid; i < g.cap; i += stride) src[i] = -1;
 }
 
 size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 
-// Workspace: [R][E+1] offsets, [R][R] pre, [R][N*k] packed_src of the
-// per-rank plans, then R copies of the single-rank plan workspace.
+// Workspace: [R][E+1] offsets and [R][N*k] packed_src of the per-rank
+// plans, then R copies of the single-rank plan workspace.
 struct Layout {
-  size_t offsets, pre, packed_src, plan_ws, total;
+  size_t offsets, packed_src, plan_ws, total;
   size_t plan_ws_bytes;  // per rank
 };
 
@@ -155,8 +201,6 @@ Layout layout(const moe_problem &p) {
   size_t at = 0;
   L.offsets = at;
   at += align256(R * (p.n_experts + 1) * sizeof(int32_t));
-  L.pre = at;
-  at += align256(R * R * sizeof(int32_t));
   L.packed_src = at;
   at += align256(R * static_cast<size_t>(p.n_tokens) * p.top_k * sizeof(int32_t));
   L.plan_ws_bytes = plan_workspace_bytes(rank_problem(p));
@@ -204,7 +248,6 @@ hipError_t launch_exchange_plan(const moe_problem &p, const int32_t *ids, const 
   g.counts = x.expert_counts;
   g.send_counts = x.send_counts;
   g.offsets = offsets;
-  g.pre = reinterpret_cast<int32_t *>(ws + L.pre);
   g.recv_expert_counts = x.recv_expert_counts;
   g.recv_rows = x.recv_rows;
   g.table = x.rank_table;
@@ -219,14 +262,14 @@ hipError_t launch_exchange_plan(const moe_problem &p, const int32_t *ids, const 
   g.r = R;
   g.l = p.n_experts / R;
   g.pair_blocks = static_cast<int>((g.npairs + kPairsPerBlock - 1) / kPairsPerBlock);
-  const int64_t tail_blocks = (g.cap + kTailRowsPerBlock - 1) / kTailRowsPerBlock;
-  g.tail_blocks = static_cast<int>(tail_blocks < kMaxTailBlocks ? tail_blocks : kMaxTailBlocks);
+  // at least one block per destination (its metadata), more for long tails
+  const int64_t dest_blocks = (g.cap + kTailRowsPerBlock - 1) / kTailRowsPerBlock;
+  g.dest_blocks = static_cast<int>(dest_blocks < 1 ? 1 : dest_blocks < kMaxTailBlocks ? dest_blocks
+                                                                                      : kMaxTailBlocks);
 
-  // 2. receive counts and displacements
-  exchange_scan_kernel<<<(R + kThreads - 1) / kThreads, kThreads, 0, stream>>>(g);
-  // 3. receive rows of every pair, their inverse, the zero rows
-  const int gx = g.pair_blocks + g.tail_blocks;
-  if (gx > 0) exchange_remap_kernel<<<dim3(gx, R), kThreads, 0, stream>>>(g);
+  // 2. receive rows of every pair and their inverse; per destination: the
+  //    receive counts and displacements, the counts all-to-all, the zero rows
+  exchange_remap_kernel<<<dim3(g.pair_blocks + g.dest_blocks, R), kThreads, 0, stream>>>(g);
   return hipGetLastError();
 }
 
