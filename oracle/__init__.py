@@ -27,7 +27,7 @@ SRC = os.path.join(HERE, "oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
 FMT = {"bf16": 0, "fp8": 1, "mxfp4": 2}
-BAD_ID, DUP_ID, CAPACITY = 1, 2, 4
+BAD_ID, DUP_ID, CAPACITY, MAP_OVERFLOW = 1, 2, 4, 8
 
 _lib = None
 
@@ -59,6 +59,12 @@ def _load():
         lib.oracle_exchange_plan.argtypes = [i64, i32, i32, i32, i64, i64] + [p] * 9
         lib.oracle_encode_row.restype = None
         lib.oracle_encode_row.argtypes = [i32, i64, p, p, p]
+        lib.oracle_encode_row_f32.restype = None
+        lib.oracle_encode_row_f32.argtypes = [i32, i64, p, p, p]
+        lib.oracle_dispatch_gated.restype = None
+        lib.oracle_dispatch_gated.argtypes = [i32, i64, i32, i64, i64, i64, p, p, p, p, p, i32]
+        lib.oracle_routing_map_to_topk.restype = None
+        lib.oracle_routing_map_to_topk.argtypes = [i64, i32, i32, p, p, p, p, p]
         lib.oracle_dispatch.restype = None
         lib.oracle_dispatch.argtypes = [i32, i64, i64, i64, p, p, p, p, i32]
         lib.oracle_combine.restype = None
@@ -203,16 +209,70 @@ def dispatch(fmt: str, x: np.ndarray, pl: dict, zero_tail: bool = True,
     return payload, (scales if sdt is not None else None)
 
 
-def combine(slot: np.ndarray, w: np.ndarray, y: np.ndarray) -> np.ndarray:
-    """``out uint16 [N, H]`` (bf16 bits) from ``slot [N,k]``, ``w f32 [N,k]``
-    and expert outputs ``y uint16 [rows, H]``."""
-    slot = np.ascontiguousarray(slot, dtype=np.int32)
+def dispatch_gated(fmt: str, x: np.ndarray, pl: dict, w: np.ndarray, zero_tail: bool = True,
+                   payload: np.ndarray | None = None, scales: np.ndarray | None = None):
+    """Packed payload and scales when every copy carries its gate: row
+    slot[t, j] holds encode(fl32(w[t, j] * x[t])) (scatter form)."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
     w = np.ascontiguousarray(w, dtype=np.float32)
+    slot = np.ascontiguousarray(pl["slot"], dtype=np.int32)
+    n, h = x.shape
+    k = slot.shape[1]
+    r_max = pl["r_max"]
+    pdt, pshape, sdt, sshape = payload_shape(fmt, r_max, h)
+    if payload is None:
+        payload = np.zeros(pshape, pdt)
+    if scales is None:
+        scales = np.zeros(sshape, sdt if sdt is not None else np.uint8)
+    _load().oracle_dispatch_gated(FMT[fmt], n, k, h, r_max, pl["r_used"], _ptr(slot), _ptr(w),
+                                  _ptr(x), _ptr(payload), _ptr(scales), int(zero_tail))
+    return payload, (scales if sdt is not None else None)
+
+
+def encode_rows_f32(fmt: str, v: np.ndarray):
+    """Encode rows of fp32 values ``[M, H]``: (payload rows, scale rows)."""
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    m, h = v.shape
+    pdt, pshape, sdt, sshape = payload_shape(fmt, m, h)
+    pay = np.zeros(pshape, pdt)
+    sc = np.zeros(sshape, sdt if sdt is not None else np.uint8)
+    lib = _load()
+    for i in range(m):
+        lib.oracle_encode_row_f32(FMT[fmt], h, ctypes.c_void_p(v[i].ctypes.data),
+                                  ctypes.c_void_p(pay[i].ctypes.data),
+                                  ctypes.c_void_p(sc[i].ctypes.data) if sdt is not None else None)
+    return pay, (sc if sdt is not None else None)
+
+
+def routing_map_to_topk(routing_map: np.ndarray, probs: np.ndarray | None, k: int):
+    """Multihot map ``[N, E]`` (nonzero = routed) and dense probabilities
+    ``[N, E]`` (or None) -> (ids int32 [N, k], weights float32 [N, k],
+    status)."""
+    m = np.ascontiguousarray(routing_map != 0, dtype=np.uint8)
+    n, e = m.shape
+    pr = None if probs is None else np.ascontiguousarray(probs, dtype=np.float32)
+    ids = np.zeros((n, k), np.int32)
+    w = np.zeros((n, k), np.float32)
+    st = np.zeros(1, np.uint32)
+    _load().oracle_routing_map_to_topk(n, e, k, _ptr(m), None if pr is None else _ptr(pr),
+                                       _ptr(ids), _ptr(w), _ptr(st))
+    return ids, w, int(st[0])
+
+
+def combine(slot: np.ndarray, w: np.ndarray | None, y: np.ndarray) -> np.ndarray:
+    """``out uint16 [N, H]`` (bf16 bits) from ``slot [N,k]``, ``w f32 [N,k]``
+    (None: every weight 1, the unweighted sum after a gated dispatch) and
+    expert outputs ``y uint16 [rows, H]``."""
+    slot = np.ascontiguousarray(slot, dtype=np.int32)
     y = np.ascontiguousarray(y, dtype=np.uint16)
     n, k = slot.shape
     h = y.shape[1]
     out = np.zeros((n, h), np.uint16)
-    _load().oracle_combine(n, k, h, _ptr(slot), _ptr(w), _ptr(y), _ptr(out))
+    wp = None
+    if w is not None:
+        w = np.ascontiguousarray(w, dtype=np.float32)
+        wp = _ptr(w)
+    _load().oracle_combine(n, k, h, _ptr(slot), wp, _ptr(y), _ptr(out))
     return out
 
 

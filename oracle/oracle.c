@@ -50,6 +50,22 @@
  *               rows a rank receives from it).
  *             - Mojo ep.dispatch_async.block.scaled.nv struct: recv_count_ptrs
  *               (tokens received per expert).
+ *   routing map  a multihot [N, E] map (nonzero byte = routed) with dense
+ *             probabilities [N, E] turned into the compact form: a token's
+ *             routed experts in ascending order, their probabilities, -1 and
+ *             0 in unused slots; more than k routed experts is flagged and
+ *             the extra ones are ignored.
+ *             - NeMo Automodel token_dispatcher API:
+ *               _DeepepManager._indices_to_multihot (top-k indices with -1
+ *               masks <-> multihot routing map and multihot probabilities),
+ *               TokenDispatcherConfig.moe_hybridep_compact_routing (compact
+ *               top-k indices or a dense Boolean routing map), and the
+ *               conversion from top-k indices to the multihot routing map.
+ *   gated dispatch  every copy (t, j) carries the token row multiplied by its
+ *             gate, fl32(w[t,j] * x), encoded in the payload format; combine
+ *             then sums the expert rows without weights.
+ *             - DeepSpeed v0.19.4 function index, page 15: pre-multiplying
+ *               token representations by router scores before expert compute.
  *   combine   out[t] = bf16(sum_j w[t,j] * Y[slot[t,j]]) accumulated in fp32
  *             in j order, one fused multiply-add per term.
  *             - DeepSpeed v0.19.4 function index, page 15: the combine entry
@@ -69,11 +85,13 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #define ORC_BAD_ID 1u
 #define ORC_DUP_ID 2u
 #define ORC_CAPACITY 4u
+#define ORC_MAP_OVERFLOW 8u
 
 #define ORC_FMT_BF16 0
 #define ORC_FMT_FP8 1
@@ -371,14 +389,15 @@ void oracle_exchange_plan(int64_t n, int k, int e_cnt, int ep, int64_t cap,
 
 /* ------------------------------------------------------------ encoders --- */
 
-/* One hidden row (h bf16 values) into one packed row.  For FP8 the payload
- * row holds h code bytes and the scale row h/128 floats; for MX the payload
- * row holds h/2 bytes (element 2m in the low nibble, 2m+1 in the high one)
- * and the scale row h/32 E8M0 bytes. */
-void oracle_encode_row(int fmt, int64_t h, const uint16_t *x, void *payload,
-                       void *scales) {
+/* One row of h fp32 values into one packed row.  For FP8 the payload row
+ * holds h code bytes and the scale row h/128 floats; for MX the payload row
+ * holds h/2 bytes (element 2m in the low nibble, 2m+1 in the high one) and
+ * the scale row h/32 E8M0 bytes. */
+void oracle_encode_row_f32(int fmt, int64_t h, const float *v, void *payload,
+                           void *scales) {
   if (fmt == ORC_FMT_BF16) {
-    memcpy(payload, x, (size_t)h * 2);
+    uint16_t *q = (uint16_t *)payload;
+    for (int64_t i = 0; i < h; i++) q[i] = oracle_f32_to_bf16(v[i]);
     return;
   }
   if (fmt == ORC_FMT_FP8) {
@@ -387,8 +406,8 @@ void oracle_encode_row(int fmt, int64_t h, const uint16_t *x, void *payload,
     for (int64_t b = 0; b < h / 128; b++) {
       float amax = 0.0f;
       for (int i = 0; i < 128; i++) {
-        float v = fabsf(oracle_bf16_to_f32(x[b * 128 + i]));
-        if (v > amax) amax = v;
+        float a = fabsf(v[b * 128 + i]);
+        if (a > amax) amax = a;
       }
       float s = amax / 448.0f;
       if (s == 0.0f) {
@@ -396,10 +415,7 @@ void oracle_encode_row(int fmt, int64_t h, const uint16_t *x, void *payload,
         sc[b] = 0.0f;
         continue;
       }
-      for (int i = 0; i < 128; i++) {
-        float v = oracle_bf16_to_f32(x[b * 128 + i]);
-        q[b * 128 + i] = oracle_e4m3_encode(v / s);
-      }
+      for (int i = 0; i < 128; i++) q[b * 128 + i] = oracle_e4m3_encode(v[b * 128 + i] / s);
       sc[b] = s;
     }
     return;
@@ -410,8 +426,8 @@ void oracle_encode_row(int fmt, int64_t h, const uint16_t *x, void *payload,
   for (int64_t b = 0; b < h / 32; b++) {
     float amax = 0.0f;
     for (int i = 0; i < 32; i++) {
-      float v = fabsf(oracle_bf16_to_f32(x[b * 32 + i]));
-      if (v > amax) amax = v;
+      float a = fabsf(v[b * 32 + i]);
+      if (a > amax) amax = a;
     }
     if (amax == 0.0f) {
       for (int i = 0; i < 16; i++) q[b * 16 + i] = 0;
@@ -425,12 +441,21 @@ void oracle_encode_row(int fmt, int64_t h, const uint16_t *x, void *payload,
     if (xs > 127) xs = 127;
     sc[b] = (uint8_t)(xs + 127);
     for (int i = 0; i < 16; i++) {
-      float v0 = ldexpf(oracle_bf16_to_f32(x[b * 32 + 2 * i]), -xs);
-      float v1 = ldexpf(oracle_bf16_to_f32(x[b * 32 + 2 * i + 1]), -xs);
+      float v0 = ldexpf(v[b * 32 + 2 * i], -xs);
+      float v1 = ldexpf(v[b * 32 + 2 * i + 1], -xs);
       q[b * 16 + i] =
           (uint8_t)(oracle_e2m1_encode(v0) | (oracle_e2m1_encode(v1) << 4));
     }
   }
+}
+
+/* One hidden row of h bf16 values: widened exactly to fp32, then encoded. */
+void oracle_encode_row(int fmt, int64_t h, const uint16_t *x, void *payload,
+                       void *scales) {
+  float *v = (float *)malloc((size_t)(h > 0 ? h : 1) * sizeof(float));
+  for (int64_t i = 0; i < h; i++) v[i] = oracle_bf16_to_f32(x[i]);
+  oracle_encode_row_f32(fmt, h, v, payload, scales);
+  free(v);
 }
 
 static int64_t payload_row_bytes(int fmt, int64_t h) {
@@ -466,8 +491,67 @@ void oracle_dispatch(int fmt, int64_t h, int64_t r_max, int64_t r_used,
   }
 }
 
+/* Gated dispatch, scatter form: each valid pair (t, j) writes
+ * encode(fl32(w[t,j] * x[t][c]) for every c) to packed row slot[t,j]; pad
+ * rows (rows below r_used that no pair names) are zero bytes; rows in
+ * [r_used, r_max) are zeroed only when zero_tail is set. */
+void oracle_dispatch_gated(int fmt, int64_t n, int k, int64_t h, int64_t r_max,
+                           int64_t r_used, const int32_t *slot, const float *w,
+                           const uint16_t *x, uint8_t *payload, uint8_t *scales,
+                           int zero_tail) {
+  int64_t pb = payload_row_bytes(fmt, h), sb = scale_row_bytes(fmt, h);
+  int64_t zero_to = zero_tail ? r_max : r_used;
+  for (int64_t r = 0; r < zero_to; r++) {
+    memset(payload + r * pb, 0, (size_t)pb);
+    if (sb) memset(scales + r * sb, 0, (size_t)sb);
+  }
+  float *v = (float *)malloc((size_t)(h > 0 ? h : 1) * sizeof(float));
+  for (int64_t t = 0; t < n; t++) {
+    for (int j = 0; j < k; j++) {
+      int32_t r = slot[t * k + j];
+      if (r < 0) continue;
+      float wt = w[t * k + j];
+      for (int64_t c = 0; c < h; c++) v[c] = wt * oracle_bf16_to_f32(x[t * h + c]);
+      oracle_encode_row_f32(fmt, h, v, payload + (int64_t)r * pb,
+                            sb ? scales + (int64_t)r * sb : 0);
+    }
+  }
+  free(v);
+}
+
+/* Multihot routing map -> compact top-k.  map[n][e_cnt] (nonzero = routed),
+ * probs[n][e_cnt] or NULL; ids[n][k] gets the routed experts of each token
+ * in ascending order, -1 after them; w[n][k] (if not NULL) their
+ * probabilities, 0 after them.  A token with more than k routed experts
+ * keeps its first k and sets ORC_MAP_OVERFLOW. */
+void oracle_routing_map_to_topk(int64_t n, int e_cnt, int k, const uint8_t *map,
+                                const float *probs, int32_t *ids, float *w,
+                                uint32_t *status) {
+  uint32_t st = 0;
+  for (int64_t t = 0; t < n; t++) {
+    int used = 0;
+    for (int e = 0; e < e_cnt; e++) {
+      if (!map[t * e_cnt + e]) continue;
+      if (used == k) {
+        st |= ORC_MAP_OVERFLOW;
+        break;
+      }
+      ids[t * k + used] = e;
+      if (w) w[t * k + used] = probs ? probs[t * e_cnt + e] : 1.0f;
+      used++;
+    }
+    for (int j = used; j < k; j++) {
+      ids[t * k + j] = -1;
+      if (w) w[t * k + j] = 0.0f;
+    }
+  }
+  *status = st;
+}
+
 /* O7: out[t][c] = bf16_rne( fmaf chain over j = 0..k-1 of w[t,j]*Y[slot][c] )
- * starting from +0.0f and skipping slots < 0. */
+ * starting from +0.0f and skipping slots < 0.  w == NULL: every weight is 1
+ * (the unweighted sum that follows a gated dispatch; fmaf(1, y, acc) is the
+ * correctly rounded y + acc). */
 void oracle_combine(int64_t n, int k, int64_t h, const int32_t *slot,
                     const float *w, const uint16_t *y, uint16_t *out) {
   for (int64_t t = 0; t < n; t++) {
@@ -476,7 +560,8 @@ void oracle_combine(int64_t n, int k, int64_t h, const int32_t *slot,
       for (int j = 0; j < k; j++) {
         int32_t s = slot[t * k + j];
         if (s < 0) continue;
-        acc = fmaf(w[t * k + j], oracle_bf16_to_f32(y[(int64_t)s * h + c]), acc);
+        float wt = w ? w[t * k + j] : 1.0f;
+        acc = fmaf(wt, oracle_bf16_to_f32(y[(int64_t)s * h + c]), acc);
       }
       out[t * h + c] = oracle_f32_to_bf16(acc);
     }
