@@ -8,7 +8,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmoe.so")
-SOURCES = ["api.hip", "plan.hip", "dispatch.hip", "combine.hip", "exchange.hip"]
+SOURCES = ["api.hip", "plan.hip", "dispatch.hip", "combine.hip", "exchange.hip", "routing_map.hip"]
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 
 

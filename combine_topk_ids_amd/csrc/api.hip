@@ -119,7 +119,26 @@ MOE_API int moe_dispatch(const moe_problem *p, const moe_plan *plan, const uint1
       !aligned(plan->expert_counts, 4) || !aligned(plan->expert_offsets, 4) ||
       (p->fmt == MOE_FMT_FP8_E4M3_B128 && !aligned(scales, 4)))
     return MOE_EALIGN;
-  return launched(moe::launch_dispatch(*p, *plan, hidden, payload, scales, static_cast<hipStream_t>(stream)));
+  return launched(moe::launch_dispatch(*p, *plan, hidden, nullptr, payload, scales,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+MOE_API int moe_dispatch_gated(const moe_problem *p, const moe_plan *plan, const uint16_t *hidden,
+                               const float *topk_weights, void *payload, void *scales, void *stream) {
+  const int rc = check(p);
+  if (rc != MOE_OK) return rc;
+  if (!plan || !plan->expert_counts || !plan->expert_offsets) return MOE_EINVAL;
+  if (p->n_tokens > 0 && (!hidden || !plan->slot || !topk_weights)) return MOE_EINVAL;
+  const bool quant = p->fmt != MOE_FMT_BF16;
+  if (max_rows_unchecked(*p) > 0 && (!payload || (quant && !scales))) return MOE_EINVAL;
+  if (!quant && scales) return MOE_EINVAL;
+  if (!aligned(hidden, 16) || !aligned(payload, 16) || !aligned(plan->slot, 4) || !aligned(topk_weights, 4) ||
+      !aligned(plan->expert_counts, 4) || !aligned(plan->expert_offsets, 4) ||
+      (p->fmt == MOE_FMT_FP8_E4M3_B128 && !aligned(scales, 4)))
+    return MOE_EALIGN;
+  // a null weight pointer selects the ungated kernels: keep the gated call gated
+  const float *w = p->n_tokens > 0 ? topk_weights : nullptr;
+  return launched(moe::launch_dispatch(*p, *plan, hidden, w, payload, scales, static_cast<hipStream_t>(stream)));
 }
 
 MOE_API int moe_combine(const moe_problem *p, const moe_plan *plan, const uint16_t *expert_out,
@@ -127,7 +146,7 @@ MOE_API int moe_combine(const moe_problem *p, const moe_plan *plan, const uint16
   const int rc = check(p);
   if (rc != MOE_OK) return rc;
   if (!plan) return MOE_EINVAL;
-  if (p->n_tokens > 0 && (!expert_out || !topk_weights || !out || !plan->slot)) return MOE_EINVAL;
+  if (p->n_tokens > 0 && (!expert_out || !out || !plan->slot)) return MOE_EINVAL;
   if (!aligned(expert_out, 16) || !aligned(out, 16) || !aligned(topk_weights, 4) || !aligned(plan->slot, 4))
     return MOE_EALIGN;
   return launched(moe::launch_combine(*p, *plan, expert_out, topk_weights, out, static_cast<hipStream_t>(stream)));
@@ -170,7 +189,26 @@ MOE_API int moe_exchange_dispatch(const moe_problem *p, const moe_exchange *x, c
   if (!aligned(hidden, 16) || !aligned(recv_payload, 16) || !aligned(x->recv_slot, 4) ||
       !aligned(x->recv_rows, 4) || (p->fmt == MOE_FMT_FP8_E4M3_B128 && !aligned(recv_scales, 4)))
     return MOE_EALIGN;
-  return launched(moe::launch_exchange_dispatch(*p, *x, hidden, recv_payload, recv_scales,
+  return launched(moe::launch_exchange_dispatch(*p, *x, hidden, nullptr, recv_payload, recv_scales,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+MOE_API int moe_exchange_dispatch_gated(const moe_problem *p, const moe_exchange *x, const uint16_t *hidden,
+                                        const float *topk_weights, void *recv_payload, void *recv_scales,
+                                        void *stream) {
+  const int rc = check_exchange(p);
+  if (rc != MOE_OK) return rc;
+  if (!x || !x->recv_rows) return MOE_EINVAL;
+  if (p->n_tokens > 0 && (!hidden || !x->recv_slot || !topk_weights)) return MOE_EINVAL;
+  const bool quant = p->fmt != MOE_FMT_BF16;
+  if (p->recv_capacity > 0 && (!recv_payload || (quant && !recv_scales))) return MOE_EINVAL;
+  if (!quant && recv_scales) return MOE_EINVAL;
+  if (!aligned(hidden, 16) || !aligned(recv_payload, 16) || !aligned(x->recv_slot, 4) ||
+      !aligned(x->recv_rows, 4) || !aligned(topk_weights, 4) ||
+      (p->fmt == MOE_FMT_FP8_E4M3_B128 && !aligned(recv_scales, 4)))
+    return MOE_EALIGN;
+  const float *w = p->n_tokens > 0 ? topk_weights : nullptr;
+  return launched(moe::launch_exchange_dispatch(*p, *x, hidden, w, recv_payload, recv_scales,
                                                 static_cast<hipStream_t>(stream)));
 }
 
@@ -179,11 +217,30 @@ MOE_API int moe_exchange_combine(const moe_problem *p, const moe_exchange *x, co
   const int rc = check_exchange(p);
   if (rc != MOE_OK) return rc;
   if (!x) return MOE_EINVAL;
-  if (p->n_tokens > 0 && (!expert_out || !topk_weights || !out || !x->recv_slot)) return MOE_EINVAL;
+  if (p->n_tokens > 0 && (!expert_out || !out || !x->recv_slot)) return MOE_EINVAL;
   if (!aligned(expert_out, 16) || !aligned(out, 16) || !aligned(topk_weights, 4) || !aligned(x->recv_slot, 4))
     return MOE_EALIGN;
   return launched(moe::launch_exchange_combine(*p, *x, expert_out, topk_weights, out,
                                                static_cast<hipStream_t>(stream)));
+}
+
+MOE_API size_t moe_map_workspace_bytes(const moe_problem *p) {
+  if (check(p) != MOE_OK) return 0;
+  return moe::map_workspace_bytes(*p);
+}
+
+MOE_API int moe_routing_map_to_topk(const moe_problem *p, const uint8_t *routing_map, const float *probs,
+                                    int32_t *topk_ids, float *topk_weights, uint32_t *status,
+                                    void *workspace, void *stream) {
+  const int rc = check(p);
+  if (rc != MOE_OK) return rc;
+  if (!status) return MOE_EINVAL;
+  if (p->n_tokens > 0 && (!routing_map || !topk_ids || !workspace)) return MOE_EINVAL;
+  if (!aligned(probs, 4) || !aligned(topk_ids, 4) || !aligned(topk_weights, 4) || !aligned(status, 4) ||
+      !aligned(workspace, 256))
+    return MOE_EALIGN;
+  return launched(moe::launch_routing_map_to_topk(*p, routing_map, probs, topk_ids, topk_weights, status,
+                                                  workspace, static_cast<hipStream_t>(stream)));
 }
 
 MOE_API const char *moe_strerror(int code) {

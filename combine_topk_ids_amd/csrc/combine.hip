@@ -13,6 +13,8 @@
 // out[t][c] = bf16_rne(acc), acc = +0 then acc = fma(w[t][j], Y[slot][c], acc)
 // for j = 0..k-1 in order, skipping masked slots: the same fp32 rounding
 // sequence on every element, so results do not depend on the launch shape.
+// Without weights (rows gated at dispatch: DeepSpeed v0.19.4 function index,
+// page 15, pre-multiplying by router scores) every w is 1.
 //
 // Design for gfx950.  One wave64 per (token, 1024-column slab); each lane
 // owns 8 consecutive columns (one 16-byte bf16 vector) of two 512-column
@@ -91,7 +93,9 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs g) {
   const int v0 = slab * kWave * kVec;
   const int64_t pair0 = static_cast<int64_t>(t) * k;
   const int my_slot = lane < k ? g.slot[pair0 + lane] : -1;
-  const float my_w = lane < k ? g.w[pair0 + lane] : 0.0f;
+  // no weights: every gate is 1 (the rows were weighted at dispatch), and
+  // fma(1, y, acc) is the correctly rounded y + acc
+  const float my_w = lane < k ? (g.w ? g.w[pair0 + lane] : 1.0f) : 0.0f;
   const u32x4 *ybase = reinterpret_cast<const u32x4 *>(g.y);
 
   float acc[kVec][8];

@@ -74,6 +74,7 @@ constexpr int kTailBlocks = MOE_TAIL_BLOCKS;
 struct DispatchArgs {
   const uint16_t *x;
   const int32_t *slot;
+  const float *w;  // [n][k] gates applied at dispatch (gated launches only)
   const int32_t *counts;
   const int32_t *offsets;
   uint8_t *payload;
@@ -272,6 +273,148 @@ __device__ void slab_mx(const DispatchArgs &g, int64_t t, int slab) {
   }
 }
 
+// ---- gated copies: row slot[t][j] holds encode(fl32(w[t][j] * x[t])) -------
+// (DeepSpeed v0.19.4 function index, page 15: token representations
+// pre-multiplied by router scores before expert compute.)  The slab is read
+// once; every copy is multiplied by its own gate and encoded on its own.  A
+// block maximum of the products needs no new reduction: rounding is
+// monotone, so max |fl32(w x_i)| = fl32(|w| max |x_i|).
+
+__device__ __forceinline__ float lane_gate(const DispatchArgs &g, int64_t t, int lane) {
+  return lane < g.k ? g.w[t * g.k + lane] : 0.0f;
+}
+
+__device__ __forceinline__ float bcast(float v, int j) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), j));
+}
+
+template <bool NT>
+__device__ void slab_bf16_gated(const DispatchArgs &g, int64_t t, int slab) {
+  const int lane = lane_id();
+  const int nvec = g.h / 8;
+  const int v0 = slab * kWave * kBf16Vec;
+  const u32x4 *src = reinterpret_cast<const u32x4 *>(g.x + t * g.h);
+  const int my_slot = lane_slot(g, t, lane);
+  const float my_w = lane_gate(g, t, lane);
+  u32x4 buf[kBf16Vec];
+#pragma unroll
+  for (int u = 0; u < kBf16Vec; ++u) {
+    const int idx = v0 + u * kWave + lane;
+    if (idx < nvec) buf[u] = __builtin_nontemporal_load(src + idx);
+  }
+  for (int j = 0; j < g.k; ++j) {
+    const int s = __builtin_amdgcn_readlane(my_slot, j);
+    if (s < 0) continue;
+    const float wj = bcast(my_w, j);
+    u32x4 *dst = reinterpret_cast<u32x4 *>(g.payload + static_cast<int64_t>(s) * g.row_bytes);
+#pragma unroll
+    for (int u = 0; u < kBf16Vec; ++u) {
+      const int idx = v0 + u * kWave + lane;
+      if (idx < nvec) {
+        uint4 r4;
+        r4.x = buf[u].x; r4.y = buf[u].y; r4.z = buf[u].z; r4.w = buf[u].w;
+        float f[8];
+        unpack8(r4, f);
+        u32x4 o;
+        o.x = f32_to_bf16(wj * f[0]) | (f32_to_bf16(wj * f[1]) << 16);
+        o.y = f32_to_bf16(wj * f[2]) | (f32_to_bf16(wj * f[3]) << 16);
+        o.z = f32_to_bf16(wj * f[4]) | (f32_to_bf16(wj * f[5]) << 16);
+        o.w = f32_to_bf16(wj * f[6]) | (f32_to_bf16(wj * f[7]) << 16);
+        store<NT>(dst + idx, o);
+      }
+    }
+  }
+}
+
+// FP8: per copy s = fl32(fl32(|w| amax) / 448) and codes E4M3(fl32(v / s)),
+// v = fl32(w x), with IEEE division (the reciprocal shortcut of the ungated
+// path is exact only for the bf16 values it was checked on).
+template <bool NT>
+__device__ void slab_fp8_gated(const DispatchArgs &g, int64_t t, int slab) {
+  static_assert(kQC == 1, "gated encoders take one chunk per wave");
+  const int lane = lane_id();
+  const int my_slot = lane_slot(g, t, lane);
+  const float my_w = lane_gate(g, t, lane);
+  const int elem = slab * kQuantSlab + lane * kLE;
+  float f[kLE];
+  load_lane(g, t, elem, f);
+  uint32_t am = quad_max(lane_absmax(f));
+  am = max(am, dpp<kRowHalfMirror>(am));
+  if (kLE == 8) am = max(am, dpp<kRowMirror>(am));
+  const float amax = __uint_as_float(am);
+  for (int j = 0; j < g.k; ++j) {
+    const int d = __builtin_amdgcn_readlane(my_slot, j);
+    if (d < 0) continue;
+    const float wj = bcast(my_w, j);
+    const float amj = fabsf(wj) * amax;
+    const float s = amj / 448.0f;  // 0 for a zero block, or when amj / 448 underflows
+    uint32_t w4[kLE / 4];
+    if (s != 0.0f) {
+      float q[kLE];
+#pragma unroll
+      for (int i = 0; i < kLE; ++i) q[i] = (wj * f[i]) / s;
+#pragma unroll
+      for (int qd = 0; qd < kLE / 4; ++qd)
+        w4[qd] = e4m3_pair_hw(q[4 * qd], q[4 * qd + 1]) | (e4m3_pair_hw(q[4 * qd + 2], q[4 * qd + 3]) << 16);
+    } else {
+#pragma unroll
+      for (int qd = 0; qd < kLE / 4; ++qd) w4[qd] = 0u;
+    }
+    if (elem < g.h) {
+      uint8_t *prow = g.payload + static_cast<int64_t>(d) * g.row_bytes;
+      float *srow = reinterpret_cast<float *>(g.scales + static_cast<int64_t>(d) * g.scale_bytes);
+      if (kLE == 16)
+        store<NT>(reinterpret_cast<u32x4 *>(prow + elem), u32x4{w4[0], w4[1], w4[2], w4[3]});
+      else
+        store<NT>(reinterpret_cast<u32x2 *>(prow + elem), u32x2{w4[0], w4[1]});
+      if ((lane & (128 / kLE - 1)) == 0) store<NT>(srow + elem / 128, s);
+    }
+  }
+}
+
+// MX-FP4: per copy X from fl32(|w| amax), codes E2M1(fl32(w x) * 2^-X).
+template <bool NT>
+__device__ void slab_mx_gated(const DispatchArgs &g, int64_t t, int slab) {
+  static_assert(kQC == 1, "gated encoders take one chunk per wave");
+  const int lane = lane_id();
+  const int my_slot = lane_slot(g, t, lane);
+  const float my_w = lane_gate(g, t, lane);
+  const int elem = slab * kQuantSlab + lane * kLE;
+  float f[kLE];
+  load_lane(g, t, elem, f);
+  uint32_t am = lane_absmax(f);
+  am = max(am, dpp<kQuadSwap1>(am));
+  if (kLE == 8) am = max(am, dpp<kQuadSwap2>(am));
+  const float amax = __uint_as_float(am);
+  for (int j = 0; j < g.k; ++j) {
+    const int d = __builtin_amdgcn_readlane(my_slot, j);
+    if (d < 0) continue;
+    const float wj = bcast(my_w, j);
+    const float amj = fabsf(wj) * amax;
+    const uint32_t ab = __float_as_uint(amj);
+    const int X = mx_exponent(ab);
+    const float mul = __uint_as_float(static_cast<uint32_t>(127 - X) << 23);  // 2^-X
+    uint32_t w8[kLE / 8];
+#pragma unroll
+    for (int qd = 0; qd < kLE / 8; ++qd) {
+      uint32_t v = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v |= e2m1_rne_sat((wj * f[8 * qd + i]) * mul) << (4 * i);
+      w8[qd] = ab == 0 ? 0u : v;
+    }
+    if (elem < g.h) {
+      uint8_t *prow = g.payload + static_cast<int64_t>(d) * g.row_bytes;
+      uint8_t *srow = g.scales + static_cast<int64_t>(d) * g.scale_bytes;
+      if (kLE == 16)
+        store<NT>(reinterpret_cast<u32x2 *>(prow + elem / 2), u32x2{w8[0], w8[1]});
+      else
+        store<NT>(reinterpret_cast<uint32_t *>(prow + elem / 2), w8[0]);
+      if ((lane & (32 / kLE - 1)) == 0)
+        store<NT>(srow + elem / 32, static_cast<uint8_t>(ab == 0 ? 0 : X + 127));
+    }
+  }
+}
+
 // ---- zero fill of one packed row (payload and scales) -----------------------
 template <bool NT>
 __device__ void zero_row(const DispatchArgs &g, int64_t r) {
@@ -316,7 +459,7 @@ __device__ void zero_tails(const DispatchArgs &g, int blk, int wave) {
   }
 }
 
-template <int FMT, bool NT>
+template <int FMT, bool NT, bool GATED>
 __global__ __launch_bounds__(kThreads) void dispatch_kernel(DispatchArgs g) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   int blk = blockIdx.x;
@@ -333,9 +476,15 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(DispatchArgs g) {
     const int t = q / g.slabs;
     if (t >= g.n) return;
     const int slab = q - t * g.slabs;
-    if (FMT == MOE_FMT_BF16) slab_bf16<NT>(g, t, slab);
-    else if (FMT == MOE_FMT_FP8_E4M3_B128) slab_fp8<NT>(g, t, slab);
-    else slab_mx<NT>(g, t, slab);
+    if (GATED) {
+      if (FMT == MOE_FMT_BF16) slab_bf16_gated<NT>(g, t, slab);
+      else if (FMT == MOE_FMT_FP8_E4M3_B128) slab_fp8_gated<NT>(g, t, slab);
+      else slab_mx_gated<NT>(g, t, slab);
+    } else {
+      if (FMT == MOE_FMT_BF16) slab_bf16<NT>(g, t, slab);
+      else if (FMT == MOE_FMT_FP8_E4M3_B128) slab_fp8<NT>(g, t, slab);
+      else slab_mx<NT>(g, t, slab);
+    }
     return;
   }
   blk -= g.token_blocks;
@@ -357,7 +506,10 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(DispatchArgs g) {
 
 template <int FMT>
 void launch_fmt(const DispatchArgs &g, int grid, hipStream_t stream) {
-  dispatch_kernel<FMT, MOE_DISPATCH_NT_STORE != 0><<<grid, kThreads, 0, stream>>>(g);
+  if (g.w)
+    dispatch_kernel<FMT, MOE_DISPATCH_NT_STORE != 0, true><<<grid, kThreads, 0, stream>>>(g);
+  else
+    dispatch_kernel<FMT, MOE_DISPATCH_NT_STORE != 0, false><<<grid, kThreads, 0, stream>>>(g);
 }
 
 }  // namespace
@@ -405,8 +557,9 @@ hipError_t launch_args(const DispatchArgs &g, int fmt, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_dispatch(const moe_problem &p, const moe_plan &plan, const uint16_t *hidden,
-                           void *payload, void *scales, hipStream_t stream) {
+                           const float *gates, void *payload, void *scales, hipStream_t stream) {
   DispatchArgs g = base_args(p, p.n_tokens, plan.slot, hidden, payload, scales);
+  g.w = gates;
   g.counts = plan.expert_counts;
   g.offsets = plan.expert_offsets;
   g.r_max = p.n_tokens * p.top_k + static_cast<int64_t>(p.n_experts) * (p.pad_multiple - 1);
@@ -421,9 +574,10 @@ hipError_t launch_dispatch(const moe_problem &p, const moe_plan &plan, const uin
 }
 
 hipError_t launch_exchange_dispatch(const moe_problem &p, const moe_exchange &x, const uint16_t *hidden,
-                                    void *payload, void *scales, hipStream_t stream) {
+                                    const float *gates, void *payload, void *scales, hipStream_t stream) {
   const int64_t tokens = p.n_tokens * p.ep;
   DispatchArgs g = base_args(p, tokens, x.recv_slot, hidden, payload, scales);
+  g.w = gates;
   g.r_max = p.recv_capacity * p.ep;
   g.pad_blocks = 0;  // no per-expert padding in receive buffers
   g.seg_used = x.recv_rows;

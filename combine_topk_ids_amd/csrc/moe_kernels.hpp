@@ -49,12 +49,20 @@ size_t exchange_workspace_bytes(const moe_problem &p);
 hipError_t launch_exchange_plan(const moe_problem &p, const int32_t *ids, const moe_exchange &x,
                                 void *workspace, hipStream_t stream);
 hipError_t launch_exchange_dispatch(const moe_problem &p, const moe_exchange &x, const uint16_t *hidden,
-                                    void *payload, void *scales, hipStream_t stream);
+                                    const float *gates, void *payload, void *scales, hipStream_t stream);
+
+// Multihot routing map [N][E] (+ optional dense probabilities) -> compact
+// top-k IDs and weights; status gets MOE_STATUS_MAP_OVERFLOW.
+size_t map_workspace_bytes(const moe_problem &p);
+hipError_t launch_routing_map_to_topk(const moe_problem &p, const uint8_t *map, const float *probs,
+                                      int32_t *ids, float *weights, uint32_t *status, void *workspace,
+                                      hipStream_t stream);
 hipError_t launch_exchange_combine(const moe_problem &p, const moe_exchange &x, const uint16_t *expert_out,
                                    const float *weights, uint16_t *out, hipStream_t stream);
 
+// gates: NULL, or [N][k] weights applied to each copy at dispatch
 hipError_t launch_dispatch(const moe_problem &p, const moe_plan &plan, const uint16_t *hidden,
-                           void *payload, void *scales, hipStream_t stream);
+                           const float *gates, void *payload, void *scales, hipStream_t stream);
 
 hipError_t launch_combine(const moe_problem &p, const moe_plan &plan, const uint16_t *expert_out,
                           const float *weights, uint16_t *out, hipStream_t stream);

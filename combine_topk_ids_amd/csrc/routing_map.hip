@@ -1,0 +1,132 @@
+// routing_map.hip -- dense multihot routing map to the compact top-k form.
+//
+// What is computed (pages cited by title and section):
+//   NeMo Automodel token_dispatcher API -- _DeepepManager._indices_to_multihot
+//     (top-k indices with -1 masks and their probabilities correspond to a
+//     multihot routing map and multihot probabilities), the conversion from
+//     top-k indices to the multihot routing_map format, and
+//     TokenDispatcherConfig.moe_hybridep_compact_routing (routing handed over
+//     either as compact top-k indices or as a dense Boolean map).
+//
+// For every token: the experts whose map byte is nonzero, in ascending
+// order, fill ids[t][0..); their probabilities (1 without a probability
+// array) fill weights[t][0..); the remaining slots get -1 and 0.  A token
+// with more than k routed experts keeps its first k, and the call's status
+// word gets MOE_STATUS_MAP_OVERFLOW.
+//
+// Design for gfx950.  The work is tiny and latency-bound: one thread per
+// token scans its map row with 16-byte loads (byte loads when rows are not
+// 16-byte aligned), each block ORs its overflow flags into one workspace
+// word, and a one-block kernel ORs those into the status word, so the
+// status needs no clearing before the call.
+#include "moe_device.hpp"
+#include "moe_kernels.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+
+struct MapArgs {
+  const uint8_t *map;
+  const float *probs;
+  int32_t *ids;
+  float *w;
+  uint32_t *partial;  // [nblocks] overflow flags per block
+  uint32_t *status;
+  int64_t n;
+  int e, k;
+  int nblocks;
+  bool vec;  // rows are 16-byte aligned
+};
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(kThreads) void map_to_topk_kernel(MapArgs g) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  uint32_t fl = 0;
+  if (t < g.n) {
+    const uint8_t *row = g.map + t * g.e;
+    int32_t *ids = g.ids + t * g.k;
+    float *w = g.w ? g.w + t * g.k : nullptr;
+    const float *pr = g.probs ? g.probs + t * g.e : nullptr;
+    int used = 0;
+    for (int e0 = 0; e0 < g.e && fl == 0; e0 += 16) {
+      uint8_t b[16];
+      if (g.vec) {
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(row + e0);
+        const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 16; ++i) b[i] = static_cast<uint8_t>(wd[i / 4] >> (8 * (i % 4)));
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) b[i] = e0 + i < g.e ? row[e0 + i] : 0;
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (b[i] == 0 || fl != 0) continue;
+        if (used == g.k) {
+          fl = MOE_STATUS_MAP_OVERFLOW;
+          continue;
+        }
+        ids[used] = e0 + i;
+        if (w) w[used] = pr ? pr[e0 + i] : 1.0f;
+        ++used;
+      }
+    }
+    for (int j = used; j < g.k; ++j) {
+      ids[j] = -1;
+      if (w) w[j] = 0.0f;
+    }
+  }
+  const uint64_t any = ballot(fl != 0);
+  __shared__ uint32_t s_fl;
+  if (threadIdx.x == 0) s_fl = 0;
+  __syncthreads();
+  if (lane_id() == 0 && any) atomicOr(&s_fl, MOE_STATUS_MAP_OVERFLOW);
+  __syncthreads();
+  if (threadIdx.x == 0) g.partial[blockIdx.x] = s_fl;
+}
+
+__global__ __launch_bounds__(kThreads) void map_status_kernel(MapArgs g) {
+  uint32_t fl = 0;
+  for (int b = threadIdx.x; b < g.nblocks; b += kThreads) fl |= g.partial[b];
+  const uint64_t any = ballot(fl != 0);
+  __shared__ uint32_t s_fl;
+  if (threadIdx.x == 0) s_fl = 0;
+  __syncthreads();
+  if (lane_id() == 0 && any) atomicOr(&s_fl, MOE_STATUS_MAP_OVERFLOW);
+  __syncthreads();
+  if (threadIdx.x == 0) *g.status = s_fl;
+}
+
+int map_blocks(const moe_problem &p) { return static_cast<int>((p.n_tokens + kThreads - 1) / kThreads); }
+
+}  // namespace
+
+size_t map_workspace_bytes(const moe_problem &p) {
+  const size_t bytes = static_cast<size_t>(map_blocks(p)) * sizeof(uint32_t);
+  return (bytes + 255) & ~static_cast<size_t>(255);
+}
+
+hipError_t launch_routing_map_to_topk(const moe_problem &p, const uint8_t *map, const float *probs,
+                                      int32_t *ids, float *weights, uint32_t *status, void *workspace,
+                                      hipStream_t stream) {
+  MapArgs g;
+  g.map = map;
+  g.probs = probs;
+  g.ids = ids;
+  g.w = weights;
+  g.partial = static_cast<uint32_t *>(workspace);
+  g.status = status;
+  g.n = p.n_tokens;
+  g.e = p.n_experts;
+  g.k = p.top_k;
+  g.nblocks = map_blocks(p);
+  g.vec = p.n_experts % 16 == 0 && (reinterpret_cast<uintptr_t>(map) & 15) == 0;
+  if (g.nblocks > 0) map_to_topk_kernel<<<g.nblocks, kThreads, 0, stream>>>(g);
+  map_status_kernel<<<1, kThreads, 0, stream>>>(g);
+  return hipGetLastError();
+}
+
+}  // namespace moe

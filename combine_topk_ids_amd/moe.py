@@ -20,16 +20,17 @@ import torch  # first: libmoe then binds to the HIP runtime torch has loaded
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 
 MOE_OK, MOE_EINVAL, MOE_EALIGN, MOE_EOVERFLOW, MOE_EHIP = 0, -1, -2, -3, -4
-STATUS_BAD_ID, STATUS_DUP_ID, STATUS_CAPACITY = 1, 2, 4
+STATUS_BAD_ID, STATUS_DUP_ID, STATUS_CAPACITY, STATUS_MAP_OVERFLOW = 1, 2, 4, 8
 FMT = {"bf16": 0, "fp8": 1, "mxfp4": 2}
 FLAG_ZERO_TAIL = 1
 
 # every symbol include/moe.h declares
 EXPORTS = ("moe_check_problem", "moe_max_rows", "moe_payload_row_bytes",
            "moe_scale_row_bytes", "moe_workspace_bytes", "moe_dispatch_plan",
-           "moe_dispatch", "moe_combine", "moe_check_exchange",
+           "moe_dispatch", "moe_dispatch_gated", "moe_combine", "moe_check_exchange",
            "moe_exchange_workspace_bytes", "moe_exchange_plan", "moe_exchange_dispatch",
-           "moe_exchange_combine", "moe_strerror")
+           "moe_exchange_dispatch_gated", "moe_exchange_combine", "moe_map_workspace_bytes",
+           "moe_routing_map_to_topk", "moe_strerror")
 
 
 class MoeError(RuntimeError):
@@ -73,12 +74,16 @@ def _load() -> ctypes.CDLL:
         "moe_workspace_bytes": (ctypes.c_size_t, [P]),
         "moe_dispatch_plan": (ctypes.c_int, [P, V, ctypes.POINTER(Plan), V, V]),
         "moe_dispatch": (ctypes.c_int, [P, ctypes.POINTER(Plan), V, V, V, V]),
+        "moe_dispatch_gated": (ctypes.c_int, [P, ctypes.POINTER(Plan), V, V, V, V, V]),
         "moe_combine": (ctypes.c_int, [P, ctypes.POINTER(Plan), V, V, V, V]),
         "moe_check_exchange": (ctypes.c_int, [P]),
         "moe_exchange_workspace_bytes": (ctypes.c_size_t, [P]),
         "moe_exchange_plan": (ctypes.c_int, [P, V, ctypes.POINTER(Exchange), V, V]),
         "moe_exchange_dispatch": (ctypes.c_int, [P, ctypes.POINTER(Exchange), V, V, V, V]),
+        "moe_exchange_dispatch_gated": (ctypes.c_int, [P, ctypes.POINTER(Exchange), V, V, V, V, V]),
         "moe_exchange_combine": (ctypes.c_int, [P, ctypes.POINTER(Exchange), V, V, V, V]),
+        "moe_map_workspace_bytes": (ctypes.c_size_t, [P]),
+        "moe_routing_map_to_topk": (ctypes.c_int, [P, V, V, V, V, V, V, V]),
         "moe_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     }
     for name, (res, args) in sig.items():
@@ -260,11 +265,29 @@ def moe_dispatch(p: Problem, plan: PlanBuffers, hidden: torch.Tensor, payload: t
     _checked(rc, "moe_dispatch")
 
 
+def moe_dispatch_gated(p: Problem, plan: PlanBuffers, hidden: torch.Tensor,
+                       topk_weights: torch.Tensor, payload: torch.Tensor,
+                       scales: torch.Tensor | None, stream=None) -> None:
+    r_max, pb, sb, _ = _sizes(p)
+    x = _dev(hidden, "hidden", _BF16, p.n_tokens * p.hidden)
+    w = _dev(topk_weights, "topk_weights", (torch.float32,), p.n_tokens * p.top_k)
+    if payload.numel() * payload.element_size() < r_max * pb:
+        raise ValueError("payload is smaller than R_max rows")
+    if scales is not None and scales.numel() * scales.element_size() < r_max * sb:
+        raise ValueError("scales is smaller than R_max rows")
+    pay = _dev(payload, "payload", _PAYLOAD)
+    sc = _dev(scales, "scales", (torch.float32, torch.uint8))
+    rc = lib.moe_dispatch_gated(ctypes.byref(p), ctypes.byref(plan.as_struct()), x, w, pay,
+                                sc or None, _stream(stream))
+    _checked(rc, "moe_dispatch_gated")
+
+
 def moe_combine(p: Problem, plan: PlanBuffers, expert_out: torch.Tensor,
-                topk_weights: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+                topk_weights: torch.Tensor | None, out: torch.Tensor, stream=None) -> None:
+    """topk_weights None: weights of 1 (after a gated dispatch)."""
     r_max = _sizes(p)[0]
     y = _dev(expert_out, "expert_out", _BF16, r_max * p.hidden)
-    w = _dev(topk_weights, "topk_weights", (torch.float32,), p.n_tokens * p.top_k)
+    w = _dev(topk_weights, "topk_weights", (torch.float32,), p.n_tokens * p.top_k) or None
     o = _dev(out, "out", _BF16, p.n_tokens * p.hidden)
     rc = lib.moe_combine(ctypes.byref(p), ctypes.byref(plan.as_struct()), y, w, o,
                          _stream(stream))
@@ -362,12 +385,55 @@ def moe_exchange_dispatch(p: Problem, x: ExchangeBuffers, hidden: torch.Tensor,
     _checked(rc, "moe_exchange_dispatch")
 
 
+def moe_exchange_dispatch_gated(p: Problem, x: ExchangeBuffers, hidden: torch.Tensor,
+                                topk_weights: torch.Tensor, payload: torch.Tensor,
+                                scales: torch.Tensor | None, stream=None) -> None:
+    _, pb, sb, _ = _sizes(p)
+    rows = p.ep * p.recv_capacity
+    h = _dev(hidden, "hidden", _BF16, p.ep * p.n_tokens * p.hidden)
+    w = _dev(topk_weights, "topk_weights", (torch.float32,), p.ep * p.n_tokens * p.top_k)
+    if payload.numel() * payload.element_size() < rows * pb:
+        raise ValueError("payload is smaller than EP * C rows")
+    if scales is not None and scales.numel() * scales.element_size() < rows * sb:
+        raise ValueError("scales is smaller than EP * C rows")
+    pay = _dev(payload, "payload", _PAYLOAD)
+    sc = _dev(scales, "scales", (torch.float32, torch.uint8))
+    rc = lib.moe_exchange_dispatch_gated(ctypes.byref(p), ctypes.byref(x.as_struct()), h, w, pay,
+                                         sc or None, _stream(stream))
+    _checked(rc, "moe_exchange_dispatch_gated")
+
+
 def moe_exchange_combine(p: Problem, x: ExchangeBuffers, expert_out: torch.Tensor,
-                         topk_weights: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+                         topk_weights: torch.Tensor | None, out: torch.Tensor, stream=None) -> None:
+    """topk_weights None: weights of 1 (after a gated dispatch)."""
     tokens = p.ep * p.n_tokens
     y = _dev(expert_out, "expert_out", _BF16, p.ep * p.recv_capacity * p.hidden)
-    w = _dev(topk_weights, "topk_weights", (torch.float32,), tokens * p.top_k)
+    w = _dev(topk_weights, "topk_weights", (torch.float32,), tokens * p.top_k) or None
     o = _dev(out, "out", _BF16, tokens * p.hidden)
     rc = lib.moe_exchange_combine(ctypes.byref(p), ctypes.byref(x.as_struct()), y, w, o,
                                   _stream(stream))
     _checked(rc, "moe_exchange_combine")
+
+
+# ---- dense routing-map input ----------------------------------------------------
+
+def moe_map_workspace_bytes(p: Problem) -> int:
+    return int(lib.moe_map_workspace_bytes(ctypes.byref(p)))
+
+
+def moe_routing_map_to_topk(p: Problem, routing_map: torch.Tensor, probs: torch.Tensor | None,
+                            topk_ids: torch.Tensor, topk_weights: torch.Tensor | None,
+                            status: torch.Tensor, workspace: torch.Tensor, stream=None) -> None:
+    """Multihot map [N, E] (uint8 or bool; nonzero = routed) and optional dense
+    probabilities [N, E] -> compact top-k IDs and weights; status[0] gets
+    STATUS_MAP_OVERFLOW if a token routes to more than k experts."""
+    ne, nk = p.n_tokens * p.n_experts, p.n_tokens * p.top_k
+    m = _dev(routing_map, "routing_map", (torch.uint8, torch.bool), ne)
+    pr = _dev(probs, "probs", (torch.float32,), ne) or None
+    ids = _dev(topk_ids, "topk_ids", (torch.int32,), nk)
+    w = _dev(topk_weights, "topk_weights", (torch.float32,), nk) or None
+    st = _dev(status, "status", (torch.int32,), 1)
+    _dev(workspace, "workspace", (torch.uint8,), moe_map_workspace_bytes(p))
+    rc = lib.moe_routing_map_to_topk(ctypes.byref(p), m, pr, ids, w, st, workspace.data_ptr(),
+                                     _stream(stream))
+    _checked(rc, "moe_routing_map_to_topk")

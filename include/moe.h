@@ -72,6 +72,9 @@ extern "C" {
 #define MOE_STATUS_BAD_ID 1u   /* an ID outside [-1, E): treated as masked   */
 #define MOE_STATUS_DUP_ID 2u   /* an ID repeated within one token: routed    */
 #define MOE_STATUS_CAPACITY 4u /* some rank receives more than recv_capacity */
+/* (status of moe_routing_map_to_topk) a token routes to more than k experts:
+ * its first k, in expert order, are kept */
+#define MOE_STATUS_MAP_OVERFLOW 8u
 
 /* ---- payload formats ---------------------------------------------------- */
 typedef enum moe_fmt {
@@ -174,11 +177,26 @@ MOE_API int moe_dispatch(const moe_problem *p, const moe_plan *plan,
                          const uint16_t *hidden, void *payload, void *scales,
                          void *stream);
 
+/* Gated dispatch: as moe_dispatch, but each valid pair (t, j) writes
+ * encode(fl32(topk_weights[t][j] * hidden[t][c]) for every c), the token row
+ * pre-multiplied by its gate, to packed row slot[t][j] (DeepSpeed v0.19.4
+ * function index, page 15: pre-multiplying token representations by router
+ * scores before expert compute).  Each copy is encoded on its own: for FP8
+ * its block scale is fl32(fl32(|w| * amax) / 448) and its codes
+ * E4M3(fl32(v / s)) with v = fl32(w * x); for MX-FP4 its exponent comes from
+ * fl32(|w| * amax).  topk_weights: device float [N][k].  A combine of gated
+ * rows passes NULL weights. */
+MOE_API int moe_dispatch_gated(const moe_problem *p, const moe_plan *plan,
+                               const uint16_t *hidden, const float *topk_weights,
+                               void *payload, void *scales, void *stream);
+
 /* Combine: out[t][c] = bf16_rne( fp32 fused multiply-add chain, starting
  * from +0 and running over j = 0..k-1 in order, of
  * topk_weights[t][j] * expert_out[slot[t][j]][c] ), skipping slots < 0.
  * expert_out: device bf16 bits [R_max][H] (only rows some slot names are
- * read); topk_weights: device float [N][k]; out: device bf16 bits [N][H]. */
+ * read); topk_weights: device float [N][k], or NULL for weights of 1 (the
+ * unweighted sum that follows a gated dispatch); out: device bf16 bits
+ * [N][H]. */
 MOE_API int moe_combine(const moe_problem *p, const moe_plan *plan,
                         const uint16_t *expert_out, const float *topk_weights,
                         uint16_t *out, void *stream);
@@ -263,15 +281,51 @@ MOE_API int moe_exchange_dispatch(const moe_problem *p, const moe_exchange *x,
                                   const uint16_t *hidden, void *recv_payload,
                                   void *recv_scales, void *stream);
 
+/* As moe_exchange_dispatch, with every copy pre-multiplied by its gate as in
+ * moe_dispatch_gated; topk_weights: device float [EP][N][k]. */
+MOE_API int moe_exchange_dispatch_gated(const moe_problem *p,
+                                        const moe_exchange *x,
+                                        const uint16_t *hidden,
+                                        const float *topk_weights,
+                                        void *recv_payload, void *recv_scales,
+                                        void *stream);
+
 /* Reverse exchange and combine: out[s][t][c] = bf16_rne( fp32 fused
  * multiply-add chain over j = 0..k-1 in order, from +0, of
  * topk_weights[s][t][j] * expert_out[recv_slot[s][t][j]][c] ), skipping
  * receive rows < 0.  expert_out: device bf16 bits [EP][C][H];
- * topk_weights: device float [EP][N][k]; out: device bf16 bits [EP][N][H]. */
+ * topk_weights: device float [EP][N][k], or NULL for weights of 1; out:
+ * device bf16 bits [EP][N][H]. */
 MOE_API int moe_exchange_combine(const moe_problem *p, const moe_exchange *x,
                                  const uint16_t *expert_out,
                                  const float *topk_weights, uint16_t *out,
                                  void *stream);
+
+/* ---- dense routing-map input -------------------------------------------
+ *
+ * NeMo Automodel token_dispatcher API: _DeepepManager._indices_to_multihot
+ * (top-k indices with -1 masks and probabilities <-> a multihot routing map
+ * and multihot probabilities) and TokenDispatcherConfig.
+ * moe_hybridep_compact_routing (routing given as compact top-k indices or as
+ * a dense Boolean map).  The dense form is turned into the compact one that
+ * moe_dispatch_plan and the combine take. */
+
+/* Device scratch bytes moe_routing_map_to_topk needs (0 for N = 0 or an
+ * invalid problem). */
+MOE_API size_t moe_map_workspace_bytes(const moe_problem *p);
+
+/* routing_map: device uint8 [N][E], nonzero = the token routes to that
+ * expert; probs: device float [N][E] or NULL.  Writes topk_ids [N][k]: the
+ * token's routed experts in ascending order, then -1; topk_weights [N][k]
+ * (or NULL to skip): probs[t][e] of those experts (1 without probs), then 0;
+ * status [1] (written, not accumulated): MOE_STATUS_MAP_OVERFLOW if some
+ * token routes to more than k experts (it keeps its first k).  Uses
+ * p->n_tokens, p->n_experts and p->top_k. */
+MOE_API int moe_routing_map_to_topk(const moe_problem *p,
+                                    const uint8_t *routing_map,
+                                    const float *probs, int32_t *topk_ids,
+                                    float *topk_weights, uint32_t *status,
+                                    void *workspace, void *stream);
 
 /* Static text for a return code. */
 MOE_API const char *moe_strerror(int code);

@@ -166,4 +166,32 @@ def test_exchange_null_and_misaligned_pointers_rejected(moe):
     p8 = moe.problem(64, 256, 2, 8, 4, recv_capacity=64, fmt="fp8")
     assert moe.lib.moe_exchange_dispatch(ref(p8), ref(full), fake, fake, None, None) == -1
     assert moe.lib.moe_exchange_combine(ref(p), ref(full), fake, fake, fake + 2, None) == -2
-    assert moe.lib.moe_exchange_combine(ref(p), ref(full), fake, None, fake, None) == -1
+    assert moe.lib.moe_exchange_combine(ref(p), ref(full), None, fake, fake, None) == -1
+
+
+# ---- gates at dispatch, dense routing map -------------------------------------
+
+def test_gated_and_map_entry_points_check_arguments(moe):
+    ref = ctypes.byref
+    fake = 1 << 20
+    p = moe.problem(64, 256, 2, 8, 4)
+    full = moe.Plan(*([fake] * 7))
+    # gates are required by the gated dispatch (and only there)
+    assert moe.lib.moe_dispatch_gated(ref(p), ref(full), fake, None, fake, None, None) == -1
+    assert moe.lib.moe_dispatch_gated(ref(p), ref(full), fake, fake + 2, fake, None, None) == -2
+    assert moe.lib.moe_dispatch_gated(ref(p), ref(full), fake, fake, fake, fake, None) == -1
+    bad = moe.problem(64, 12, 2, 8, 4)
+    assert moe.lib.moe_dispatch_gated(ref(bad), ref(full), fake, fake, fake, None, None) == -1
+    px = moe.problem(64, 256, 2, 8, 4, recv_capacity=64)
+    fx = moe.Exchange(*([fake] * 8))
+    assert moe.lib.moe_exchange_dispatch_gated(ref(px), ref(fx), fake, None, fake, None, None) == -1
+    assert moe.lib.moe_exchange_dispatch_gated(ref(px), ref(fx), fake, fake + 1, fake, None, None) == -2
+    # routing map
+    assert moe.moe_map_workspace_bytes(p) % 256 == 0 and moe.moe_map_workspace_bytes(p) > 0
+    assert moe.moe_map_workspace_bytes(moe.problem(0, 256, 2, 8, 4)) == 0
+    assert moe.lib.moe_routing_map_to_topk(ref(p), fake, None, fake, None, None, fake, None) == -1
+    assert moe.lib.moe_routing_map_to_topk(ref(p), None, None, fake, None, fake, fake, None) == -1
+    assert moe.lib.moe_routing_map_to_topk(ref(p), fake, None, fake, None, fake, None, None) == -1
+    assert moe.lib.moe_routing_map_to_topk(ref(p), fake, fake + 2, fake, None, fake, fake, None) == -2
+    assert moe.lib.moe_routing_map_to_topk(ref(p), fake, None, fake, None, fake, fake + 16, None) == -2
+    assert moe.lib.moe_routing_map_to_topk(ref(bad), fake, None, fake, None, fake, fake, None) == -1
