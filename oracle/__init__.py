@@ -27,7 +27,7 @@ SRC = os.path.join(HERE, "oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
 FMT = {"bf16": 0, "fp8": 1, "mxfp4": 2}
-BAD_ID, DUP_ID, CAPACITY, MAP_OVERFLOW = 1, 2, 4, 8
+BAD_ID, DUP_ID, CAPACITY, MAP_OVERFLOW, DROPPED = 1, 2, 4, 8, 16
 
 _lib = None
 
@@ -55,6 +55,10 @@ def _load():
         lib.oracle_max_rows.argtypes = [i64, i32, i32, i32]
         lib.oracle_plan.restype = None
         lib.oracle_plan.argtypes = [i64, i32, i32, i32, i32, i64, i64] + [p] * 8
+        lib.oracle_expert_capacity.restype = i64
+        lib.oracle_expert_capacity.argtypes = [i64, i32, i32, ctypes.c_double]
+        lib.oracle_capacity_plan.restype = None
+        lib.oracle_capacity_plan.argtypes = [i64, i32, i32, i32, i64, i64, i64] + [p] * 8
         lib.oracle_exchange_plan.restype = None
         lib.oracle_exchange_plan.argtypes = [i64, i32, i32, i32, i64, i64] + [p] * 9
         lib.oracle_encode_row.restype = None
@@ -128,6 +132,38 @@ def plan(ids: np.ndarray, n_experts: int, ep: int, pad_multiple: int,
                         _ptr(out["packed_src"]), _ptr(out["status"]))
     out["r_max"] = r_max
     out["r_used"] = int(out["expert_offsets"][e])
+    out["status"] = int(out["status"][0])
+    return out
+
+
+def expert_capacity(n: int, k: int, e: int, cf: float) -> int:
+    """ceil(cf * N * k / E)."""
+    return int(_load().oracle_expert_capacity(n, k, e, cf))
+
+
+def capacity_plan(ids: np.ndarray, n_experts: int, ep: int, expert_cap: int,
+                  recv_capacity: int, hidden: int) -> dict:
+    """Plan of the fixed-capacity layout: expert e owns rows e*cap ..
+    e*cap+cap-1; pairs past an expert's capacity are dropped."""
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    n, k = ids.shape
+    e = n_experts
+    r_max = e * expert_cap
+    out = dict(
+        expert_counts=np.zeros(e, np.int32),
+        expert_offsets=np.zeros(e + 1, np.int32),
+        dest_counts=np.zeros(ep, np.int32),
+        rank_table=np.zeros((4, ep), np.uint32),
+        slot=np.zeros((n, k), np.int32),
+        packed_src=np.zeros(max(r_max, 0), np.int32),
+        status=np.zeros(1, np.uint32),
+    )
+    _load().oracle_capacity_plan(n, k, e, ep, recv_capacity, hidden, expert_cap, _ptr(ids),
+                                 _ptr(out["expert_counts"]), _ptr(out["expert_offsets"]),
+                                 _ptr(out["dest_counts"]), _ptr(out["rank_table"]),
+                                 _ptr(out["slot"]), _ptr(out["packed_src"]), _ptr(out["status"]))
+    out["r_max"] = r_max
+    out["r_used"] = r_max
     out["status"] = int(out["status"][0])
     return out
 

@@ -50,6 +50,18 @@
  *               rows a rank receives from it).
  *             - Mojo ep.dispatch_async.block.scaled.nv struct: recv_count_ptrs
  *               (tokens received per expert).
+ *   capacity plan  fixed per-expert capacity: expert e owns rows
+ *             e*cap .. e*cap+cap-1; its first cap pairs in flat order are
+ *             kept, later ones dropped (slot -1, DROPPED flagged); unused
+ *             rows of an expert are zero rows; cap = ceil(cf * N * k / E)
+ *             for a capacity factor cf.
+ *             - NeMo Automodel token_dispatcher API:
+ *               TokenDispatcherConfig.moe_expert_capacity_factor (a capacity
+ *               factor per expert; None means nothing is dropped) and the
+ *               _DeepepManager capacity_factor argument.
+ *             - DeepSpeed v0.19.4 function index, page 15: the dispatch entry
+ *               (every routed token placed in its expert slot of an
+ *               [e, c, m] buffer; the inverted map makes it one gather).
  *   routing map  a multihot [N, E] map (nonzero byte = routed) with dense
  *             probabilities [N, E] turned into the compact form: a token's
  *             routed experts in ascending order, their probabilities, -1 and
@@ -92,6 +104,7 @@
 #define ORC_DUP_ID 2u
 #define ORC_CAPACITY 4u
 #define ORC_MAP_OVERFLOW 8u
+#define ORC_DROPPED 16u
 
 #define ORC_FMT_BF16 0
 #define ORC_FMT_FP8 1
@@ -273,6 +286,78 @@ void oracle_plan(int64_t n, int k, int e_cnt, int ep, int a, int64_t cap,
           packed_src[next] = (int32_t)t;
           next++;
         }
+      }
+    }
+  }
+  *status = st;
+}
+
+/* ------------------------------------------------------- capacity plan --- */
+
+/* Per-expert capacity from a capacity factor: ceil(cf * N * k / E), computed
+ * in double precision. */
+int64_t oracle_expert_capacity(int64_t n, int k, int e, double cf) {
+  return (int64_t)ceil(cf * (double)n * (double)k / (double)e);
+}
+
+/* C1..C5: validate and count as O1-O2; offsets[e] = e*cap; per rank r the
+ * kept rows S_r = sum of min(c_e, cap) (table row 0, cumsum in row 1), the
+ * fixed segment L*cap (row 2, cumsum in row 3), CAPACITY if some S_r > rcap;
+ * slots: the i-th pair of expert e in flat order takes row e*cap + i while
+ * i < cap, later pairs are dropped (slot -1, DROPPED); packed_src holds the
+ * token of every kept row and -1 for the unused rows of each expert. */
+void oracle_capacity_plan(int64_t n, int k, int e_cnt, int ep, int64_t rcap,
+                          int64_t h, int64_t cap, const int32_t *ids,
+                          int32_t *counts, int32_t *offsets,
+                          int32_t *dest_counts, uint32_t *table,
+                          int32_t *slot, int32_t *packed_src,
+                          uint32_t *status) {
+  int l = e_cnt / ep;
+  uint32_t st = 0;
+  for (int x = 0; x < e_cnt; x++) counts[x] = 0;
+  for (int64_t t = 0; t < n; t++) {
+    for (int j = 0; j < k; j++) {
+      int32_t e = ids[t * k + j];
+      if (e == -1) continue;
+      if (e < -1 || e >= e_cnt) {
+        st |= ORC_BAD_ID;
+        continue;
+      }
+      for (int jj = 0; jj < j; jj++)
+        if (ids[t * k + jj] == e) st |= ORC_DUP_ID;
+      counts[e] += 1;
+    }
+  }
+  for (int x = 0; x <= e_cnt; x++) offsets[x] = (int32_t)(x * cap);
+  uint32_t send_disp = 0, seg_disp = 0;
+  for (int r = 0; r < ep; r++) {
+    int64_t kept = 0;
+    for (int x = r * l; x < (r + 1) * l; x++) kept += counts[x] < cap ? counts[x] : cap;
+    int64_t seg = (int64_t)l * cap;
+    dest_counts[r] = (int32_t)kept;
+    if (kept > rcap) st |= ORC_CAPACITY;
+    table[0 * ep + r] = (uint32_t)(kept * h);
+    table[1 * ep + r] = send_disp;
+    table[2 * ep + r] = (uint32_t)(seg * h);
+    table[3 * ep + r] = seg_disp;
+    send_disp += (uint32_t)(kept * h);
+    seg_disp += (uint32_t)(seg * h);
+  }
+  for (int64_t r = 0; r < (int64_t)e_cnt * cap; r++) packed_src[r] = -1;
+  for (int64_t t = 0; t < n; t++)
+    for (int j = 0; j < k; j++) slot[t * k + j] = -1;
+  for (int x = 0; x < e_cnt; x++) {
+    int64_t next = 0;
+    for (int64_t t = 0; t < n; t++) {
+      for (int j = 0; j < k; j++) {
+        if (ids[t * k + j] != x) continue;
+        if (next < cap) {
+          slot[t * k + j] = (int32_t)(x * cap + next);
+          packed_src[x * cap + next] = (int32_t)t;
+        } else {
+          st |= ORC_DROPPED;
+        }
+        next++;
       }
     }
   }
