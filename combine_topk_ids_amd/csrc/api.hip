@@ -1,5 +1,6 @@
 // api.hip -- the C ABI of libmoe: argument checks, sizes, and launches.
 // Declarations, argument meaning, layouts and error behaviour: include/moe.h.
+#include <math.h>
 #include <stdint.h>
 
 #include "moe.h"
@@ -9,9 +10,7 @@ namespace {
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-int64_t max_rows_unchecked(const moe_problem &p) {
-  return p.n_tokens * p.top_k + static_cast<int64_t>(p.n_experts) * (p.pad_multiple - 1);
-}
+int64_t max_rows_unchecked(const moe_problem &p) { return moe::max_rows(p); }
 
 int check(const moe_problem *p) {
   if (!p) return MOE_EINVAL;
@@ -20,6 +19,8 @@ int check(const moe_problem *p) {
   if (p->top_k < 1 || p->top_k > p->n_experts || p->top_k > moe::kMaxTopK) return MOE_EINVAL;
   if (p->ep < 1 || p->n_experts % p->ep != 0) return MOE_EINVAL;
   if (p->pad_multiple < 1 || p->recv_capacity < 0) return MOE_EINVAL;
+  if (p->expert_capacity < 0 || (p->expert_capacity > 0 && p->pad_multiple != 1)) return MOE_EINVAL;
+  if (p->expert_capacity > INT32_MAX) return MOE_EOVERFLOW;
   if (p->flags & ~MOE_FLAG_ZERO_TAIL) return MOE_EINVAL;
   switch (p->fmt) {
     case MOE_FMT_BF16: break;
@@ -31,6 +32,11 @@ int check(const moe_problem *p) {
   if (p->n_tokens > INT32_MAX / p->top_k) return MOE_EOVERFLOW;
   const int64_t r_max = max_rows_unchecked(*p);
   if (r_max > INT32_MAX) return MOE_EOVERFLOW;
+  // with a fixed capacity the plan forms e*cap + (rank in expert) and
+  // e*cap + 2*cap in int32
+  if (p->expert_capacity > 0 &&
+      r_max + p->expert_capacity + p->n_tokens * p->top_k > INT32_MAX)
+    return MOE_EOVERFLOW;
   if (r_max * static_cast<int64_t>(p->hidden) >= (int64_t{1} << 32)) return MOE_EOVERFLOW;
   if (p->n_tokens * static_cast<int64_t>(p->hidden) >= (int64_t{1} << 40)) return MOE_EOVERFLOW;
   // one wave per (token, column slab of >= 512 values) must index within int
@@ -42,7 +48,7 @@ int check(const moe_problem *p) {
 int check_exchange(const moe_problem *p) {
   const int rc = check(p);
   if (rc != MOE_OK) return rc;
-  if (p->pad_multiple != 1) return MOE_EINVAL;
+  if (p->pad_multiple != 1 || p->expert_capacity != 0) return MOE_EINVAL;
   const int64_t ranks = p->ep;
   const int64_t tokens = p->n_tokens * ranks;  // < 2^31 * 1024: no overflow
   // global pair and token indices, receive rows: int32; table: uint32 elements
@@ -65,6 +71,15 @@ MOE_API int moe_check_problem(const moe_problem *p) { return check(p); }
 MOE_API int64_t moe_max_rows(const moe_problem *p) {
   const int rc = check(p);
   return rc != MOE_OK ? rc : max_rows_unchecked(*p);
+}
+
+MOE_API int64_t moe_expert_capacity(int64_t n_tokens, int32_t top_k, int32_t n_experts,
+                                    double capacity_factor) {
+  if (n_tokens < 0 || top_k < 1 || n_experts < 1 || !(capacity_factor >= 0.0)) return MOE_EINVAL;
+  const double cap = ceil(capacity_factor * static_cast<double>(n_tokens) * static_cast<double>(top_k) /
+                          static_cast<double>(n_experts));
+  if (cap > static_cast<double>(INT32_MAX)) return MOE_EOVERFLOW;
+  return static_cast<int64_t>(cap);
 }
 
 MOE_API int64_t moe_payload_row_bytes(const moe_problem *p) {

@@ -493,11 +493,13 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(DispatchArgs g) {
     const int e = q / g.pad_groups;
     if (e >= g.e) return;
     const int grp = q - e * g.pad_groups;
-    const int lo = g.offsets[e] + g.counts[e];
-    const int hi = g.offsets[e + 1];
-    const int r0 = lo + grp * kPadRowsPerWave;
-    const int r1 = min(r0 + kPadRowsPerWave, hi);
-    for (int r = r0; r < r1; ++r) zero_row<NT>(g, r);
+    // unused rows [offsets[e] + counts[e], offsets[e+1]); with a fixed
+    // capacity counts[e] may exceed the expert's rows (int64: no overflow)
+    const int64_t hi = g.offsets[e + 1];
+    const int64_t lo = min(static_cast<int64_t>(g.offsets[e]) + g.counts[e], hi);
+    const int64_t r0 = lo + static_cast<int64_t>(grp) * kPadRowsPerWave;
+    const int64_t r1 = min(r0 + kPadRowsPerWave, hi);
+    for (int64_t r = r0; r < r1; ++r) zero_row<NT>(g, r);
     return;
   }
   blk -= g.pad_blocks;
@@ -562,8 +564,11 @@ hipError_t launch_dispatch(const moe_problem &p, const moe_plan &plan, const uin
   g.w = gates;
   g.counts = plan.expert_counts;
   g.offsets = plan.expert_offsets;
-  g.r_max = p.n_tokens * p.top_k + static_cast<int64_t>(p.n_experts) * (p.pad_multiple - 1);
-  const int pad_groups = (p.pad_multiple - 1 + kPadRowsPerWave - 1) / kPadRowsPerWave;
+  g.r_max = max_rows(p);
+  // unused rows per expert: fewer than A with padding, up to cap with a fixed
+  // capacity (rows [offsets[e] + counts[e], offsets[e+1]) either way)
+  const int64_t pad_span = p.expert_capacity > 0 ? p.expert_capacity : p.pad_multiple - 1;
+  const int pad_groups = static_cast<int>((pad_span + kPadRowsPerWave - 1) / kPadRowsPerWave);
   g.pad_blocks = pad_groups == 0 ? 0 : (p.n_experts * pad_groups + kWaves - 1) / kWaves;
   if (pad_groups > 0) g.pad_groups = pad_groups;
   g.seg_used = plan.expert_offsets + p.n_experts;  // R_used

@@ -192,6 +192,7 @@ moe_problem rank_problem(const moe_problem &p) {
   q.pad_multiple = 1;
   q.recv_capacity = INT64_MAX;  // capacity applies to receive buffers only
   q.flags = 0;
+  q.expert_capacity = 0;
   return q;
 }
 

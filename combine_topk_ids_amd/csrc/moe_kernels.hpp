@@ -11,6 +11,12 @@ namespace moe {
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 64;
 constexpr int kPlanThreads = 512;          // 8 waves per plan block
+
+// Rows of the packed buffer: N*k + E*(A-1), or E*cap with a fixed capacity.
+inline int64_t max_rows(const moe_problem &p) {
+  if (p.expert_capacity > 0) return static_cast<int64_t>(p.n_experts) * p.expert_capacity;
+  return p.n_tokens * p.top_k + static_cast<int64_t>(p.n_experts) * (p.pad_multiple - 1);
+}
 constexpr int kPlanWaves = kPlanThreads / 64;
 
 // How the (token, k) pairs are split into tiles for the plan kernels.

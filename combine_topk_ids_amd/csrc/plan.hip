@@ -62,6 +62,7 @@ struct PlanArgs {
   int64_t cap;
   uint32_t h;
   int k, e, ep, a;
+  int ecap;           // fixed capacity per expert (0: dropless, padded to A)
   int tile_tokens;    // tokens per count tile
   int ntiles;         // count tiles
   int subs;           // sub-tiles per count tile
@@ -102,7 +103,8 @@ __device__ __forceinline__ void select_rank(PlanArgs &g) {
 __device__ __forceinline__ int padded(int c, int a) { return ((c + a - 1) / a) * a; }
 
 __device__ __forceinline__ uint32_t wave_or_bits(uint32_t v) {
-  return (ballot(v & 1u) ? 1u : 0u) | (ballot(v & 2u) ? 2u : 0u) | (ballot(v & 4u) ? 4u : 0u);
+  return (ballot(v & 1u) ? 1u : 0u) | (ballot(v & 2u) ? 2u : 0u) | (ballot(v & 4u) ? 4u : 0u) |
+         (ballot(v & MOE_STATUS_DROPPED) ? MOE_STATUS_DROPPED : 0u);
 }
 
 struct Tile {
@@ -326,9 +328,17 @@ __global__ __launch_bounds__(kThreads) void plan_assign_kernel(PlanArgs g) {
   // thread tid owns experts 2*tid and 2*tid+1 (E <= 1024 = 2 * kThreads)
   {
     const int e0 = 2 * tid;
-    const int c0 = e0 < E ? s_tot[e0] : 0;
-    const int c1 = e0 + 1 < E ? s_tot[e0 + 1] : 0;
-    const int p0 = padded(c0, g.a), p1 = padded(c1, g.a);
+    // segment sizes: c padded to A, or the fixed capacity; with a fixed
+    // capacity the unpadded sums count kept pairs, min(c, cap)
+    int c0 = e0 < E ? s_tot[e0] : 0;
+    int c1 = e0 + 1 < E ? s_tot[e0 + 1] : 0;
+    int p0 = padded(c0, g.a), p1 = padded(c1, g.a);
+    if (g.ecap > 0) {
+      c0 = min(c0, g.ecap);
+      c1 = min(c1, g.ecap);
+      p0 = e0 < E ? g.ecap : 0;
+      p1 = e0 + 1 < E ? g.ecap : 0;
+    }
     const int ip = wave_incl_scan(p0 + p1), ic = wave_incl_scan(c0 + c1);
     if (lane == kWave - 1) {
       s_scan[0][wave] = ip;
@@ -377,6 +387,9 @@ __global__ __launch_bounds__(kThreads) void plan_assign_kernel(PlanArgs g) {
   uint32_t cap = 0;
   for (int r = tid; r < g.ep; r += kThreads)
     if (s_cpre[(r + 1) * L] - s_cpre[r * L] > g.cap) cap = MOE_STATUS_CAPACITY;
+  if (g.ecap > 0)
+    for (int e = tid; e < E; e += kThreads)
+      if (s_tot[e] > g.ecap) cap |= MOE_STATUS_DROPPED;
   cap = wave_or_bits(cap);
   if (lane == 0 && cap) atomicOr(&s_fl, cap);
   // rank among the equal IDs of this chunk: one ballot per ID bit, a lane
@@ -395,7 +408,9 @@ __global__ __launch_bounds__(kThreads) void plan_assign_kernel(PlanArgs g) {
     int sl = -1;
     if (valid) {
       sl = cur[ev] + rank;
-      g.packed_src[sl] = static_cast<int32_t>(t.tok0 + i_loc / k);
+      // a fixed capacity keeps the first cap pairs of each expert
+      if (g.ecap > 0 && sl - s_off[ev] >= g.ecap) sl = -1;
+      if (sl >= 0) g.packed_src[sl] = static_cast<int32_t>(t.tok0 + i_loc / k);
     }
     g.slot[t.pair0 + i_loc] = sl;
   }
@@ -422,14 +437,16 @@ __global__ __launch_bounds__(kThreads) void plan_assign_kernel(PlanArgs g) {
     }
   }
 
-  // packed_src = -1 on pad rows (an expert has at most A-1 of them: the grid
-  // strides over all E*(A-1) candidates) and on the tail rows
-  if (g.a > 1) {
-    const int per = g.a - 1;
-    const int cand = E * per;
+  // packed_src = -1 on the unused rows of each expert (at most A-1 pad rows,
+  // or up to cap with a fixed capacity: the grid strides over E * that many
+  // candidates) and on the tail rows
+  const int per = g.ecap > 0 ? g.ecap : g.a - 1;
+  if (per > 0) {
+    const int cand = E * per;  // <= R_max < 2^31
     for (int q = b * kThreads + tid; q < cand; q += g.nblocks * kThreads) {
       const int e = q / per;
-      const int r = s_off[e] + s_tot[e] + (q - e * per);
+      const int used = g.ecap > 0 ? min(s_tot[e], g.ecap) : s_tot[e];
+      const int r = s_off[e] + used + (q - e * per);
       if (r < s_off[e + 1]) g.packed_src[r] = -1;
     }
   }
@@ -485,8 +502,9 @@ hipError_t launch_plan_ranks(const moe_problem &p, int ranks, const int32_t *ids
   g.ids = ids;
   g.n = p.n_tokens;
   g.npairs = geo.npairs;
-  g.r_max = p.n_tokens * p.top_k + static_cast<int64_t>(p.n_experts) * (p.pad_multiple - 1);
+  g.r_max = max_rows(p);
   g.cap = p.recv_capacity;
+  g.ecap = static_cast<int>(p.expert_capacity);
   g.h = static_cast<uint32_t>(p.hidden);
   g.k = p.top_k;
   g.e = p.n_experts;

@@ -20,12 +20,12 @@ import torch  # first: libmoe then binds to the HIP runtime torch has loaded
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 
 MOE_OK, MOE_EINVAL, MOE_EALIGN, MOE_EOVERFLOW, MOE_EHIP = 0, -1, -2, -3, -4
-STATUS_BAD_ID, STATUS_DUP_ID, STATUS_CAPACITY, STATUS_MAP_OVERFLOW = 1, 2, 4, 8
+STATUS_BAD_ID, STATUS_DUP_ID, STATUS_CAPACITY, STATUS_MAP_OVERFLOW, STATUS_DROPPED = 1, 2, 4, 8, 16
 FMT = {"bf16": 0, "fp8": 1, "mxfp4": 2}
 FLAG_ZERO_TAIL = 1
 
 # every symbol include/moe.h declares
-EXPORTS = ("moe_check_problem", "moe_max_rows", "moe_payload_row_bytes",
+EXPORTS = ("moe_check_problem", "moe_max_rows", "moe_expert_capacity", "moe_payload_row_bytes",
            "moe_scale_row_bytes", "moe_workspace_bytes", "moe_dispatch_plan",
            "moe_dispatch", "moe_dispatch_gated", "moe_combine", "moe_check_exchange",
            "moe_exchange_workspace_bytes", "moe_exchange_plan", "moe_exchange_dispatch",
@@ -44,7 +44,7 @@ class Problem(ctypes.Structure):
                 ("top_k", ctypes.c_int32), ("n_experts", ctypes.c_int32),
                 ("ep", ctypes.c_int32), ("recv_capacity", ctypes.c_int64),
                 ("pad_multiple", ctypes.c_int32), ("fmt", ctypes.c_int32),
-                ("flags", ctypes.c_uint32)]
+                ("flags", ctypes.c_uint32), ("expert_capacity", ctypes.c_int64)]
 
 
 class Plan(ctypes.Structure):
@@ -69,6 +69,8 @@ def _load() -> ctypes.CDLL:
     sig = {
         "moe_check_problem": (ctypes.c_int, [P]),
         "moe_max_rows": (ctypes.c_int64, [P]),
+        "moe_expert_capacity": (ctypes.c_int64, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                                 ctypes.c_double]),
         "moe_payload_row_bytes": (ctypes.c_int64, [P]),
         "moe_scale_row_bytes": (ctypes.c_int64, [P]),
         "moe_workspace_bytes": (ctypes.c_size_t, [P]),
@@ -101,12 +103,19 @@ def strerror(code: int) -> str:
 
 def problem(n_tokens: int, hidden: int, top_k: int, n_experts: int, ep: int,
             recv_capacity: int | None = None, pad_multiple: int = 1,
-            fmt: str = "bf16", zero_tail: bool = False) -> Problem:
-    """Build a moe_problem; recv_capacity None means the dropless bound."""
+            fmt: str = "bf16", zero_tail: bool = False, expert_capacity: int = 0) -> Problem:
+    """Build a moe_problem; recv_capacity None means the dropless bound;
+    expert_capacity > 0 selects the fixed-capacity [E][cap] layout."""
     if recv_capacity is None:
         recv_capacity = n_tokens * min(top_k, n_experts // max(ep, 1))
     return Problem(n_tokens, hidden, top_k, n_experts, ep, recv_capacity,
-                   pad_multiple, FMT[fmt], FLAG_ZERO_TAIL if zero_tail else 0)
+                   pad_multiple, FMT[fmt], FLAG_ZERO_TAIL if zero_tail else 0, expert_capacity)
+
+
+def moe_expert_capacity(n_tokens: int, top_k: int, n_experts: int, capacity_factor: float) -> int:
+    """ceil(capacity_factor * N * k / E)."""
+    return _checked(lib.moe_expert_capacity(n_tokens, top_k, n_experts, float(capacity_factor)),
+                    "moe_expert_capacity")
 
 
 def _checked(value: int, where: str) -> int:
@@ -142,7 +151,7 @@ def _sizes(p: Problem):
     """(R_max, payload row bytes, scale row bytes, workspace bytes), cached per
     problem value (the C library stays the source of these numbers)."""
     key = (p.n_tokens, p.hidden, p.top_k, p.n_experts, p.ep, p.recv_capacity,
-           p.pad_multiple, p.fmt, p.flags)
+           p.pad_multiple, p.fmt, p.flags, p.expert_capacity)
     v = _SIZES.get(key)
     if v is None:
         v = (moe_max_rows(p), moe_payload_row_bytes(p), moe_scale_row_bytes(p),

@@ -45,6 +45,7 @@ class Workload:
     experts: str      # "identity" (expert output = dispatched rows) | "random"
     recv_capacity: int | None = None  # None: dropless (all tokens) * min(k, E/EP)
     ranks: int = 1    # simulated source ranks, N tokens each (exchange workloads: EP)
+    capacity_factor: float | None = None  # fixed per-expert capacity from this factor
 
     @property
     def l(self) -> int:
@@ -68,6 +69,8 @@ class Workload:
     def describe(self) -> str:
         head = f"{self.ranks} ranks x " if self.exchange else ""
         tail = f", C={self.capacity} rows per receive buffer" if self.exchange else ""
+        if self.capacity_factor is not None:
+            tail += f", expert capacity factor {self.capacity_factor}"
         return (f"{head}N={self.n} H={self.h} E={self.e} k={self.k} EP={self.ep} "
                 f"A={self.a} {self.fmt} {self.routing} routing, "
                 f"{self.experts} experts{tail}")
@@ -92,6 +95,12 @@ WORKLOADS = {
         # decode-sized MX-FP4 dispatch
         Workload("decode_mxfp4_n128", n=128, h=7168, e=256, k=8, ep=8, a=1,
                  fmt="mxfp4", routing="softmax", experts="random"),
+        # fixed per-expert capacity (factor 1.0: experts above the mean drop)
+        Workload("capacity_bf16_n4096", n=4096, h=4096, e=64, k=6, ep=8, a=1,
+                 fmt="bf16", routing="softmax", experts="identity",
+                 capacity_factor=1.0),
+        Workload("capacity_fp8_n8192", n=8192, h=7168, e=256, k=8, ep=32, a=1,
+                 fmt="fp8", routing="softmax", experts="random", capacity_factor=1.25),
         # exchange across 8 simulated ranks of the uniform prefill share;
         # receive buffers of 1.25 * N * k rows (the mean receive is N * k)
         Workload("exchange_bf16_ep8_n4096", n=4096, h=4096, e=64, k=6, ep=8,

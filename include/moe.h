@@ -75,6 +75,9 @@ extern "C" {
 /* (status of moe_routing_map_to_topk) a token routes to more than k experts:
  * its first k, in expert order, are kept */
 #define MOE_STATUS_MAP_OVERFLOW 8u
+/* (fixed expert capacity) some expert was routed more pairs than its
+ * capacity: the later ones were dropped */
+#define MOE_STATUS_DROPPED 16u
 
 /* ---- payload formats ---------------------------------------------------- */
 typedef enum moe_fmt {
@@ -114,14 +117,28 @@ typedef struct moe_problem {
                             a multiple of A with zero rows                   */
   int32_t fmt;           /* a moe_fmt value                                  */
   uint32_t flags;        /* MOE_FLAG_*                                       */
+  int64_t expert_capacity; /* 0: dropless (the layout above).  cap > 0: fixed
+                            capacity -- expert e owns rows e*cap .. e*cap+cap-1
+                            of an [E][cap] buffer (R_max = E*cap); its first
+                            cap pairs in flat order are kept, later ones get
+                            slot -1 (combine skips them) and set
+                            MOE_STATUS_DROPPED; unused rows are zero rows;
+                            needs pad_multiple == 1.  (NeMo Automodel
+                            token_dispatcher API, TokenDispatcherConfig.
+                            moe_expert_capacity_factor; DeepSpeed v0.19.4
+                            function index, page 15, the dispatch entry's
+                            [e, c, m] buffer.)  See moe_expert_capacity.   */
 } moe_problem;
 
 /* ---- routing plan (device pointers; written by moe_dispatch_plan) ------- */
 typedef struct moe_plan {
   int32_t *expert_counts;  /* [E]   c_e: valid (token, k) pairs of expert e   */
   int32_t *expert_offsets; /* [E+1] exclusive cumsum of A*ceil(c_e/A);
-                                    [E] = R_used rows in use                 */
-  int32_t *dest_counts;    /* [EP]  S_r = sum of c_e over rank r's experts   */
+                                    [E] = R_used rows in use (fixed capacity:
+                                    e*cap)                                   */
+  int32_t *dest_counts;    /* [EP]  S_r = sum of c_e over rank r's experts
+                                    (fixed capacity: of the kept min(c_e, cap);
+                                    rows 2-3 of the table then hold L*cap)  */
   uint32_t *rank_table;    /* [4][EP] row-major, in elements (rows * H):
                               0 send counts S_r*H, 1 their exclusive cumsum,
                               2 padded segment sizes P_r*H, 3 their exclusive
@@ -141,9 +158,15 @@ typedef struct moe_plan {
  * points would return for it. */
 MOE_API int moe_check_problem(const moe_problem *p);
 
-/* R_max = N*k + E*(A-1): rows of the static packed buffer (always >= R_used).
- * Negative error code if the problem is invalid. */
+/* R_max = N*k + E*(A-1): rows of the static packed buffer (always >= R_used);
+ * E*cap with a fixed expert capacity.  Negative error code if the problem is
+ * invalid. */
 MOE_API int64_t moe_max_rows(const moe_problem *p);
+
+/* Capacity per expert for a capacity factor cf >= 0: ceil(cf * N * k / E),
+ * computed in double precision; negative error code for invalid sizes. */
+MOE_API int64_t moe_expert_capacity(int64_t n_tokens, int32_t top_k,
+                                    int32_t n_experts, double capacity_factor);
 
 /* Bytes of one payload row (2H, H or H/2) and of one scale row (0, 4*H/128
  * or H/32).  Negative error code if the problem is invalid. */

@@ -195,3 +195,26 @@ def test_gated_and_map_entry_points_check_arguments(moe):
     assert moe.lib.moe_routing_map_to_topk(ref(p), fake, fake + 2, fake, None, fake, fake, None) == -2
     assert moe.lib.moe_routing_map_to_topk(ref(p), fake, None, fake, None, fake, fake + 16, None) == -2
     assert moe.lib.moe_routing_map_to_topk(ref(bad), fake, None, fake, None, fake, fake, None) == -1
+
+
+# ---- fixed expert capacity ------------------------------------------------------
+
+def test_expert_capacity_sizes_and_checks(moe):
+    import oracle
+    for n, k, e, cf in [(4096, 6, 64, 1.25), (10, 3, 4, 0.5), (100, 1, 1, 0.0), (7, 2, 5, 2.0)]:
+        assert moe.moe_expert_capacity(n, k, e, cf) == oracle.expert_capacity(n, k, e, cf)
+    assert moe.lib.moe_expert_capacity(10, 0, 4, 1.0) == -1
+    assert moe.lib.moe_expert_capacity(10, 2, 4, -1.0) == -1
+    assert moe.lib.moe_expert_capacity(1 << 40, 64, 1, 1.0) == -3
+    p = moe.problem(4096, 4096, 6, 64, 8, expert_capacity=480)
+    assert moe.moe_check_problem(p) == 0
+    assert moe.moe_max_rows(p) == 64 * 480
+    # a fixed capacity replaces per-expert padding
+    assert moe.moe_check_problem(moe.problem(64, 256, 2, 8, 4, pad_multiple=2,
+                                             expert_capacity=8)) == -1
+    assert moe.moe_check_problem(moe.problem(64, 256, 2, 8, 4, expert_capacity=-1)) == -1
+    # E*cap + N*k must fit int32
+    assert moe.moe_check_problem(moe.problem(64, 8, 2, 1024, 4, expert_capacity=1 << 21)) == -3
+    # no fixed capacity in the exchange
+    assert moe.moe_check_exchange(moe.problem(64, 256, 2, 8, 4, recv_capacity=64,
+                                              expert_capacity=8)) == -1
