@@ -45,15 +45,21 @@ def row_bytes(fmt, h):
     return {"bf16": 2 * h, "fp8": h + 4 * (h // 128), "mxfp4": h // 2 + h // 32}[fmt]
 
 
-def step_bytes(w, r_used, r_max):
+def step_bytes(w, r_used, r_max, kept=None):
     """Algorithmic bytes of one step (each array read or written once).
 
     One buffer: r_used = R_used rows (live + pad), r_max = R_max.  Exchange:
     r_used = receive rows in use over all buffers, r_max = EP * C; the
-    dispatch writes every receive row (live rows, then zero rows)."""
+    dispatch writes every receive row (live rows, then zero rows).  Fixed
+    expert capacity: r_used = r_max = E * cap rows, all written; kept = pairs
+    kept, the rows the combine reads."""
     t = w.tokens
     nk = t * w.k
-    if w.exchange:
+    if kept is not None:
+        plan = 4 * nk + 4 * nk + 4 * r_max                       # ids, slot, packed_src
+        dispatch = 2 * t * w.h + r_max * row_bytes(w.fmt, w.h)   # read x once, write all rows
+        combine = 4 * nk + 4 * nk + 2 * w.h * kept + 2 * t * w.h  # slot, w, kept rows, out
+    elif w.exchange:
         plan = 4 * nk + 4 * nk + 4 * r_max                       # ids, recv_slot, recv_src
         dispatch = 2 * t * w.h + r_max * row_bytes(w.fmt, w.h)   # read x once, write all rows
         combine = 4 * nk + 4 * nk + 2 * w.h * r_used + 2 * t * w.h  # slot, w, kept rows, out
@@ -65,8 +71,11 @@ def step_bytes(w, r_used, r_max):
                 total=plan + dispatch + combine)
 
 
-def buffer_rows(w):
-    """Rows of the packed buffer (R_max) or of all receive buffers (EP * C)."""
+def buffer_rows(w, expert_cap=0):
+    """Rows of the packed buffer (R_max; E * cap with a fixed expert
+    capacity) or of all receive buffers (EP * C)."""
+    if expert_cap:
+        return w.e * expert_cap
     return w.ep * w.capacity if w.exchange else w.n * w.k + w.e * (w.a - 1)
 
 
@@ -88,10 +97,12 @@ def traffic_from_profile(workload, kernel):
 class Path:
     """Device buffers and the three calls of one step, for one workload."""
 
-    def __init__(self, moe, torch, w, inp, copies):
+    def __init__(self, moe, torch, w, inp, copies, expert_cap=0):
         self.moe, self.torch, self.w = moe, torch, w
         self.p = moe.problem(w.n, w.h, w.k, w.e, w.ep, recv_capacity=w.capacity,
-                             pad_multiple=w.a, fmt=w.fmt, zero_tail=False)
+                             pad_multiple=w.a, fmt=w.fmt, zero_tail=False,
+                             expert_capacity=expert_cap)
+        self.expert_cap = expert_cap
         self.r_max = moe.moe_max_rows(self.p)
         dev = "cuda"
         x = torch.from_numpy(inp["hidden"].view(np.int16)).to(dev).view(torch.bfloat16)
@@ -131,6 +142,10 @@ class Path:
 
     def r_used(self):
         return int(self.sets[0]["plan"].expert_offsets[-1].item())
+
+    def kept(self):
+        """Pairs kept by a fixed expert capacity (rows the combine reads)."""
+        return int(self.sets[0]["plan"].dest_counts.sum().item())
 
 
 class ExchangePath:
@@ -289,14 +304,20 @@ def cpu_baseline(w, inp, budget_s=10.0, pass_s=2.0):
     def one_pass(m):
         ids, wts, x = inp["ids"][:m], inp["weights"][:m], inp["hidden"][:m]
         t0 = time.process_time()
-        pl = oracle.plan(ids, w.e, w.ep, w.a, m * min(w.k, w.l), w.h)
+        kept = None
+        if w.capacity_factor is not None:
+            cap = oracle.expert_capacity(m, w.k, w.e, w.capacity_factor)
+            pl = oracle.capacity_plan(ids, w.e, w.ep, cap, m * min(w.k, w.l), w.h)
+            kept = int(pl["dest_counts"].sum())
+        else:
+            pl = oracle.plan(ids, w.e, w.ep, w.a, m * min(w.k, w.l), w.h)
         pay, _ = oracle.dispatch(w.fmt, x, pl, zero_tail=False)
         y = pay.view(np.uint16).reshape(pl["r_max"], -1) if "expert_out" not in inp \
             else inp["expert_out"]
         oracle.combine(pl["slot"], wts, y)
         dt = time.process_time() - t0
         sub = dataclasses.replace(w, n=m)
-        return dt, step_bytes(sub, pl["r_used"], pl["r_max"])["total"]
+        return dt, step_bytes(sub, pl["r_used"], pl["r_max"], kept)["total"]
 
     m = min(w.n, 64)
     dt, _ = one_pass(m)
@@ -382,12 +403,16 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     w = WORKLOADS[args.workload]
     log(f"[bench] workload {w.name}: {w.describe()}")
-    r_max = buffer_rows(w)
+    expert_cap = 0
+    if w.capacity_factor is not None:
+        expert_cap = moe.moe_expert_capacity(w.n, w.k, w.e, w.capacity_factor)
+    r_max = buffer_rows(w, expert_cap)
     inp = make_inputs(w, seed=0, expert_rows=r_max)
     set_bytes = (w.tokens * w.h * 2 * 2 + r_max * row_bytes(w.fmt, w.h)
                  + (r_max * w.h * 2 if "expert_out" in inp else 0))
     copies = args.copies or max(2, min(8, -(-(768 << 20) // max(set_bytes, 1)) + 1))
-    path = (ExchangePath if w.exchange else Path)(moe, torch, w, inp, copies)
+    path = ExchangePath(moe, torch, w, inp, copies) if w.exchange else \
+        Path(moe, torch, w, inp, copies, expert_cap)
     log(f"[bench] {copies} buffer sets of {set_bytes / 1e6:.1f} MB rotated")
 
     ms, wall = time_steps(torch, path, args.steps, args.warmup)
@@ -396,7 +421,7 @@ def main():
     log(f"[bench] per-kernel means (us): plan {kt['plan'] * 1e3:.2f} dispatch "
         f"{kt['dispatch'] * 1e3:.2f} combine {kt['combine'] * 1e3:.2f}")
     ru = path.r_used()
-    b = step_bytes(w, ru, r_max)
+    b = step_bytes(w, ru, r_max, path.kept() if expert_cap else None)
     value = b["total"] / (ms * 1e-3) / 1e9
 
     dom = "dispatch" if kt["dispatch"] >= kt["combine"] else "combine"
@@ -430,6 +455,9 @@ def main():
     if w.exchange:
         config.update(source_ranks=w.ranks, recv_capacity=w.capacity,
                       path="exchange: source-major receive buffers of C rows per rank")
+    if expert_cap:
+        config.update(capacity_factor=w.capacity_factor, expert_capacity=expert_cap,
+                      pairs_kept=path.kept(), path="fixed expert capacity, later pairs dropped")
     rec = {
         "metric": METRIC,
         "value": round(value, 1),
