@@ -59,6 +59,10 @@ def _load():
         lib.oracle_expert_capacity.argtypes = [i64, i32, i32, ctypes.c_double]
         lib.oracle_capacity_plan.restype = None
         lib.oracle_capacity_plan.argtypes = [i64, i32, i32, i32, i64, i64, i64] + [p] * 8
+        lib.oracle_encode_row_nvfp4.restype = None
+        lib.oracle_encode_row_nvfp4.argtypes = [i64, p, ctypes.c_float, p, p]
+        lib.oracle_dispatch_nvfp4.restype = None
+        lib.oracle_dispatch_nvfp4.argtypes = [i64, i64, i64, p, p, ctypes.c_float, p, p, i32]
         lib.oracle_exchange_plan.restype = None
         lib.oracle_exchange_plan.argtypes = [i64, i32, i32, i32, i64, i64] + [p] * 9
         lib.oracle_encode_row.restype = None
@@ -293,6 +297,33 @@ def routing_map_to_topk(routing_map: np.ndarray, probs: np.ndarray | None, k: in
     _load().oracle_routing_map_to_topk(n, e, k, _ptr(m), None if pr is None else _ptr(pr),
                                        _ptr(ids), _ptr(w), _ptr(st))
     return ids, w, int(st[0])
+
+
+def encode_rows_nvfp4(x: np.ndarray, gs: float):
+    """NVFP4 rows of bf16 ``x [M, H]`` with global encode scale ``gs``:
+    (payload uint8 [M, H/2], scales uint8 [M, H/16] of E4M3 codes)."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    m, h = x.shape
+    pay = np.zeros((m, h // 2), np.uint8)
+    sc = np.zeros((m, h // 16), np.uint8)
+    lib = _load()
+    for i in range(m):
+        lib.oracle_encode_row_nvfp4(h, ctypes.c_void_p(x[i].ctypes.data), float(gs),
+                                    ctypes.c_void_p(pay[i].ctypes.data),
+                                    ctypes.c_void_p(sc[i].ctypes.data))
+    return pay, sc
+
+
+def dispatch_nvfp4(x: np.ndarray, pl: dict, gs: float, zero_tail: bool = True):
+    """Gather-form NVFP4 dispatch over the plan's packed rows."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    h = x.shape[1]
+    r_max = pl["r_max"]
+    pay = np.zeros((r_max, h // 2), np.uint8)
+    sc = np.zeros((r_max, h // 16), np.uint8)
+    _load().oracle_dispatch_nvfp4(h, r_max, pl["r_used"], _ptr(np.ascontiguousarray(pl["packed_src"])),
+                                  _ptr(x), float(gs), _ptr(pay), _ptr(sc), int(zero_tail))
+    return pay, sc
 
 
 def combine(slot: np.ndarray, w: np.ndarray | None, y: np.ndarray) -> np.ndarray:

@@ -78,6 +78,18 @@
  *             then sums the expert rows without weights.
  *             - DeepSpeed v0.19.4 function index, page 15: pre-multiplying
  *               token representations by router scores before expert compute.
+ *   NVFP4     E2M1 codes with one E4M3 scale per 16 values and one fp32
+ *             global encode scale gs given by the caller: per block, the
+ *             scale code sf = E4M3(fl32(fl32(amax / 6) * gs)) (saturating),
+ *             and each code E2M1(fl32(fl32(x * gs) / value(sf))); a block
+ *             whose scale is 0 has zero codes.  Decoding: q * value(sf) / gs.
+ *             - Mojo ep.dispatch_async.block.scaled.nv struct: execute
+ *               (tokens transferred in NVFP4; input_scales, the global
+ *               input scales for NVFP4 quantization).
+ *             - Mojo shmem ep_comm module: NVBlockScaledTokenFormat
+ *               (block-scaled FP4), input_scales_wrapper_type.
+ *             - The published NVFP4 format: E2M1 elements, 16-value blocks
+ *               with E4M3 scales, one fp32 per-tensor scale.
  *   combine   out[t] = bf16(sum_j w[t,j] * Y[slot[t,j]]) accumulated in fp32
  *             in j order, one fused multiply-add per term.
  *             - DeepSpeed v0.19.4 function index, page 15: the combine entry
@@ -541,6 +553,51 @@ void oracle_encode_row(int fmt, int64_t h, const uint16_t *x, void *payload,
   for (int64_t i = 0; i < h; i++) v[i] = oracle_bf16_to_f32(x[i]);
   oracle_encode_row_f32(fmt, h, v, payload, scales);
   free(v);
+}
+
+/* NVFP4 row: h/2 payload bytes (element 2m in the low nibble of byte m) and
+ * h/16 E4M3 scale bytes, with global encode scale gs. */
+void oracle_encode_row_nvfp4(int64_t h, const uint16_t *x, float gs,
+                             uint8_t *payload, uint8_t *scales) {
+  for (int64_t b = 0; b < h / 16; b++) {
+    float amax = 0.0f;
+    for (int i = 0; i < 16; i++) {
+      float a = fabsf(oracle_bf16_to_f32(x[b * 16 + i]));
+      if (a > amax) amax = a;
+    }
+    float d = amax / 6.0f;            /* ideal decode scale of the block */
+    uint8_t sf = oracle_e4m3_encode(d * gs);
+    double sv = oracle_e4m3_value(sf & 0x7F);
+    scales[b] = sf;
+    if (sv == 0.0) {
+      for (int i = 0; i < 8; i++) payload[b * 8 + i] = 0;
+      continue;
+    }
+    float sfv = (float)sv;            /* exact: every E4M3 value is an fp32 */
+    for (int i = 0; i < 8; i++) {
+      float v0 = (oracle_bf16_to_f32(x[b * 16 + 2 * i]) * gs) / sfv;
+      float v1 = (oracle_bf16_to_f32(x[b * 16 + 2 * i + 1]) * gs) / sfv;
+      payload[b * 8 + i] =
+          (uint8_t)(oracle_e2m1_encode(v0) | (oracle_e2m1_encode(v1) << 4));
+    }
+  }
+}
+
+/* Gather-form dispatch in NVFP4 (as oracle_dispatch). */
+void oracle_dispatch_nvfp4(int64_t h, int64_t r_max, int64_t r_used,
+                           const int32_t *packed_src, const uint16_t *x, float gs,
+                           uint8_t *payload, uint8_t *scales, int zero_tail) {
+  int64_t pb = h / 2, sb = h / 16;
+  for (int64_t r = 0; r < r_max; r++) {
+    if (r >= r_used && !zero_tail) continue;
+    int32_t t = r < r_used ? packed_src[r] : -1;
+    if (t < 0) {
+      memset(payload + r * pb, 0, (size_t)pb);
+      memset(scales + r * sb, 0, (size_t)sb);
+    } else {
+      oracle_encode_row_nvfp4(h, x + (int64_t)t * h, gs, payload + r * pb, scales + r * sb);
+    }
+  }
 }
 
 static int64_t payload_row_bytes(int fmt, int64_t h) {
