@@ -26,6 +26,7 @@ int check(const moe_problem *p) {
     case MOE_FMT_BF16: break;
     case MOE_FMT_FP8_E4M3_B128: if (p->hidden % 128 != 0) return MOE_EINVAL; break;
     case MOE_FMT_MXFP4_B32: if (p->hidden % 32 != 0) return MOE_EINVAL; break;
+    case MOE_FMT_NVFP4_B16: if (p->hidden % 32 != 0) return MOE_EINVAL; break;
     default: return MOE_EINVAL;
   }
   // pair indices, rows and token*H offsets are int32 / uint32 on the device
@@ -87,6 +88,7 @@ MOE_API int64_t moe_payload_row_bytes(const moe_problem *p) {
   if (rc != MOE_OK) return rc;
   if (p->fmt == MOE_FMT_BF16) return 2 * static_cast<int64_t>(p->hidden);
   if (p->fmt == MOE_FMT_FP8_E4M3_B128) return p->hidden;
+  if (p->fmt == MOE_FMT_NVFP4_B16) return p->hidden / 2;
   return p->hidden / 2;
 }
 
@@ -95,6 +97,7 @@ MOE_API int64_t moe_scale_row_bytes(const moe_problem *p) {
   if (rc != MOE_OK) return rc;
   if (p->fmt == MOE_FMT_BF16) return 0;
   if (p->fmt == MOE_FMT_FP8_E4M3_B128) return 4 * static_cast<int64_t>(p->hidden / 128);
+  if (p->fmt == MOE_FMT_NVFP4_B16) return p->hidden / 16;
   return p->hidden / 32;
 }
 
@@ -134,7 +137,23 @@ MOE_API int moe_dispatch(const moe_problem *p, const moe_plan *plan, const uint1
       !aligned(plan->expert_counts, 4) || !aligned(plan->expert_offsets, 4) ||
       (p->fmt == MOE_FMT_FP8_E4M3_B128 && !aligned(scales, 4)))
     return MOE_EALIGN;
-  return launched(moe::launch_dispatch(*p, *plan, hidden, nullptr, payload, scales,
+  if (p->fmt == MOE_FMT_NVFP4_B16) return MOE_EINVAL;  // needs its global scale: moe_dispatch_scaled
+  return launched(moe::launch_dispatch(*p, *plan, hidden, nullptr, nullptr, payload, scales,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+MOE_API int moe_dispatch_scaled(const moe_problem *p, const moe_plan *plan, const uint16_t *hidden,
+                                const float *input_scale, void *payload, void *scales, void *stream) {
+  const int rc = check(p);
+  if (rc != MOE_OK) return rc;
+  if (p->fmt != MOE_FMT_NVFP4_B16 || !input_scale) return MOE_EINVAL;
+  if (!plan || !plan->expert_counts || !plan->expert_offsets) return MOE_EINVAL;
+  if (p->n_tokens > 0 && (!hidden || !plan->slot)) return MOE_EINVAL;
+  if (max_rows_unchecked(*p) > 0 && (!payload || !scales)) return MOE_EINVAL;
+  if (!aligned(hidden, 16) || !aligned(payload, 16) || !aligned(plan->slot, 4) || !aligned(input_scale, 4) ||
+      !aligned(plan->expert_counts, 4) || !aligned(plan->expert_offsets, 4))
+    return MOE_EALIGN;
+  return launched(moe::launch_dispatch(*p, *plan, hidden, nullptr, input_scale, payload, scales,
                                        static_cast<hipStream_t>(stream)));
 }
 
@@ -152,8 +171,10 @@ MOE_API int moe_dispatch_gated(const moe_problem *p, const moe_plan *plan, const
       (p->fmt == MOE_FMT_FP8_E4M3_B128 && !aligned(scales, 4)))
     return MOE_EALIGN;
   // a null weight pointer selects the ungated kernels: keep the gated call gated
+  if (p->fmt == MOE_FMT_NVFP4_B16) return MOE_EINVAL;
   const float *w = p->n_tokens > 0 ? topk_weights : nullptr;
-  return launched(moe::launch_dispatch(*p, *plan, hidden, w, payload, scales, static_cast<hipStream_t>(stream)));
+  return launched(moe::launch_dispatch(*p, *plan, hidden, w, nullptr, payload, scales,
+                                       static_cast<hipStream_t>(stream)));
 }
 
 MOE_API int moe_combine(const moe_problem *p, const moe_plan *plan, const uint16_t *expert_out,
@@ -204,8 +225,25 @@ MOE_API int moe_exchange_dispatch(const moe_problem *p, const moe_exchange *x, c
   if (!aligned(hidden, 16) || !aligned(recv_payload, 16) || !aligned(x->recv_slot, 4) ||
       !aligned(x->recv_rows, 4) || (p->fmt == MOE_FMT_FP8_E4M3_B128 && !aligned(recv_scales, 4)))
     return MOE_EALIGN;
-  return launched(moe::launch_exchange_dispatch(*p, *x, hidden, nullptr, recv_payload, recv_scales,
+  if (p->fmt == MOE_FMT_NVFP4_B16) return MOE_EINVAL;  // moe_exchange_dispatch_scaled
+  return launched(moe::launch_exchange_dispatch(*p, *x, hidden, nullptr, nullptr, recv_payload, recv_scales,
                                                 static_cast<hipStream_t>(stream)));
+}
+
+MOE_API int moe_exchange_dispatch_scaled(const moe_problem *p, const moe_exchange *x, const uint16_t *hidden,
+                                         const float *input_scale, void *recv_payload, void *recv_scales,
+                                         void *stream) {
+  const int rc = check_exchange(p);
+  if (rc != MOE_OK) return rc;
+  if (p->fmt != MOE_FMT_NVFP4_B16 || !input_scale) return MOE_EINVAL;
+  if (!x || !x->recv_rows) return MOE_EINVAL;
+  if (p->n_tokens > 0 && (!hidden || !x->recv_slot)) return MOE_EINVAL;
+  if (p->recv_capacity > 0 && (!recv_payload || !recv_scales)) return MOE_EINVAL;
+  if (!aligned(hidden, 16) || !aligned(recv_payload, 16) || !aligned(x->recv_slot, 4) ||
+      !aligned(x->recv_rows, 4) || !aligned(input_scale, 4))
+    return MOE_EALIGN;
+  return launched(moe::launch_exchange_dispatch(*p, *x, hidden, nullptr, input_scale, recv_payload,
+                                                recv_scales, static_cast<hipStream_t>(stream)));
 }
 
 MOE_API int moe_exchange_dispatch_gated(const moe_problem *p, const moe_exchange *x, const uint16_t *hidden,
@@ -222,8 +260,9 @@ MOE_API int moe_exchange_dispatch_gated(const moe_problem *p, const moe_exchange
       !aligned(x->recv_rows, 4) || !aligned(topk_weights, 4) ||
       (p->fmt == MOE_FMT_FP8_E4M3_B128 && !aligned(recv_scales, 4)))
     return MOE_EALIGN;
+  if (p->fmt == MOE_FMT_NVFP4_B16) return MOE_EINVAL;
   const float *w = p->n_tokens > 0 ? topk_weights : nullptr;
-  return launched(moe::launch_exchange_dispatch(*p, *x, hidden, w, recv_payload, recv_scales,
+  return launched(moe::launch_exchange_dispatch(*p, *x, hidden, w, nullptr, recv_payload, recv_scales,
                                                 static_cast<hipStream_t>(stream)));
 }
 

@@ -75,6 +75,7 @@ struct DispatchArgs {
   const uint16_t *x;
   const int32_t *slot;
   const float *w;  // [n][k] gates applied at dispatch (gated launches only)
+  const float *gscale;  // [1] NVFP4 global encode scale
   const int32_t *counts;
   const int32_t *offsets;
   uint8_t *payload;
@@ -269,6 +270,42 @@ __device__ void slab_mx(const DispatchArgs &g, int64_t t, int slab) {
           store<NT>(reinterpret_cast<uint32_t *>(prow + elem / 2), w[c][0]);
         if ((lane & (32 / kLE - 1)) == 0) store<NT>(srow + elem / 32, sbyte[c]);
       }
+    }
+  }
+}
+
+// ---- NVFP4: E2M1 codes, one E4M3 scale per 16 values, fp32 global scale -----
+// (Mojo ep.dispatch_async.block.scaled.nv struct: NVFP4 transfer with global
+// input scales.)  Per 16-value block (a lane pair): sf = E4M3(fl32(amax / 6)
+// * gs), saturated at 448 (the hardware conversion is exact below 464), and
+// codes E2M1(fl32(fl32(x * gs) / value(sf))) with IEEE division.
+template <bool NT>
+__device__ void slab_nvfp4(const DispatchArgs &g, int64_t t, int slab) {
+  static_assert(kLE == 8 && kQC == 1, "a 16-value block is one lane pair");
+  const int lane = lane_id();
+  const int my_slot = lane_slot(g, t, lane);
+  const int elem = slab * kQuantSlab + lane * kLE;
+  float f[kLE];
+  load_lane(g, t, elem, f);
+  uint32_t am = lane_absmax(f);
+  am = max(am, dpp<kQuadSwap1>(am));
+  const float gs = *g.gscale;
+  const float ts = (__uint_as_float(am) / 6.0f) * gs;
+  const uint32_t sf = e4m3_pair_hw(fminf(fmaxf(ts, -448.0f), 448.0f), 0.0f) & 0xFFu;
+  const float sfv = e4m3_magnitude(sf & 0x7Fu);
+  uint32_t w = 0;
+  if (sfv != 0.0f) {
+#pragma unroll
+    for (int i = 0; i < kLE; ++i) w |= e2m1_rne_sat((f[i] * gs) / sfv) << (4 * i);
+  }
+  for (int j = 0; j < g.k; ++j) {
+    const int d = __builtin_amdgcn_readlane(my_slot, j);
+    if (d < 0) continue;
+    if (elem < g.h) {
+      uint8_t *prow = g.payload + static_cast<int64_t>(d) * g.row_bytes;
+      uint8_t *srow = g.scales + static_cast<int64_t>(d) * g.scale_bytes;
+      store<NT>(reinterpret_cast<uint32_t *>(prow + elem / 2), w);
+      if ((lane & 1) == 0) store<NT>(srow + elem / 16, static_cast<uint8_t>(sf));
     }
   }
 }
@@ -476,13 +513,14 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(DispatchArgs g) {
     const int t = q / g.slabs;
     if (t >= g.n) return;
     const int slab = q - t * g.slabs;
-    if (GATED) {
+    if (GATED) {  // not instantiated for NVFP4 (the host rejects it)
       if (FMT == MOE_FMT_BF16) slab_bf16_gated<NT>(g, t, slab);
       else if (FMT == MOE_FMT_FP8_E4M3_B128) slab_fp8_gated<NT>(g, t, slab);
       else slab_mx_gated<NT>(g, t, slab);
     } else {
       if (FMT == MOE_FMT_BF16) slab_bf16<NT>(g, t, slab);
       else if (FMT == MOE_FMT_FP8_E4M3_B128) slab_fp8<NT>(g, t, slab);
+      else if (FMT == MOE_FMT_NVFP4_B16) slab_nvfp4<NT>(g, t, slab);
       else slab_mx<NT>(g, t, slab);
     }
     return;
@@ -508,8 +546,8 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(DispatchArgs g) {
 
 template <int FMT>
 void launch_fmt(const DispatchArgs &g, int grid, hipStream_t stream) {
-  if (g.w)
-    dispatch_kernel<FMT, MOE_DISPATCH_NT_STORE != 0, true><<<grid, kThreads, 0, stream>>>(g);
+  if (FMT != MOE_FMT_NVFP4_B16 && g.w)
+    dispatch_kernel<FMT, MOE_DISPATCH_NT_STORE != 0, FMT != MOE_FMT_NVFP4_B16><<<grid, kThreads, 0, stream>>>(g);
   else
     dispatch_kernel<FMT, MOE_DISPATCH_NT_STORE != 0, false><<<grid, kThreads, 0, stream>>>(g);
 }
@@ -536,6 +574,9 @@ DispatchArgs base_args(const moe_problem &p, int64_t tokens, const int32_t *slot
   } else if (p.fmt == MOE_FMT_FP8_E4M3_B128) {
     g.row_bytes = p.hidden;
     g.scale_bytes = 4 * static_cast<int64_t>(p.hidden / 128);
+  } else if (p.fmt == MOE_FMT_NVFP4_B16) {
+    g.row_bytes = p.hidden / 2;
+    g.scale_bytes = p.hidden / 16;
   } else {
     g.row_bytes = p.hidden / 2;
     g.scale_bytes = p.hidden / 32;
@@ -552,6 +593,7 @@ hipError_t launch_args(const DispatchArgs &g, int fmt, hipStream_t stream) {
   if (grid == 0) return hipSuccess;
   if (fmt == MOE_FMT_BF16) launch_fmt<MOE_FMT_BF16>(g, grid, stream);
   else if (fmt == MOE_FMT_FP8_E4M3_B128) launch_fmt<MOE_FMT_FP8_E4M3_B128>(g, grid, stream);
+  else if (fmt == MOE_FMT_NVFP4_B16) launch_fmt<MOE_FMT_NVFP4_B16>(g, grid, stream);
   else launch_fmt<MOE_FMT_MXFP4_B32>(g, grid, stream);
   return hipGetLastError();
 }
@@ -559,9 +601,11 @@ hipError_t launch_args(const DispatchArgs &g, int fmt, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_dispatch(const moe_problem &p, const moe_plan &plan, const uint16_t *hidden,
-                           const float *gates, void *payload, void *scales, hipStream_t stream) {
+                           const float *gates, const float *gscale, void *payload, void *scales,
+                           hipStream_t stream) {
   DispatchArgs g = base_args(p, p.n_tokens, plan.slot, hidden, payload, scales);
   g.w = gates;
+  g.gscale = gscale;
   g.counts = plan.expert_counts;
   g.offsets = plan.expert_offsets;
   g.r_max = max_rows(p);
@@ -579,10 +623,12 @@ hipError_t launch_dispatch(const moe_problem &p, const moe_plan &plan, const uin
 }
 
 hipError_t launch_exchange_dispatch(const moe_problem &p, const moe_exchange &x, const uint16_t *hidden,
-                                    const float *gates, void *payload, void *scales, hipStream_t stream) {
+                                    const float *gates, const float *gscale, void *payload, void *scales,
+                                    hipStream_t stream) {
   const int64_t tokens = p.n_tokens * p.ep;
   DispatchArgs g = base_args(p, tokens, x.recv_slot, hidden, payload, scales);
   g.w = gates;
+  g.gscale = gscale;
   g.r_max = p.recv_capacity * p.ep;
   g.pad_blocks = 0;  // no per-expert padding in receive buffers
   g.seg_used = x.recv_rows;

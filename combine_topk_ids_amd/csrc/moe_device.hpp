@@ -9,6 +9,8 @@
 //          saturating at 6.
 //   E8M0   OCP MX v1.0 shared scale: X = floor(log2 amax) - 2 (2 is the
 //          largest E2M1 exponent), stored as X + 127.
+//   NVFP4  E2M1 codes, one E4M3 scale per 16 values, one fp32 global
+//          encode scale.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -149,6 +151,13 @@ __device__ __forceinline__ float fp8_quotient_fast(float x, float s, float r) {
 // fp32 |v| < 464 (checked exhaustively), and |fl32(x/s)| <= 448 * (1 + 2^-22).
 __device__ __forceinline__ uint32_t e4m3_pair_hw(float a, float b) {
   return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false)) & 0xFFFFu;
+}
+
+// Value of an E4M3 magnitude code (0 .. 0x7E): exact in fp32.
+__device__ __forceinline__ float e4m3_magnitude(uint32_t code) {
+  const uint32_t e = (code >> 3) & 15u, m = code & 7u;
+  if (e == 0) return static_cast<float>(m) * 0x1p-9f;  // subnormals: m/8 * 2^-6
+  return __uint_as_float(((e + 120u) << 23) | (m << 20));
 }
 
 // ---------------------------------------------------------------- E2M1 ---

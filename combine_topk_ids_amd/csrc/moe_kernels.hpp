@@ -55,7 +55,8 @@ size_t exchange_workspace_bytes(const moe_problem &p);
 hipError_t launch_exchange_plan(const moe_problem &p, const int32_t *ids, const moe_exchange &x,
                                 void *workspace, hipStream_t stream);
 hipError_t launch_exchange_dispatch(const moe_problem &p, const moe_exchange &x, const uint16_t *hidden,
-                                    const float *gates, void *payload, void *scales, hipStream_t stream);
+                                    const float *gates, const float *gscale, void *payload, void *scales,
+                                    hipStream_t stream);
 
 // Multihot routing map [N][E] (+ optional dense probabilities) -> compact
 // top-k IDs and weights; status gets MOE_STATUS_MAP_OVERFLOW.
@@ -66,9 +67,11 @@ hipError_t launch_routing_map_to_topk(const moe_problem &p, const uint8_t *map, 
 hipError_t launch_exchange_combine(const moe_problem &p, const moe_exchange &x, const uint16_t *expert_out,
                                    const float *weights, uint16_t *out, hipStream_t stream);
 
-// gates: NULL, or [N][k] weights applied to each copy at dispatch
+// gates: NULL, or [N][k] weights applied to each copy at dispatch;
+// gscale: the NVFP4 global encode scale (device, one float) or NULL
 hipError_t launch_dispatch(const moe_problem &p, const moe_plan &plan, const uint16_t *hidden,
-                           const float *gates, void *payload, void *scales, hipStream_t stream);
+                           const float *gates, const float *gscale, void *payload, void *scales,
+                           hipStream_t stream);
 
 hipError_t launch_combine(const moe_problem &p, const moe_plan &plan, const uint16_t *expert_out,
                           const float *weights, uint16_t *out, hipStream_t stream);

@@ -21,15 +21,16 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 
 MOE_OK, MOE_EINVAL, MOE_EALIGN, MOE_EOVERFLOW, MOE_EHIP = 0, -1, -2, -3, -4
 STATUS_BAD_ID, STATUS_DUP_ID, STATUS_CAPACITY, STATUS_MAP_OVERFLOW, STATUS_DROPPED = 1, 2, 4, 8, 16
-FMT = {"bf16": 0, "fp8": 1, "mxfp4": 2}
+FMT = {"bf16": 0, "fp8": 1, "mxfp4": 2, "nvfp4": 3}
 FLAG_ZERO_TAIL = 1
 
 # every symbol include/moe.h declares
 EXPORTS = ("moe_check_problem", "moe_max_rows", "moe_expert_capacity", "moe_payload_row_bytes",
            "moe_scale_row_bytes", "moe_workspace_bytes", "moe_dispatch_plan",
-           "moe_dispatch", "moe_dispatch_gated", "moe_combine", "moe_check_exchange",
-           "moe_exchange_workspace_bytes", "moe_exchange_plan", "moe_exchange_dispatch",
-           "moe_exchange_dispatch_gated", "moe_exchange_combine", "moe_map_workspace_bytes",
+           "moe_dispatch", "moe_dispatch_scaled", "moe_dispatch_gated", "moe_combine",
+           "moe_check_exchange", "moe_exchange_workspace_bytes", "moe_exchange_plan",
+           "moe_exchange_dispatch", "moe_exchange_dispatch_scaled", "moe_exchange_dispatch_gated",
+           "moe_exchange_combine", "moe_map_workspace_bytes",
            "moe_routing_map_to_topk", "moe_strerror")
 
 
@@ -77,6 +78,8 @@ def _load() -> ctypes.CDLL:
         "moe_dispatch_plan": (ctypes.c_int, [P, V, ctypes.POINTER(Plan), V, V]),
         "moe_dispatch": (ctypes.c_int, [P, ctypes.POINTER(Plan), V, V, V, V]),
         "moe_dispatch_gated": (ctypes.c_int, [P, ctypes.POINTER(Plan), V, V, V, V, V]),
+        "moe_dispatch_scaled": (ctypes.c_int, [P, ctypes.POINTER(Plan), V, V, V, V, V]),
+        "moe_exchange_dispatch_scaled": (ctypes.c_int, [P, ctypes.POINTER(Exchange), V, V, V, V, V]),
         "moe_combine": (ctypes.c_int, [P, ctypes.POINTER(Plan), V, V, V, V]),
         "moe_check_exchange": (ctypes.c_int, [P]),
         "moe_exchange_workspace_bytes": (ctypes.c_size_t, [P]),
@@ -212,6 +215,9 @@ def alloc_payload(p: Problem, device="cuda"):
     if p.fmt == FMT["fp8"]:
         return (torch.empty((r_max, h), dtype=torch.uint8, device=device),
                 torch.empty((r_max, h // 128), dtype=torch.float32, device=device))
+    if p.fmt == FMT["nvfp4"]:
+        return (torch.empty((r_max, h // 2), dtype=torch.uint8, device=device),
+                torch.empty((r_max, h // 16), dtype=torch.uint8, device=device))
     return (torch.empty((r_max, h // 2), dtype=torch.uint8, device=device),
             torch.empty((r_max, h // 32), dtype=torch.uint8, device=device))
 
@@ -272,6 +278,25 @@ def moe_dispatch(p: Problem, plan: PlanBuffers, hidden: torch.Tensor, payload: t
     rc = lib.moe_dispatch(ctypes.byref(p), ctypes.byref(plan.as_struct()), x, pay, sc or None,
                           _stream(stream))
     _checked(rc, "moe_dispatch")
+
+
+def moe_dispatch_scaled(p: Problem, plan: PlanBuffers, hidden: torch.Tensor,
+                        input_scale: torch.Tensor, payload: torch.Tensor, scales: torch.Tensor,
+                        stream=None) -> None:
+    """NVFP4 dispatch; input_scale: device float32 tensor holding the global
+    encode scale."""
+    r_max, pb, sb, _ = _sizes(p)
+    x = _dev(hidden, "hidden", _BF16, p.n_tokens * p.hidden)
+    gs = _dev(input_scale, "input_scale", (torch.float32,), 1)
+    if payload.numel() * payload.element_size() < r_max * pb:
+        raise ValueError("payload is smaller than R_max rows")
+    if scales.numel() * scales.element_size() < r_max * sb:
+        raise ValueError("scales is smaller than R_max rows")
+    pay = _dev(payload, "payload", _PAYLOAD)
+    sc = _dev(scales, "scales", (torch.uint8,))
+    rc = lib.moe_dispatch_scaled(ctypes.byref(p), ctypes.byref(plan.as_struct()), x, gs, pay, sc,
+                                 _stream(stream))
+    _checked(rc, "moe_dispatch_scaled")
 
 
 def moe_dispatch_gated(p: Problem, plan: PlanBuffers, hidden: torch.Tensor,
@@ -363,6 +388,9 @@ def alloc_recv_payload(p: Problem, device="cuda"):
     if p.fmt == FMT["fp8"]:
         return (torch.empty((rows, h), dtype=torch.uint8, device=device),
                 torch.empty((rows, h // 128), dtype=torch.float32, device=device))
+    if p.fmt == FMT["nvfp4"]:
+        return (torch.empty((rows, h // 2), dtype=torch.uint8, device=device),
+                torch.empty((rows, h // 16), dtype=torch.uint8, device=device))
     return (torch.empty((rows, h // 2), dtype=torch.uint8, device=device),
             torch.empty((rows, h // 32), dtype=torch.uint8, device=device))
 
@@ -392,6 +420,24 @@ def moe_exchange_dispatch(p: Problem, x: ExchangeBuffers, hidden: torch.Tensor,
     rc = lib.moe_exchange_dispatch(ctypes.byref(p), ctypes.byref(x.as_struct()), h, pay,
                                    sc or None, _stream(stream))
     _checked(rc, "moe_exchange_dispatch")
+
+
+def moe_exchange_dispatch_scaled(p: Problem, x: ExchangeBuffers, hidden: torch.Tensor,
+                                 input_scale: torch.Tensor, payload: torch.Tensor,
+                                 scales: torch.Tensor, stream=None) -> None:
+    _, pb, sb, _ = _sizes(p)
+    rows = p.ep * p.recv_capacity
+    h = _dev(hidden, "hidden", _BF16, p.ep * p.n_tokens * p.hidden)
+    gs = _dev(input_scale, "input_scale", (torch.float32,), 1)
+    if payload.numel() * payload.element_size() < rows * pb:
+        raise ValueError("payload is smaller than EP * C rows")
+    if scales.numel() * scales.element_size() < rows * sb:
+        raise ValueError("scales is smaller than EP * C rows")
+    pay = _dev(payload, "payload", _PAYLOAD)
+    sc = _dev(scales, "scales", (torch.uint8,))
+    rc = lib.moe_exchange_dispatch_scaled(ctypes.byref(p), ctypes.byref(x.as_struct()), h, gs, pay,
+                                          sc, _stream(stream))
+    _checked(rc, "moe_exchange_dispatch_scaled")
 
 
 def moe_exchange_dispatch_gated(p: Problem, x: ExchangeBuffers, hidden: torch.Tensor,

@@ -46,6 +46,7 @@ class Workload:
     recv_capacity: int | None = None  # None: dropless (all tokens) * min(k, E/EP)
     ranks: int = 1    # simulated source ranks, N tokens each (exchange workloads: EP)
     capacity_factor: float | None = None  # fixed per-expert capacity from this factor
+    input_scale: float = 1.0    # NVFP4 global encode scale handed to the dispatch
 
     @property
     def l(self) -> int:
@@ -95,6 +96,12 @@ WORKLOADS = {
         # decode-sized MX-FP4 dispatch
         Workload("decode_mxfp4_n128", n=128, h=7168, e=256, k=8, ep=8, a=1,
                  fmt="mxfp4", routing="softmax", experts="random"),
+        # NVFP4 dispatch (global encode scale 448 * 6 / 8: blocks of N(0,1)
+        # rows keep their E4M3 scales below saturation for |x| up to 8)
+        Workload("nvfp4_b16_n8192", n=8192, h=7168, e=256, k=8, ep=32, a=1,
+                 fmt="nvfp4", routing="softmax", experts="random", input_scale=336.0),
+        Workload("decode_nvfp4_n128", n=128, h=7168, e=256, k=8, ep=8, a=1,
+                 fmt="nvfp4", routing="softmax", experts="random", input_scale=336.0),
         # fixed per-expert capacity (factor 1.0: experts above the mean drop)
         Workload("capacity_bf16_n4096", n=4096, h=4096, e=64, k=6, ep=8, a=1,
                  fmt="bf16", routing="softmax", experts="identity",

@@ -94,7 +94,18 @@ typedef enum moe_fmt {
    * low nibble of byte m; an all-zero block has scale byte 0 and zero
    * codes.  payload uint8 [R_max][H/2], scales uint8 [R_max][H/32].
    * Needs H % 32 == 0.                                                    */
-  MOE_FMT_MXFP4_B32 = 2
+  MOE_FMT_MXFP4_B32 = 2,
+  /* NVFP4: E2M1 codes with one E4M3 scale per 16 values and one fp32 global
+   * encode scale gs (a device value the caller passes to the *_scaled
+   * dispatch calls): per block sf = E4M3(fl32(fl32(amax / 6) * gs)),
+   * rounded to nearest even and saturated at 448; code = E2M1(fl32(fl32(x *
+   * gs) / value(sf))) as for MX-FP4; a block whose scale is 0 has zero codes.
+   * Decoding: code * value(sf) / gs.  payload uint8 [R_max][H/2] (element
+   * 2m in the low nibble of byte m), scales uint8 [R_max][H/16] (E4M3
+   * codes).  Needs H % 32 == 0.  (Mojo ep.dispatch_async.block.scaled.nv
+   * struct: NVFP4 transfer and its global input scales; Mojo shmem ep_comm
+   * module: NVBlockScaledTokenFormat.)                                      */
+  MOE_FMT_NVFP4_B16 = 3
 } moe_fmt;
 
 /* ---- flags -------------------------------------------------------------- */
@@ -200,6 +211,14 @@ MOE_API int moe_dispatch(const moe_problem *p, const moe_plan *plan,
                          const uint16_t *hidden, void *payload, void *scales,
                          void *stream);
 
+/* Dispatch in a format that takes a global encode scale (MOE_FMT_NVFP4_B16;
+ * the others return MOE_EINVAL): as moe_dispatch, with input_scale a device
+ * pointer to the fp32 global encode scale gs.  moe_dispatch itself returns
+ * MOE_EINVAL for such a format. */
+MOE_API int moe_dispatch_scaled(const moe_problem *p, const moe_plan *plan,
+                                const uint16_t *hidden, const float *input_scale,
+                                void *payload, void *scales, void *stream);
+
 /* Gated dispatch: as moe_dispatch, but each valid pair (t, j) writes
  * encode(fl32(topk_weights[t][j] * hidden[t][c]) for every c), the token row
  * pre-multiplied by its gate, to packed row slot[t][j] (DeepSpeed v0.19.4
@@ -208,7 +227,7 @@ MOE_API int moe_dispatch(const moe_problem *p, const moe_plan *plan,
  * its block scale is fl32(fl32(|w| * amax) / 448) and its codes
  * E4M3(fl32(v / s)) with v = fl32(w * x); for MX-FP4 its exponent comes from
  * fl32(|w| * amax).  topk_weights: device float [N][k].  A combine of gated
- * rows passes NULL weights. */
+ * rows passes NULL weights.  Not for MOE_FMT_NVFP4_B16 (MOE_EINVAL). */
 MOE_API int moe_dispatch_gated(const moe_problem *p, const moe_plan *plan,
                                const uint16_t *hidden, const float *topk_weights,
                                void *payload, void *scales, void *stream);
@@ -304,8 +323,18 @@ MOE_API int moe_exchange_dispatch(const moe_problem *p, const moe_exchange *x,
                                   const uint16_t *hidden, void *recv_payload,
                                   void *recv_scales, void *stream);
 
+/* As moe_exchange_dispatch, for MOE_FMT_NVFP4_B16 with its global encode
+ * scale (see moe_dispatch_scaled). */
+MOE_API int moe_exchange_dispatch_scaled(const moe_problem *p,
+                                         const moe_exchange *x,
+                                         const uint16_t *hidden,
+                                         const float *input_scale,
+                                         void *recv_payload, void *recv_scales,
+                                         void *stream);
+
 /* As moe_exchange_dispatch, with every copy pre-multiplied by its gate as in
- * moe_dispatch_gated; topk_weights: device float [EP][N][k]. */
+ * moe_dispatch_gated (not for MOE_FMT_NVFP4_B16); topk_weights: device
+ * float [EP][N][k]. */
 MOE_API int moe_exchange_dispatch_gated(const moe_problem *p,
                                         const moe_exchange *x,
                                         const uint16_t *hidden,

@@ -61,7 +61,7 @@ def test_sizes_match_the_closed_form(moe):
 @pytest.mark.parametrize("field,value,code", [
     ("n_tokens", -1, -1), ("hidden", 0, -1), ("hidden", 12, -1), ("top_k", 0, -1),
     ("top_k", 9, -1), ("n_experts", 0, -1), ("n_experts", 1025, -1), ("ep", 3, -1),
-    ("ep", 0, -1), ("pad_multiple", 0, -1), ("recv_capacity", -5, -1), ("fmt", 3, -1),
+    ("ep", 0, -1), ("pad_multiple", 0, -1), ("recv_capacity", -5, -1), ("fmt", 4, -1),
     ("flags", 2, -1), ("n_tokens", 1 << 30, -3),
 ])
 def test_invalid_problems_rejected(moe, field, value, code):
@@ -218,3 +218,29 @@ def test_expert_capacity_sizes_and_checks(moe):
     # no fixed capacity in the exchange
     assert moe.moe_check_exchange(moe.problem(64, 256, 2, 8, 4, recv_capacity=64,
                                               expert_capacity=8)) == -1
+
+
+# ---- NVFP4 ------------------------------------------------------------------------
+
+def test_nvfp4_sizes_and_entry_points(moe):
+    ref = ctypes.byref
+    fake = 1 << 20
+    p = moe.problem(64, 256, 2, 8, 4, fmt="nvfp4")
+    assert moe.moe_check_problem(p) == 0
+    assert moe.moe_payload_row_bytes(p) == 128 and moe.moe_scale_row_bytes(p) == 16
+    assert moe.moe_check_problem(moe.problem(64, 48, 2, 8, 4, fmt="nvfp4")) == -1  # H % 32
+    full = moe.Plan(*([fake] * 7))
+    # the plain and gated dispatches cannot carry the global scale
+    assert moe.lib.moe_dispatch(ref(p), ref(full), fake, fake, fake, None) == -1
+    assert moe.lib.moe_dispatch_gated(ref(p), ref(full), fake, fake, fake, fake, None) == -1
+    # the scaled dispatch needs NVFP4, the scale pointer and the scale rows
+    assert moe.lib.moe_dispatch_scaled(ref(p), ref(full), fake, None, fake, fake, None) == -1
+    assert moe.lib.moe_dispatch_scaled(ref(p), ref(full), fake, fake, fake, None, None) == -1
+    assert moe.lib.moe_dispatch_scaled(ref(p), ref(full), fake, fake + 2, fake, fake, None) == -2
+    pb = moe.problem(64, 256, 2, 8, 4)
+    assert moe.lib.moe_dispatch_scaled(ref(pb), ref(full), fake, fake, fake, None, None) == -1
+    px = moe.problem(64, 256, 2, 8, 4, recv_capacity=64, fmt="nvfp4")
+    fx = moe.Exchange(*([fake] * 8))
+    assert moe.lib.moe_exchange_dispatch(ref(px), ref(fx), fake, fake, fake, None) == -1
+    assert moe.lib.moe_exchange_dispatch_scaled(ref(px), ref(fx), fake, None, fake, fake, None) == -1
+    assert moe.lib.moe_exchange_dispatch_scaled(ref(px), ref(fx), fake, fake, fake, None, None) == -1

@@ -1,0 +1,134 @@
+"""GPU parity of NVFP4 dispatch (E2M1 codes, E4M3 scale per 16 values, fp32
+global encode scale) through the C ABI against the CPU oracle.
+
+Bar: plan arrays, payload nibbles and E4M3 scale bytes bit-exact (pad and
+tail rows included); combine within one bf16 ulp.  Inputs come from the
+seeded generators only; expected values only from ``oracle``.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from combine_topk_ids_amd.workloads import (WORKLOADS, make_inputs, random_bf16,
+                                            random_routing)
+from gpu_helpers import SENTINEL, assert_combine_close, say, to_dev_bf16, u16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def moe():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import combine_topk_ids_amd.moe as m
+    return m
+
+
+def run_nvfp4(moe, *, ids, weights, hidden, e, ep, a, gs, expert_out, zero_tail=True):
+    n, k = ids.shape
+    h = hidden.shape[1]
+    p = moe.problem(n, h, k, e, ep, pad_multiple=a, fmt="nvfp4", zero_tail=zero_tail)
+    plan = moe.alloc_plan(p)
+    payload, scales = moe.alloc_payload(p)
+    payload.fill_(SENTINEL)
+    scales.fill_(SENTINEL)
+    out = torch.full((n, h), 7.0, dtype=torch.bfloat16, device="cuda")
+    gs_d = torch.tensor([gs], dtype=torch.float32, device="cuda")
+    moe.moe_dispatch_plan(p, torch.from_numpy(ids).cuda(), plan)
+    moe.moe_dispatch_scaled(p, plan, to_dev_bf16(hidden), gs_d, payload, scales)
+    moe.moe_combine(p, plan, to_dev_bf16(expert_out), torch.from_numpy(weights).cuda(), out)
+    torch.cuda.synchronize()
+    return dict(slot=plan.slot.cpu().numpy(), payload=payload.cpu().numpy(),
+                scales=scales.cpu().numpy(), out=u16(out),
+                status=int(plan.status.cpu().numpy().view(np.uint32)[0]))
+
+
+def check_nvfp4(moe, *, ids, weights, hidden, e, ep, a, gs, expert_out):
+    n, k = ids.shape
+    h = hidden.shape[1]
+    got = run_nvfp4(moe, ids=ids, weights=weights, hidden=hidden, e=e, ep=ep, a=a, gs=gs,
+                    expert_out=expert_out)
+    pl = oracle.plan(ids, e, ep, a, n * min(k, e // ep), h)
+    assert np.array_equal(got["slot"], pl["slot"])
+    pay, sc = oracle.dispatch_nvfp4(hidden, pl, gs, zero_tail=True)
+    assert np.array_equal(got["payload"], pay)
+    assert np.array_equal(got["scales"], sc)
+    ref = oracle.combine(pl["slot"], weights, expert_out)
+    return got, assert_combine_close(got["out"], ref)
+
+
+@pytest.mark.parametrize("name", ["decode_nvfp4_n128", "nvfp4_b16_n8192"])
+def test_nvfp4_workload_parity(moe, name):
+    """Every packed row of the workload at full size."""
+    w = WORKLOADS[name]
+    say(f"[nvfp4 parity] {name}: {w.describe()}, gs={w.input_scale}")
+    r_max = oracle.max_rows(w.n, w.k, w.e, w.a)
+    inp = make_inputs(w, seed=0, expert_rows=r_max)
+    got, nonexact = check_nvfp4(moe, ids=inp["ids"], weights=inp["weights"], hidden=inp["hidden"],
+                                e=w.e, ep=w.ep, a=w.a, gs=w.input_scale,
+                                expert_out=inp["expert_out"])
+    assert got["status"] == 0 and nonexact == 0
+
+
+# n, h, e, k, ep, a, gs, value scale, masked fraction
+FUZZ = [
+    (1, 32, 1, 1, 1, 1, 1.0, 1.0, 0.0),
+    (777, 544, 16, 5, 4, 3, 0.37, 3.0, 0.1),
+    (2049, 384, 64, 7, 8, 16, 250.0, 1.0, 0.05),     # many scales saturate at 448
+    (1000, 96, 1024, 16, 64, 4, 3.0e-4, 1.0, 0.2),   # subnormal and zero scales
+    (300, 7168, 256, 8, 32, 1, 336.0, 1.0, 0.0),
+    (4097, 160, 12, 12, 3, 1, 1.0, 1e-3, 0.0),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(FUZZ)),
+                         ids=[f"n{c[0]}_h{c[1]}_e{c[2]}_k{c[3]}_gs{c[6]}" for c in FUZZ])
+def test_nvfp4_fuzz_shapes(moe, idx):
+    n, h, e, k, ep, a, gs, scale, masked = FUZZ[idx]
+    say(f"[nvfp4 fuzz] N={n} H={h} E={e} k={k} EP={ep} A={a} gs={gs} scale={scale}")
+    rng = np.random.default_rng(900 + idx)
+    ids, wts = random_routing(rng, n, e, k, masked_frac=masked)
+    x = random_bf16(rng, (n, h), scale=scale)
+    y = random_bf16(rng, (oracle.max_rows(n, k, e, a), h))
+    check_nvfp4(moe, ids=ids, weights=wts, hidden=x, e=e, ep=ep, a=a, gs=gs, expert_out=y)
+
+
+def test_nvfp4_extreme_values(moe):
+    """Largest finite bf16, subnormals, signed zeros, zero blocks, one huge
+    value per block, with a global scale that saturates some scales."""
+    rng = np.random.default_rng(5)
+    n, h, e, k = 64, 256, 4, 2
+    ids, wts = random_routing(rng, n, e, k)
+    x = random_bf16(rng, (n, h))
+    x[0] = 0x7F7F                 # largest finite bf16
+    x[1] = 0x0001                 # smallest subnormal
+    x[2] = 0x8000                 # -0
+    x[3, ::16] = 0x4700           # one large value per block
+    x[4] = 0
+    x[5, :16] = 0xFF7F            # most negative finite
+    say("[nvfp4 extremes]")
+    for gs in (1.0, 1e-30, 3.0e38):
+        check_nvfp4(moe, ids=ids, weights=wts, hidden=x, e=e, ep=2, a=2, gs=gs,
+                    expert_out=random_bf16(rng, (n * k + e, h)))
+
+
+def test_nvfp4_exchange(moe):
+    rng = np.random.default_rng(6)
+    ep, n, e, k, cap, h = 4, 200, 32, 4, 230, 512
+    ids, wts = random_routing(rng, ep * n, e, k)
+    x = random_bf16(rng, (ep * n, h))
+    say(f"[nvfp4 exchange] EP={ep} N={n} E={e} k={k} C={cap} H={h}")
+    p = moe.problem(n, h, k, e, ep, recv_capacity=cap, fmt="nvfp4")
+    xb = moe.alloc_exchange(p)
+    payload, scales = moe.alloc_recv_payload(p)
+    payload.fill_(SENTINEL)
+    scales.fill_(SENTINEL)
+    gs = torch.tensor([20.0], dtype=torch.float32, device="cuda")
+    moe.moe_exchange_plan(p, torch.from_numpy(ids.reshape(ep, n, k)).cuda(), xb)
+    moe.moe_exchange_dispatch_scaled(p, xb, to_dev_bf16(x), gs, payload, scales)
+    torch.cuda.synchronize()
+    xp = oracle.exchange_plan(ids.reshape(ep, n, k), e, cap, h)
+    pl = dict(packed_src=xp["recv_src"].reshape(-1), r_max=ep * cap, r_used=ep * cap)
+    pay, sc = oracle.dispatch_nvfp4(x, pl, 20.0)
+    assert np.array_equal(payload.cpu().numpy(), pay)
+    assert np.array_equal(scales.cpu().numpy(), sc)
