@@ -42,7 +42,8 @@ def log(msg):
 
 
 def row_bytes(fmt, h):
-    return {"bf16": 2 * h, "fp8": h + 4 * (h // 128), "mxfp4": h // 2 + h // 32}[fmt]
+    return {"bf16": 2 * h, "fp8": h + 4 * (h // 128), "mxfp4": h // 2 + h // 32,
+            "nvfp4": h // 2 + h // 16}[fmt]
 
 
 def step_bytes(w, r_used, r_max, kept=None):
@@ -111,6 +112,7 @@ class Path:
         y = None
         if "expert_out" in inp:
             y = torch.from_numpy(inp["expert_out"].view(np.int16)).to(dev).view(torch.bfloat16)
+        self.gs = torch.tensor([w.input_scale], dtype=torch.float32, device=dev)
         self.sets = []
         for c in range(copies):
             plan = moe.alloc_plan(self.p, dev)
@@ -133,7 +135,10 @@ class Path:
         m.moe_dispatch_plan(p, s["ids"], s["plan"])
         if ev is not None:
             ev[1].record()
-        m.moe_dispatch(p, s["plan"], s["x"], s["payload"], s["scales"])
+        if self.w.fmt == "nvfp4":
+            m.moe_dispatch_scaled(p, s["plan"], s["x"], self.gs, s["payload"], s["scales"])
+        else:
+            m.moe_dispatch(p, s["plan"], s["x"], s["payload"], s["scales"])
         if ev is not None:
             ev[2].record()
         m.moe_combine(p, s["plan"], s["y"], s["w"], s["out"])
@@ -311,7 +316,10 @@ def cpu_baseline(w, inp, budget_s=10.0, pass_s=2.0):
             kept = int(pl["dest_counts"].sum())
         else:
             pl = oracle.plan(ids, w.e, w.ep, w.a, m * min(w.k, w.l), w.h)
-        pay, _ = oracle.dispatch(w.fmt, x, pl, zero_tail=False)
+        if w.fmt == "nvfp4":
+            pay, _ = oracle.dispatch_nvfp4(x, pl, w.input_scale, zero_tail=False)
+        else:
+            pay, _ = oracle.dispatch(w.fmt, x, pl, zero_tail=False)
         y = pay.view(np.uint16).reshape(pl["r_max"], -1) if "expert_out" not in inp \
             else inp["expert_out"]
         oracle.combine(pl["slot"], wts, y)
@@ -455,6 +463,8 @@ def main():
     if w.exchange:
         config.update(source_ranks=w.ranks, recv_capacity=w.capacity,
                       path="exchange: source-major receive buffers of C rows per rank")
+    if w.fmt == "nvfp4":
+        config["input_scale"] = w.input_scale
     if expert_cap:
         config.update(capacity_factor=w.capacity_factor, expert_capacity=expert_cap,
                       pairs_kept=path.kept(), path="fixed expert capacity, later pairs dropped")
