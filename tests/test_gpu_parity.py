@@ -181,6 +181,9 @@ FUZZ = [
     (600, 2112, 128, 9, 16, 8, "bf16", 0.3),
     (64, 7168, 256, 8, 8, 1, "mxfp4", 0.0),
     (260, 128, 2, 2, 1, 5, "fp8", 0.5),
+    (3840, 64, 64, 8, 8, 128, "bf16", 0.0),    # 15 count tiles of whole tokens
+    (32000, 64, 8, 1, 8, 1, "bf16", 0.1),      # k=1: 16 tiles of 2048 pairs
+    (1500, 64, 1024, 6, 64, 2, "bf16", 0.1),   # E=1024 over 5 tiles (expert passes)
 ]
 
 
@@ -239,6 +242,23 @@ def test_fault_bits(moe):
     got, pl, _ = check_full(moe, ids=ids, weights=w, hidden=random_bf16(rng, (n, 64)), e=e,
                             ep=4, a=1, fmt="bf16", cap=10)
     assert got["status"] == 1 | 2 | 4 == pl["status"]
+
+
+def test_fault_bits_far_from_block_zero(moe):
+    """Faults only in the last tokens: the block that writes the status word
+    must report pairs of a count tile it does not place itself."""
+    n = 8000
+    say(f"[edge] bad / duplicate ids in the last tokens, n={n}")
+    rng = np.random.default_rng(11)
+    k, e = 4, 16
+    ids, w = random_routing(rng, n, e, k)
+    for bits, edit in ((2, lambda a: a.__setitem__((n - 1, 3), a[n - 1, 1])),
+                       (1, lambda a: a.__setitem__((n - 2, 2), 16))):
+        bad = ids.copy()
+        edit(bad)
+        got, pl, _ = check_full(moe, ids=bad, weights=w, hidden=random_bf16(rng, (n, 64)), e=e,
+                                ep=4, a=2, fmt="bf16")
+        assert got["status"] == bits == pl["status"]
 
 
 def test_extreme_values(moe):
