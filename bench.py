@@ -13,9 +13,11 @@ GB/s.  Inputs are resident in HBM before timing starts; consecutive steps
 rotate over several copies of all buffers so that a step does not find its
 inputs in the 256 MB last-level cache from the step before.
 
-Per-kernel durations for the roofline come from HIP events recorded around
-every launch on the stream the kernels run on, in a second pass over the
-same number of steps.
+Per-kernel durations for the roofline (means, and p10/p50/p90 of each phase
+and of the step) come from HIP events recorded around every launch on the
+stream the kernels run on, in a second pass over the same number of steps.
+``payload_only`` repeats the rate counting only packed rows that hold a
+token.
 """
 from __future__ import annotations
 
@@ -152,6 +154,12 @@ class Path:
         """Pairs kept by a fixed expert capacity (rows the combine reads)."""
         return int(self.sets[0]["plan"].dest_counts.sum().item())
 
+    def live_rows(self):
+        """Packed rows that hold a token (not padding)."""
+        if self.expert_cap:
+            return self.kept()
+        return int(self.sets[0]["plan"].expert_counts.sum().item())
+
 
 class ExchangePath:
     """Device buffers and the three calls of one step of the exchange across
@@ -201,6 +209,10 @@ class ExchangePath:
         rows = self.sets[0]["xb"].recv_rows.clamp(max=self.w.capacity)
         return int(rows.sum().item())
 
+    def live_rows(self):
+        """Receive rows that hold a token (not zero rows)."""
+        return self.r_used()
+
 
 def time_steps(torch, path, steps, warmup):
     for i in range(warmup):
@@ -223,12 +235,14 @@ def time_kernels(torch, path, steps):
     for i in range(steps):
         path.step(i, evs[i])
     torch.cuda.synchronize()
-    d = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])]
-                  for e in evs])
-    return dict(plan=float(np.mean(d[:, 0])), dispatch=float(np.mean(d[:, 1])),
-                combine=float(np.mean(d[:, 2])),
-                plan_p50=float(np.median(d[:, 0])), dispatch_p50=float(np.median(d[:, 1])),
-                combine_p50=float(np.median(d[:, 2])))
+    d = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3]),
+                   e[0].elapsed_time(e[3])] for e in evs])
+    out = {}
+    for c, name in enumerate(("plan", "dispatch", "combine", "step")):
+        out[name] = float(np.mean(d[:, c]))
+        for q in (10, 50, 90):
+            out[f"{name}_p{q}"] = float(np.percentile(d[:, c], q))
+    return out
 
 
 def stream_reference(torch, gib=1.0):
@@ -428,9 +442,19 @@ def main():
     kt = time_kernels(torch, path, args.steps)
     log(f"[bench] per-kernel means (us): plan {kt['plan'] * 1e3:.2f} dispatch "
         f"{kt['dispatch'] * 1e3:.2f} combine {kt['combine'] * 1e3:.2f}")
+    log("[bench] p10/p50/p90 (us): " + "; ".join(
+        f"{n} {kt[n + '_p10'] * 1e3:.2f}/{kt[n + '_p50'] * 1e3:.2f}/{kt[n + '_p90'] * 1e3:.2f}"
+        for n in ("plan", "dispatch", "combine", "step")))
     ru = path.r_used()
     b = step_bytes(w, ru, r_max, path.kept() if expert_cap else None)
     value = b["total"] / (ms * 1e-3) / 1e9
+    # the same step counting only rows that hold a token (no pad, zero or
+    # tail rows written)
+    live = path.live_rows()
+    disp_live = 2 * w.tokens * w.h + live * row_bytes(w.fmt, w.h)
+    payload_only = dict(live_rows=live, dispatch_bytes=disp_live,
+                        total_bytes=b["plan"] + disp_live + b["combine"],
+                        gbps=round((b["plan"] + disp_live + b["combine"]) / (ms * 1e-3) / 1e9, 1))
 
     dom = "dispatch" if kt["dispatch"] >= kt["combine"] else "combine"
     achieved = b[dom] / (kt[dom] * 1e-3) / 1e9
@@ -484,6 +508,7 @@ def main():
         "config": config,
         "frac_of_peak": round(value / PEAK_HBM_GBPS, 4),
         "bytes_per_step": b,
+        "payload_only": payload_only,
         "kernel_us": {k: round(v * 1e3, 2) for k, v in kt.items()},
         "roofline": roofline,
         "cpu_baseline": cpu,
