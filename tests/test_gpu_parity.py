@@ -184,6 +184,10 @@ FUZZ = [
     (3840, 64, 64, 8, 8, 128, "bf16", 0.0),    # 15 count tiles of whole tokens
     (32000, 64, 8, 1, 8, 1, "bf16", 0.1),      # k=1: 16 tiles of 2048 pairs
     (1500, 64, 1024, 6, 64, 2, "bf16", 0.1),   # E=1024 over 5 tiles (expert passes)
+    (200, 64, 128, 64, 8, 2, "bf16", 0.1),     # k=64, the largest top-k: every lane a slot
+    (70, 256, 64, 64, 4, 1, "fp8", 0.0),       # k=E=64
+    (40, 65536, 16, 4, 4, 1, "bf16", 0.0),     # H=65536: 32 slabs per token
+    (24, 16384, 8, 2, 2, 3, "fp8", 0.0),       # H=16384: 32 FP8 slabs per token
 ]
 
 
