@@ -14,11 +14,16 @@
 // with more than k routed experts keeps its first k, and the call's status
 // word gets MOE_STATUS_MAP_OVERFLOW.
 //
-// Design for gfx950.  The work is tiny and latency-bound: one thread per
-// token scans its map row with 16-byte loads (byte loads when rows are not
-// 16-byte aligned), each block ORs its overflow flags into one workspace
-// word, and a one-block kernel ORs those into the status word, so the
-// status needs no clearing before the call.
+// Design for gfx950.  The work is tiny, so latency decides.  A token's row
+// is read by a group of lanes in one round of loads: each lane takes 16
+// experts (one 16-byte load when rows are 16-byte aligned, else byte
+// loads), so a group is ceil(E/16) lanes rounded up to a power of two, at
+// most a wave (E <= 1024).  A segmented prefix sum of the lanes' counts of
+// routed experts gives every lane the first output slot of its experts;
+// the probabilities of those experts are loaded together, then stored.
+// Each block ORs its overflow flags into one workspace word, and a
+// one-block kernel ORs those into the status word, so the status needs no
+// clearing before the call.
 #include "moe_device.hpp"
 #include "moe_kernels.hpp"
 
@@ -26,6 +31,7 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kLaneExperts = 16;  // map bytes per lane
 
 struct MapArgs {
   const uint8_t *map;
@@ -36,45 +42,72 @@ struct MapArgs {
   uint32_t *status;
   int64_t n;
   int e, k;
+  int lpt;            // lanes per token: a power of two, at most a wave
   int nblocks;
-  bool vec;  // rows are 16-byte aligned
+  bool vec;           // rows are 16-byte aligned
 };
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(kThreads) void map_to_topk_kernel(MapArgs g) {
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  uint32_t fl = 0;
-  if (t < g.n) {
+  const int lpt = g.lpt;
+  const int sl = threadIdx.x & (lpt - 1);  // lane within the token's group
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * (kThreads / lpt) + threadIdx.x / lpt;
+  const bool live = t < g.n;
+  const int e0 = sl * kLaneExperts;  // this lane's experts e0 .. e0+15
+  uint32_t nz = 0;                   // bit i: expert e0 + i is routed
+  if (live && e0 < g.e) {
     const uint8_t *row = g.map + t * g.e;
+    if (g.vec) {  // E % 16 == 0, so e0 + 16 <= E
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(row + e0);
+      const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < kLaneExperts; ++i)
+        nz |= ((wd[i / 4] >> (8 * (i % 4))) & 0xFFu) != 0 ? 1u << i : 0u;
+    } else {
+      uint8_t b[kLaneExperts];
+#pragma unroll
+      for (int i = 0; i < kLaneExperts; ++i) b[i] = e0 + i < g.e ? row[e0 + i] : 0;
+#pragma unroll
+      for (int i = 0; i < kLaneExperts; ++i) nz |= b[i] != 0 ? 1u << i : 0u;
+    }
+  }
+  // routed experts before this lane's, and in the whole row
+  const int cnt = __popc(nz);
+  int inc = cnt;
+  for (int d = 1; d < lpt; d <<= 1) {
+    const int v = __shfl_up(inc, d, lpt);
+    if (sl >= d) inc += v;
+  }
+  const int total = __shfl(inc, lpt - 1, lpt);
+  const uint32_t fl = live && total > g.k ? MOE_STATUS_MAP_OVERFLOW : 0u;
+  if (live) {
     int32_t *ids = g.ids + t * g.k;
     float *w = g.w ? g.w + t * g.k : nullptr;
     const float *pr = g.probs ? g.probs + t * g.e : nullptr;
-    int used = 0;
-    for (int e0 = 0; e0 < g.e && fl == 0; e0 += 16) {
-      uint8_t b[16];
-      if (g.vec) {
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(row + e0);
-        const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int i = 0; i < 16; ++i) b[i] = static_cast<uint8_t>(wd[i / 4] >> (8 * (i % 4)));
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) b[i] = e0 + i < g.e ? row[e0 + i] : 0;
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        if (b[i] == 0 || fl != 0) continue;
-        if (used == g.k) {
-          fl = MOE_STATUS_MAP_OVERFLOW;
-          continue;
-        }
-        ids[used] = e0 + i;
-        if (w) w[used] = pr ? pr[e0 + i] : 1.0f;
-        ++used;
+    int pos = inc - cnt;
+    // the ascending experts of this lane that still fit: probabilities
+    // loaded together first, then every store
+    uint32_t keep = 0;
+    {
+      uint32_t m = nz;
+      for (int p = pos; m != 0 && p < g.k; ++p) {
+        keep |= m & (~m + 1u);
+        m &= m - 1u;
       }
     }
-    for (int j = used; j < g.k; ++j) {
+    float pv[kLaneExperts];
+#pragma unroll
+    for (int i = 0; i < kLaneExperts; ++i) pv[i] = (w && pr && ((keep >> i) & 1u)) ? pr[e0 + i] : 1.0f;
+#pragma unroll
+    for (int i = 0; i < kLaneExperts; ++i) {
+      if ((keep >> i) & 1u) {
+        ids[pos] = e0 + i;
+        if (w) w[pos] = pv[i];
+        ++pos;
+      }
+    }
+    for (int j = total + sl; j < g.k; j += lpt) {
       ids[j] = -1;
       if (w) w[j] = 0.0f;
     }
@@ -100,7 +133,18 @@ __global__ __launch_bounds__(kThreads) void map_status_kernel(MapArgs g) {
   if (threadIdx.x == 0) *g.status = s_fl;
 }
 
-int map_blocks(const moe_problem &p) { return static_cast<int>((p.n_tokens + kThreads - 1) / kThreads); }
+// lanes per token: ceil(E / 16) rounded up to a power of two (E <= 1024)
+int lanes_per_token(int e) {
+  const int need = (e + kLaneExperts - 1) / kLaneExperts;
+  int lpt = 1;
+  while (lpt < need) lpt <<= 1;
+  return lpt;
+}
+
+int map_blocks(const moe_problem &p) {
+  const int64_t per = kThreads / lanes_per_token(p.n_experts);
+  return static_cast<int>((p.n_tokens + per - 1) / per);
+}
 
 }  // namespace
 
@@ -122,6 +166,7 @@ hipError_t launch_routing_map_to_topk(const moe_problem &p, const uint8_t *map, 
   g.n = p.n_tokens;
   g.e = p.n_experts;
   g.k = p.top_k;
+  g.lpt = lanes_per_token(p.n_experts);
   g.nblocks = map_blocks(p);
   g.vec = p.n_experts % 16 == 0 && (reinterpret_cast<uintptr_t>(map) & 15) == 0;
   if (g.nblocks > 0) map_to_topk_kernel<<<g.nblocks, kThreads, 0, stream>>>(g);
