@@ -147,6 +147,15 @@ class Path:
         if ev is not None:
             ev[3].record()
 
+    def step_one_launch(self, i):
+        """The same step with the plan and the dispatch in one call (one launch
+        for problems of at most 2048 pairs)."""
+        s = self.sets[i % len(self.sets)]
+        gs = self.gs if self.w.fmt == "nvfp4" else None
+        self.moe.moe_plan_and_dispatch(self.p, s["ids"], s["plan"], s["x"], s["payload"],
+                                       s["scales"], input_scale=gs)
+        self.moe.moe_combine(self.p, s["plan"], s["y"], s["w"], s["out"])
+
     def r_used(self):
         return int(self.sets[0]["plan"].expert_offsets[-1].item())
 
@@ -214,6 +223,16 @@ class ExchangePath:
         return self.r_used()
 
 
+class _SameSet:
+    """A path whose every step uses the first buffer set."""
+
+    def __init__(self, path):
+        self.path = path
+
+    def step(self, i, ev=None):
+        self.path.step(0, ev)
+
+
 def time_steps(torch, path, steps, warmup):
     for i in range(warmup):
         path.step(i)
@@ -271,10 +290,21 @@ def decode_latency(moe, torch, w, inp, iters=200, per_graph=16):
     """µs per plan + dispatch + combine at the decode shape, three ways:
     back-to-back calls from Python (host-bound: each call costs a few µs of
     Python and ctypes), one HIP graph per step, and one HIP graph holding
-    `per_graph` steps (closest to the GPU's own time per step)."""
+    `per_graph` steps (closest to the GPU's own time per step).  For a single
+    packed buffer the same is reported with the plan and the dispatch in one
+    call (``one_launch_plan_dispatch``)."""
     path = (ExchangePath if w.exchange else Path)(moe, torch, w, inp, copies=1)
+    out = dict(workload=w.name)
+    out.update(_latencies(torch, path, lambda: path.step(0), iters, per_graph))
+    if isinstance(path, Path) and not path.expert_cap:
+        out["one_launch_plan_dispatch"] = _latencies(torch, path, lambda: path.step_one_launch(0),
+                                                     iters, per_graph)
+    return out
+
+
+def _latencies(torch, path, step, iters, per_graph):
     for i in range(20):
-        path.step(0)
+        step()
     torch.cuda.synchronize()
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
@@ -289,22 +319,21 @@ def decode_latency(moe, torch, w, inp, iters=200, per_graph=16):
         torch.cuda.synchronize()
         return s.elapsed_time(e) / reps * 1e3
 
-    plain = clock(lambda: path.step(0), iters)
+    plain = clock(step, iters)
     ref = path.sets[0]["out"].clone()
     graphs = {}
     for n in (1, per_graph):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for _ in range(n):
-                path.step(0)
+                step()
         graphs[n] = (g, clock(g.replay, max(iters // n, 10)) / n)
     # every replay recomputes the same output as the eager path
     path.sets[0]["out"].zero_()
     graphs[per_graph][0].replay()
     torch.cuda.synchronize()
     same = bool(torch.equal(ref.view(torch.int16), path.sets[0]["out"].view(torch.int16)))
-    out = dict(workload=w.name, us_per_step_python_launch=round(plain, 2),
-               us_per_step_graph=round(graphs[1][1], 2))
+    out = dict(us_per_step_python_launch=round(plain, 2), us_per_step_graph=round(graphs[1][1], 2))
     out[f"us_per_step_graph_x{per_graph}"] = round(graphs[per_graph][1], 2)
     out["graph_matches_eager"] = same
     return out
@@ -439,6 +468,9 @@ def main():
 
     ms, wall = time_steps(torch, path, args.steps, args.warmup)
     log(f"[bench] timed {args.steps} steps: {ms * 1e3:.2f} us/step (wall {wall:.3f} s)")
+    # context: the same buffer set every step, so inputs may stay in the caches
+    warm_ms, _ = time_steps(torch, _SameSet(path), args.steps, args.warmup)
+    log(f"[bench] warm (one buffer set): {warm_ms * 1e3:.2f} us/step")
     kt = time_kernels(torch, path, args.steps)
     log(f"[bench] per-kernel means (us): plan {kt['plan'] * 1e3:.2f} dispatch "
         f"{kt['dispatch'] * 1e3:.2f} combine {kt['combine'] * 1e3:.2f}")
@@ -509,6 +541,7 @@ def main():
         "frac_of_peak": round(value / PEAK_HBM_GBPS, 4),
         "bytes_per_step": b,
         "payload_only": payload_only,
+        "warm_us_per_step": round(warm_ms * 1e3, 2),
         "kernel_us": {k: round(v * 1e3, 2) for k, v in kt.items()},
         "roofline": roofline,
         "cpu_baseline": cpu,

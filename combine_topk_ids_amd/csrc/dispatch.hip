@@ -30,6 +30,7 @@
 // buffer (NKI permute_a2av API reference, :return:).
 #include "moe_device.hpp"
 #include "moe_kernels.hpp"
+#include "small_plan.hpp"
 
 namespace moe {
 namespace {
@@ -116,19 +117,69 @@ __device__ __forceinline__ int lane_slot(const DispatchArgs &g, int64_t t, int l
 // ---- bf16: copy the slab to every destination -------------------------------
 constexpr int kBf16Vec = MOE_DISPATCH_VEC;  // 16-byte vectors per lane per slab
 
+// quantising formats: each lane encodes LE consecutive values
+constexpr int kLE = MOE_QUANT_LANE_ELEMS;           // 8 or 16
+constexpr int kQC = MOE_QUANT_CHUNKS;               // chunks of kWave*kLE per wave
+constexpr int kQuantSlab = kWave * kLE * kQC;       // values per wave
+static_assert(kLE == 8 || kLE == 16, "8 or 16 values per lane");
+
+// What one lane of a token wave reads: its 16-byte vectors of the slab
+// (zeros past the row end) and, for gated copies, its gate (lane j holds
+// the gate of pair (t, j)).  Loading is separate from encoding and storing
+// so that a caller can issue these loads before other work.
+constexpr int kRawVec = kBf16Vec > kQC * kLE / 8 ? kBf16Vec : kQC * kLE / 8;
+struct RawSlab {
+  u32x4 v[kRawVec];
+  float w;
+};
+
+template <int FMT, bool GATED>
+__device__ __forceinline__ RawSlab load_slab(const DispatchArgs &g, int64_t t, int slab) {
+  const int lane = lane_id();
+  const u32x4 *row = reinterpret_cast<const u32x4 *>(g.x + t * g.h);
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  RawSlab r;
+  if (FMT == MOE_FMT_BF16) {
+    const int nvec = g.h / 8;
+    const int v0 = slab * kWave * kBf16Vec;
+#pragma unroll
+    for (int u = 0; u < kBf16Vec; ++u) {
+      const int idx = v0 + u * kWave + lane;
+      r.v[u] = idx < nvec ? __builtin_nontemporal_load(row + idx) : zero;
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < kQC; ++c) {
+      const int elem = slab * kQuantSlab + c * kWave * kLE + lane * kLE;
+#pragma unroll
+      for (int q = 0; q < kLE / 8; ++q)
+        r.v[c * (kLE / 8) + q] = elem < g.h ? __builtin_nontemporal_load(row + elem / 8 + q) : zero;
+    }
+  }
+  r.w = GATED && lane < g.k ? g.w[t * g.k + lane] : 0.0f;
+  return r;
+}
+
+// Chunk c of this lane's values as fp32.
+__device__ __forceinline__ void unpack_lane(const RawSlab &r, int c, float (&f)[kLE]) {
+#pragma unroll
+  for (int q = 0; q < kLE / 8; ++q) {
+    const u32x4 v = r.v[c * (kLE / 8) + q];
+    uint4 r4;
+    r4.x = v.x; r4.y = v.y; r4.z = v.z; r4.w = v.w;
+    float h[8];
+    unpack8(r4, h);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[q * 8 + i] = h[i];
+  }
+}
+
 template <bool NT>
-__device__ void slab_bf16(const DispatchArgs &g, int64_t t, int slab) {
+__device__ void slab_bf16(const DispatchArgs &g, int slab, int my_slot, const RawSlab &r) {
   const int lane = lane_id();
   const int nvec = g.h / 8;
   const int v0 = slab * kWave * kBf16Vec;
-  const u32x4 *src = reinterpret_cast<const u32x4 *>(g.x + t * g.h);
-  const int my_slot = lane_slot(g, t, lane);
-  u32x4 buf[kBf16Vec];
-#pragma unroll
-  for (int u = 0; u < kBf16Vec; ++u) {
-    const int idx = v0 + u * kWave + lane;
-    if (idx < nvec) buf[u] = __builtin_nontemporal_load(src + idx);
-  }
+  const u32x4 *buf = r.v;
   for (int j = 0; j < g.k; ++j) {
     const int s = __builtin_amdgcn_readlane(my_slot, j);
     if (s < 0) continue;
@@ -141,29 +192,7 @@ __device__ void slab_bf16(const DispatchArgs &g, int64_t t, int slab) {
   }
 }
 
-// ---- quantising formats: each lane encodes LE consecutive values ----------
-constexpr int kLE = MOE_QUANT_LANE_ELEMS;           // 8 or 16
-constexpr int kQC = MOE_QUANT_CHUNKS;               // chunks of kWave*kLE per wave
-constexpr int kQuantSlab = kWave * kLE * kQC;       // values per wave
-static_assert(kLE == 8 || kLE == 16, "8 or 16 values per lane");
-
-// Load this lane's LE bf16 values (zeros past the row end) as fp32.
-__device__ __forceinline__ void load_lane(const DispatchArgs &g, int64_t t, int elem, float (&f)[kLE]) {
-  const u32x4 *src = reinterpret_cast<const u32x4 *>(g.x + t * g.h) + elem / 8;
-  u32x4 raw[kLE / 8];
-#pragma unroll
-  for (int q = 0; q < kLE / 8; ++q)
-    raw[q] = elem < g.h ? __builtin_nontemporal_load(src + q) : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int q = 0; q < kLE / 8; ++q) {
-    uint4 r4;
-    r4.x = raw[q].x; r4.y = raw[q].y; r4.z = raw[q].z; r4.w = raw[q].w;
-    float h[8];
-    unpack8(r4, h);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) f[q * 8 + i] = h[i];
-  }
-}
+// ---- quantising formats -------------------------------------------------------
 
 __device__ __forceinline__ uint32_t lane_absmax(const float (&f)[kLE]) {
   uint32_t am = 0;
@@ -174,12 +203,11 @@ __device__ __forceinline__ uint32_t lane_absmax(const float (&f)[kLE]) {
 
 // ---- FP8 E4M3, one fp32 scale per 1x128 block -------------------------------
 template <bool NT>
-__device__ void slab_fp8(const DispatchArgs &g, int64_t t, int slab) {
+__device__ void slab_fp8(const DispatchArgs &g, int slab, int my_slot, const RawSlab &r) {
   const int lane = lane_id();
-  const int my_slot = lane_slot(g, t, lane);
   float f[kQC][kLE];
 #pragma unroll
-  for (int c = 0; c < kQC; ++c) load_lane(g, t, slab * kQuantSlab + c * kWave * kLE + lane * kLE, f[c]);
+  for (int c = 0; c < kQC; ++c) unpack_lane(r, c, f[c]);
   uint32_t w[kQC][kLE / 4];
   float sc[kQC];
 #pragma unroll
@@ -230,12 +258,11 @@ __device__ void slab_fp8(const DispatchArgs &g, int64_t t, int slab) {
 
 // ---- MX-FP4: E2M1 codes, one E8M0 scale per 32 values -----------------------
 template <bool NT>
-__device__ void slab_mx(const DispatchArgs &g, int64_t t, int slab) {
+__device__ void slab_mx(const DispatchArgs &g, int slab, int my_slot, const RawSlab &r) {
   const int lane = lane_id();
-  const int my_slot = lane_slot(g, t, lane);
   float f[kQC][kLE];
 #pragma unroll
-  for (int c = 0; c < kQC; ++c) load_lane(g, t, slab * kQuantSlab + c * kWave * kLE + lane * kLE, f[c]);
+  for (int c = 0; c < kQC; ++c) unpack_lane(r, c, f[c]);
   uint32_t w[kQC][kLE / 8];
   uint8_t sbyte[kQC];
 #pragma unroll
@@ -280,13 +307,12 @@ __device__ void slab_mx(const DispatchArgs &g, int64_t t, int slab) {
 // * gs), saturated at 448 (the hardware conversion is exact below 464), and
 // codes E2M1(fl32(fl32(x * gs) / value(sf))) with IEEE division.
 template <bool NT>
-__device__ void slab_nvfp4(const DispatchArgs &g, int64_t t, int slab) {
+__device__ void slab_nvfp4(const DispatchArgs &g, int slab, int my_slot, const RawSlab &r) {
   static_assert(kLE == 8 && kQC == 1, "a 16-value block is one lane pair");
   const int lane = lane_id();
-  const int my_slot = lane_slot(g, t, lane);
   const int elem = slab * kQuantSlab + lane * kLE;
   float f[kLE];
-  load_lane(g, t, elem, f);
+  unpack_lane(r, 0, f);
   uint32_t am = lane_absmax(f);
   am = max(am, dpp<kQuadSwap1>(am));
   const float gs = *g.gscale;
@@ -317,28 +343,17 @@ __device__ void slab_nvfp4(const DispatchArgs &g, int64_t t, int slab) {
 // block maximum of the products needs no new reduction: rounding is
 // monotone, so max |fl32(w x_i)| = fl32(|w| max |x_i|).
 
-__device__ __forceinline__ float lane_gate(const DispatchArgs &g, int64_t t, int lane) {
-  return lane < g.k ? g.w[t * g.k + lane] : 0.0f;
-}
-
 __device__ __forceinline__ float bcast(float v, int j) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), j));
 }
 
 template <bool NT>
-__device__ void slab_bf16_gated(const DispatchArgs &g, int64_t t, int slab) {
+__device__ void slab_bf16_gated(const DispatchArgs &g, int slab, int my_slot, const RawSlab &r) {
   const int lane = lane_id();
   const int nvec = g.h / 8;
   const int v0 = slab * kWave * kBf16Vec;
-  const u32x4 *src = reinterpret_cast<const u32x4 *>(g.x + t * g.h);
-  const int my_slot = lane_slot(g, t, lane);
-  const float my_w = lane_gate(g, t, lane);
-  u32x4 buf[kBf16Vec];
-#pragma unroll
-  for (int u = 0; u < kBf16Vec; ++u) {
-    const int idx = v0 + u * kWave + lane;
-    if (idx < nvec) buf[u] = __builtin_nontemporal_load(src + idx);
-  }
+  const float my_w = r.w;
+  const u32x4 *buf = r.v;
   for (int j = 0; j < g.k; ++j) {
     const int s = __builtin_amdgcn_readlane(my_slot, j);
     if (s < 0) continue;
@@ -367,14 +382,13 @@ __device__ void slab_bf16_gated(const DispatchArgs &g, int64_t t, int slab) {
 // v = fl32(w x), with IEEE division (the reciprocal shortcut of the ungated
 // path is exact only for the bf16 values it was checked on).
 template <bool NT>
-__device__ void slab_fp8_gated(const DispatchArgs &g, int64_t t, int slab) {
+__device__ void slab_fp8_gated(const DispatchArgs &g, int slab, int my_slot, const RawSlab &r) {
   static_assert(kQC == 1, "gated encoders take one chunk per wave");
   const int lane = lane_id();
-  const int my_slot = lane_slot(g, t, lane);
-  const float my_w = lane_gate(g, t, lane);
+  const float my_w = r.w;
   const int elem = slab * kQuantSlab + lane * kLE;
   float f[kLE];
-  load_lane(g, t, elem, f);
+  unpack_lane(r, 0, f);
   uint32_t am = quad_max(lane_absmax(f));
   am = max(am, dpp<kRowHalfMirror>(am));
   if (kLE == 8) am = max(am, dpp<kRowMirror>(am));
@@ -411,14 +425,13 @@ __device__ void slab_fp8_gated(const DispatchArgs &g, int64_t t, int slab) {
 
 // MX-FP4: per copy X from fl32(|w| amax), codes E2M1(fl32(w x) * 2^-X).
 template <bool NT>
-__device__ void slab_mx_gated(const DispatchArgs &g, int64_t t, int slab) {
+__device__ void slab_mx_gated(const DispatchArgs &g, int slab, int my_slot, const RawSlab &r) {
   static_assert(kQC == 1, "gated encoders take one chunk per wave");
   const int lane = lane_id();
-  const int my_slot = lane_slot(g, t, lane);
-  const float my_w = lane_gate(g, t, lane);
+  const float my_w = r.w;
   const int elem = slab * kQuantSlab + lane * kLE;
   float f[kLE];
-  load_lane(g, t, elem, f);
+  unpack_lane(r, 0, f);
   uint32_t am = lane_absmax(f);
   am = max(am, dpp<kQuadSwap1>(am));
   if (kLE == 8) am = max(am, dpp<kQuadSwap2>(am));
@@ -496,10 +509,25 @@ __device__ void zero_tails(const DispatchArgs &g, int blk, int wave) {
   }
 }
 
+// Encode a loaded slab and store it to the token's k packed rows.
 template <int FMT, bool NT, bool GATED>
-__global__ __launch_bounds__(kThreads) void dispatch_kernel(DispatchArgs g) {
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  int blk = blockIdx.x;
+__device__ __forceinline__ void emit_slab(const DispatchArgs &g, int slab, int my_slot, const RawSlab &r) {
+  if (GATED) {  // not instantiated for NVFP4 (the host rejects it)
+    if (FMT == MOE_FMT_BF16) slab_bf16_gated<NT>(g, slab, my_slot, r);
+    else if (FMT == MOE_FMT_FP8_E4M3_B128) slab_fp8_gated<NT>(g, slab, my_slot, r);
+    else slab_mx_gated<NT>(g, slab, my_slot, r);
+  } else {
+    if (FMT == MOE_FMT_BF16) slab_bf16<NT>(g, slab, my_slot, r);
+    else if (FMT == MOE_FMT_FP8_E4M3_B128) slab_fp8<NT>(g, slab, my_slot, r);
+    else if (FMT == MOE_FMT_NVFP4_B16) slab_nvfp4<NT>(g, slab, my_slot, r);
+    else slab_mx<NT>(g, slab, my_slot, r);
+  }
+}
+
+// The three workgroup ranges of a dispatch launch: token slabs, pad rows,
+// zero tails.  `blk` < token_blocks + pad_blocks + tail_blocks.
+template <int FMT, bool NT, bool GATED>
+__device__ __forceinline__ void dispatch_body(const DispatchArgs &g, int blk, int wave) {
   if (MOE_TAIL_FIRST) {
     if (blk < g.tail_blocks) {
       zero_tails<NT || MOE_TAIL_NT>(g, blk, wave);
@@ -513,16 +541,10 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(DispatchArgs g) {
     const int t = q / g.slabs;
     if (t >= g.n) return;
     const int slab = q - t * g.slabs;
-    if (GATED) {  // not instantiated for NVFP4 (the host rejects it)
-      if (FMT == MOE_FMT_BF16) slab_bf16_gated<NT>(g, t, slab);
-      else if (FMT == MOE_FMT_FP8_E4M3_B128) slab_fp8_gated<NT>(g, t, slab);
-      else slab_mx_gated<NT>(g, t, slab);
-    } else {
-      if (FMT == MOE_FMT_BF16) slab_bf16<NT>(g, t, slab);
-      else if (FMT == MOE_FMT_FP8_E4M3_B128) slab_fp8<NT>(g, t, slab);
-      else if (FMT == MOE_FMT_NVFP4_B16) slab_nvfp4<NT>(g, t, slab);
-      else slab_mx<NT>(g, t, slab);
-    }
+    // the token's slots (one per lane) and the slab: one round trip
+    const int my_slot = lane_slot(g, t, lane_id());
+    const RawSlab r = load_slab<FMT, GATED>(g, t, slab);
+    emit_slab<FMT, NT, GATED>(g, slab, my_slot, r);
     return;
   }
   blk -= g.token_blocks;
@@ -542,6 +564,113 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(DispatchArgs g) {
   }
   blk -= g.pad_blocks;
   if (!MOE_TAIL_FIRST) zero_tails<NT || MOE_TAIL_NT>(g, blk, wave);
+}
+
+template <int FMT, bool NT, bool GATED>
+__global__ __launch_bounds__(kThreads) void dispatch_kernel(DispatchArgs g) {
+  dispatch_body<FMT, NT, GATED>(g, blockIdx.x, __builtin_amdgcn_readfirstlane(threadIdx.x / kWave));
+}
+
+// ---- plan and dispatch in one launch (at most kSmallPairs pairs) ----------
+// Every workgroup issues the loads of the IDs and of its token slabs, then
+// computes in LDS the part of the plan it needs (small_plan.hpp) while the
+// slabs arrive, and encodes and stores its slabs with the slots it found.
+// Workgroup 0 writes the counts, offsets, table and status; the wave that
+// holds slab 0 of a token writes that token's slots and packed_src rows;
+// all workgroups stride over the pad and tail rows of packed_src; the
+// workgroups past the token range zero pad and tail rows as in dispatch.
+struct PlanDispatchArgs {
+  DispatchArgs d;       // plan pointers are replaced by LDS in the kernel
+  SmallPlanArgs sp;
+  int32_t *counts, *offsets, *dest_counts, *slot, *packed_src;
+  uint32_t *table, *status;
+  uint32_t h;           // elements per row, for the table
+  int r_max;
+  int dispatch_blocks;  // workgroups of the three dispatch ranges
+};
+
+static_assert(kThreads == kSmallThreads, "one small plan per dispatch workgroup");
+static_assert(MOE_TAIL_FIRST == 0, "the one-launch kernel places the token workgroups first");
+
+template <int FMT, bool NT, bool GATED>
+__global__ __launch_bounds__(kThreads) void plan_dispatch_kernel(PlanDispatchArgs g) {
+  extern __shared__ int smem[];
+  const int E = g.sp.e, k = g.sp.k, np = g.sp.n * g.sp.k;
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const DispatchArgs &d = g.d;
+  const SmallPlanLds s = small_plan_lds(smem, E);
+
+  // the IDs, then this wave's token slab: all loads in flight during the plan
+  int v[kSmallLoads];
+  small_plan_load(g.sp, v);
+  const bool tok = b < d.token_blocks;
+  const int blk = tok && FMT != MOE_FMT_BF16 ? xcd_local_block(b, d.token_blocks) : b;
+  const int q = blk * kWaves + wave;  // the grid size keeps q within int
+  const int t = tok ? q / d.slabs : 0;
+  const int slab = q - t * d.slabs;
+  const bool live = tok && t < g.sp.n;
+  RawSlab r{};
+  if (live) r = load_slab<FMT, GATED>(d, t, slab);
+  // the workgroup's own pairs: every pair of its (at most kWaves) tokens
+  int p0 = 0, p1 = 0;
+  if (tok) {
+    const int t0 = (blk * kWaves) / d.slabs;
+    const int t1 = min(g.sp.n - 1, (blk * kWaves + kWaves - 1) / d.slabs);
+    if (t0 < g.sp.n) {
+      p0 = t0 * k;
+      p1 = (t1 + 1) * k;
+    }
+  }
+  const uint32_t fl = small_plan(g.sp, s, v, p0, p1, b == 0);
+
+  if (b == 0) {
+    for (int e = tid; e < E; e += kThreads) {
+      g.counts[e] = s.cnt[e];
+      g.offsets[e] = s.off[e];
+    }
+    if (tid == 0) {
+      g.offsets[E] = s.off[E];
+      *g.status = fl;
+    }
+    const int L = E / g.sp.ep;
+    for (int rk = tid; rk < g.sp.ep; rk += kThreads) {
+      const int lo = rk * L, hi = lo + L;
+      const int S = s.cpre[hi] - s.cpre[lo];
+      g.dest_counts[rk] = S;
+      g.table[rk] = static_cast<uint32_t>(S) * g.h;
+      g.table[g.sp.ep + rk] = static_cast<uint32_t>(s.cpre[lo]) * g.h;
+      g.table[2 * g.sp.ep + rk] = static_cast<uint32_t>(s.off[hi] - s.off[lo]) * g.h;
+      g.table[3 * g.sp.ep + rk] = static_cast<uint32_t>(s.off[lo]) * g.h;
+    }
+  }
+  // a token's slots and packed_src rows: written by the wave of its slab 0
+  const int my_slot = live && lane < k ? s.tslot[t * k + lane - p0] : -1;
+  if (live && slab == 0 && lane < k) {
+    g.slot[t * k + lane] = my_slot;
+    if (my_slot >= 0) g.packed_src[my_slot] = t;
+  }
+  // packed_src = -1 on the unused rows of each expert and on the tail
+  const int stride = gridDim.x * kThreads;
+  const int per = g.sp.a - 1;
+  for (int qq = b * kThreads + tid; qq < E * per; qq += stride) {
+    const int e = qq / per;
+    const int row = s.off[e] + s.cnt[e] + (qq - e * per);
+    if (row < s.off[e + 1]) g.packed_src[row] = -1;
+  }
+  for (int row = s.off[E] + b * kThreads + tid; row < g.r_max; row += stride) g.packed_src[row] = -1;
+
+  if (live) {
+    emit_slab<FMT, NT, GATED>(d, slab, my_slot, r);
+  } else if (!tok && b < g.dispatch_blocks) {
+    // pad and tail ranges, reading the plan from LDS
+    DispatchArgs dp = d;
+    dp.counts = s.cnt;
+    dp.offsets = s.off;
+    dp.seg_used = s.off + E;
+    dispatch_body<FMT, NT, GATED>(dp, b, wave);
+  }
 }
 
 template <int FMT>
@@ -598,16 +727,16 @@ hipError_t launch_args(const DispatchArgs &g, int fmt, hipStream_t stream) {
   return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_dispatch(const moe_problem &p, const moe_plan &plan, const uint16_t *hidden,
-                           const float *gates, const float *gscale, void *payload, void *scales,
-                           hipStream_t stream) {
-  DispatchArgs g = base_args(p, p.n_tokens, plan.slot, hidden, payload, scales);
+// Dispatch into one packed buffer, with the plan at `slot`, `counts` and
+// `offsets` (device memory, or LDS inside the one-launch kernel).
+DispatchArgs single_buffer_args(const moe_problem &p, const int32_t *slot, const int32_t *counts,
+                                const int32_t *offsets, const uint16_t *hidden, const float *gates,
+                                const float *gscale, void *payload, void *scales) {
+  DispatchArgs g = base_args(p, p.n_tokens, slot, hidden, payload, scales);
   g.w = gates;
   g.gscale = gscale;
-  g.counts = plan.expert_counts;
-  g.offsets = plan.expert_offsets;
+  g.counts = counts;
+  g.offsets = offsets;
   g.r_max = max_rows(p);
   // unused rows per expert: fewer than A with padding, up to cap with a fixed
   // capacity (rows [offsets[e] + counts[e], offsets[e+1]) either way)
@@ -615,11 +744,66 @@ hipError_t launch_dispatch(const moe_problem &p, const moe_plan &plan, const uin
   const int pad_groups = static_cast<int>((pad_span + kPadRowsPerWave - 1) / kPadRowsPerWave);
   g.pad_blocks = pad_groups == 0 ? 0 : (p.n_experts * pad_groups + kWaves - 1) / kWaves;
   if (pad_groups > 0) g.pad_groups = pad_groups;
-  g.seg_used = plan.expert_offsets + p.n_experts;  // R_used
+  g.seg_used = offsets ? offsets + p.n_experts : nullptr;  // R_used
   g.nseg = 1;
   g.seg_rows = g.r_max;
   g.tail_blocks = (p.flags & MOE_FLAG_ZERO_TAIL) && g.r_max > 0 ? kTailBlocks : 0;
+  return g;
+}
+
+template <int FMT>
+void launch_plan_dispatch_fmt(const PlanDispatchArgs &g, int grid, size_t lds, hipStream_t stream) {
+  constexpr bool kNT = MOE_DISPATCH_NT_STORE != 0;
+  if (FMT != MOE_FMT_NVFP4_B16 && g.d.w)
+    plan_dispatch_kernel<FMT, kNT, FMT != MOE_FMT_NVFP4_B16><<<grid, kThreads, lds, stream>>>(g);
+  else
+    plan_dispatch_kernel<FMT, kNT, false><<<grid, kThreads, lds, stream>>>(g);
+}
+
+}  // namespace
+
+hipError_t launch_dispatch(const moe_problem &p, const moe_plan &plan, const uint16_t *hidden,
+                           const float *gates, const float *gscale, void *payload, void *scales,
+                           hipStream_t stream) {
+  const DispatchArgs g = single_buffer_args(p, plan.slot, plan.expert_counts, plan.expert_offsets,
+                                            hidden, gates, gscale, payload, scales);
   return launch_args(g, p.fmt, stream);
+}
+
+bool plan_dispatch_fits(const moe_problem &p) {
+  return p.n_tokens * p.top_k <= kSmallPairs && p.expert_capacity == 0;
+}
+
+hipError_t launch_plan_dispatch(const moe_problem &p, const int32_t *ids, const moe_plan &plan,
+                                const uint16_t *hidden, const float *gates, const float *gscale,
+                                void *payload, void *scales, hipStream_t stream) {
+  PlanDispatchArgs g{};
+  // plan pointers are taken from LDS inside the kernel
+  g.d = single_buffer_args(p, nullptr, nullptr, nullptr, hidden, gates, gscale, payload, scales);
+  g.sp.ids = ids;
+  g.sp.n = static_cast<int>(p.n_tokens);
+  g.sp.k = p.top_k;
+  g.sp.e = p.n_experts;
+  g.sp.ep = p.ep;
+  g.sp.a = p.pad_multiple;
+  g.sp.cap = p.recv_capacity;
+  g.counts = plan.expert_counts;
+  g.offsets = plan.expert_offsets;
+  g.dest_counts = plan.dest_counts;
+  g.slot = plan.slot;
+  g.packed_src = plan.packed_src;
+  g.table = plan.rank_table;
+  g.status = plan.status;
+  g.h = static_cast<uint32_t>(p.hidden);
+  g.r_max = static_cast<int>(max_rows(p));
+  g.dispatch_blocks = g.d.token_blocks + g.d.pad_blocks + g.d.tail_blocks;
+  const int grid = max(g.dispatch_blocks, 1);  // N = 0 still writes the plan
+  const size_t lds = small_plan_lds_bytes(p.n_experts);
+  if (p.fmt == MOE_FMT_BF16) launch_plan_dispatch_fmt<MOE_FMT_BF16>(g, grid, lds, stream);
+  else if (p.fmt == MOE_FMT_FP8_E4M3_B128) launch_plan_dispatch_fmt<MOE_FMT_FP8_E4M3_B128>(g, grid, lds, stream);
+  else if (p.fmt == MOE_FMT_NVFP4_B16) launch_plan_dispatch_fmt<MOE_FMT_NVFP4_B16>(g, grid, lds, stream);
+  else launch_plan_dispatch_fmt<MOE_FMT_MXFP4_B32>(g, grid, lds, stream);
+  return hipGetLastError();
 }
 
 hipError_t launch_exchange_dispatch(const moe_problem &p, const moe_exchange &x, const uint16_t *hidden,

@@ -73,6 +73,12 @@ hipError_t launch_dispatch(const moe_problem &p, const moe_plan &plan, const uin
                            const float *gates, const float *gscale, void *payload, void *scales,
                            hipStream_t stream);
 
+// Plan and dispatch in one launch; only where plan_dispatch_fits(p).
+bool plan_dispatch_fits(const moe_problem &p);
+hipError_t launch_plan_dispatch(const moe_problem &p, const int32_t *ids, const moe_plan &plan,
+                                const uint16_t *hidden, const float *gates, const float *gscale,
+                                void *payload, void *scales, hipStream_t stream);
+
 hipError_t launch_combine(const moe_problem &p, const moe_plan &plan, const uint16_t *expert_out,
                           const float *weights, uint16_t *out, hipStream_t stream);
 

@@ -27,7 +27,8 @@ FLAG_ZERO_TAIL = 1
 # every symbol include/moe.h declares
 EXPORTS = ("moe_check_problem", "moe_max_rows", "moe_expert_capacity", "moe_payload_row_bytes",
            "moe_scale_row_bytes", "moe_workspace_bytes", "moe_dispatch_plan",
-           "moe_dispatch", "moe_dispatch_scaled", "moe_dispatch_gated", "moe_combine",
+           "moe_dispatch", "moe_dispatch_scaled", "moe_dispatch_gated", "moe_plan_and_dispatch",
+           "moe_combine",
            "moe_check_exchange", "moe_exchange_workspace_bytes", "moe_exchange_plan",
            "moe_exchange_dispatch", "moe_exchange_dispatch_scaled", "moe_exchange_dispatch_gated",
            "moe_exchange_combine", "moe_map_workspace_bytes",
@@ -78,6 +79,7 @@ def _load() -> ctypes.CDLL:
         "moe_dispatch_plan": (ctypes.c_int, [P, V, ctypes.POINTER(Plan), V, V]),
         "moe_dispatch": (ctypes.c_int, [P, ctypes.POINTER(Plan), V, V, V, V]),
         "moe_dispatch_gated": (ctypes.c_int, [P, ctypes.POINTER(Plan), V, V, V, V, V]),
+        "moe_plan_and_dispatch": (ctypes.c_int, [P, V, ctypes.POINTER(Plan), V, V, V, V, V, V, V]),
         "moe_dispatch_scaled": (ctypes.c_int, [P, ctypes.POINTER(Plan), V, V, V, V, V]),
         "moe_exchange_dispatch_scaled": (ctypes.c_int, [P, ctypes.POINTER(Exchange), V, V, V, V, V]),
         "moe_combine": (ctypes.c_int, [P, ctypes.POINTER(Plan), V, V, V, V]),
@@ -314,6 +316,33 @@ def moe_dispatch_gated(p: Problem, plan: PlanBuffers, hidden: torch.Tensor,
     rc = lib.moe_dispatch_gated(ctypes.byref(p), ctypes.byref(plan.as_struct()), x, w, pay,
                                 sc or None, _stream(stream))
     _checked(rc, "moe_dispatch_gated")
+
+
+def moe_plan_and_dispatch(p: Problem, topk_ids: torch.Tensor, plan: PlanBuffers,
+                          hidden: torch.Tensor, payload: torch.Tensor, scales: torch.Tensor | None,
+                          topk_weights: torch.Tensor | None = None,
+                          input_scale: torch.Tensor | None = None, stream=None) -> None:
+    """moe_dispatch_plan then moe_dispatch (or the gated dispatch with
+    topk_weights, or the NVFP4 dispatch with input_scale), in one launch for
+    problems of at most 2048 pairs."""
+    r_max, pb, sb, ws = _sizes(p)
+    npairs = p.n_tokens * p.top_k
+    ids = _dev(topk_ids, "topk_ids", (torch.int32,), npairs)
+    _dev(plan.slot, "plan.slot", (torch.int32,), npairs)
+    _dev(plan.packed_src, "plan.packed_src", (torch.int32,), r_max)
+    _dev(plan.workspace, "plan.workspace", (torch.uint8,), ws)
+    x = _dev(hidden, "hidden", _BF16, p.n_tokens * p.hidden)
+    w = _dev(topk_weights, "topk_weights", (torch.float32,), npairs) or None
+    gs = _dev(input_scale, "input_scale", (torch.float32,), 1) or None
+    if payload.numel() * payload.element_size() < r_max * pb:
+        raise ValueError("payload is smaller than R_max rows")
+    if scales is not None and scales.numel() * scales.element_size() < r_max * sb:
+        raise ValueError("scales is smaller than R_max rows")
+    pay = _dev(payload, "payload", _PAYLOAD)
+    sc = _dev(scales, "scales", (torch.float32, torch.uint8))
+    rc = lib.moe_plan_and_dispatch(ctypes.byref(p), ids, ctypes.byref(plan.as_struct()), x, w, gs,
+                                   pay, sc or None, plan.workspace.data_ptr(), _stream(stream))
+    _checked(rc, "moe_plan_and_dispatch")
 
 
 def moe_combine(p: Problem, plan: PlanBuffers, expert_out: torch.Tensor,

@@ -232,6 +232,24 @@ MOE_API int moe_dispatch_gated(const moe_problem *p, const moe_plan *plan,
                                const uint16_t *hidden, const float *topk_weights,
                                void *payload, void *scales, void *stream);
 
+/* Plan and dispatch in one call: the outputs of moe_dispatch_plan followed
+ * by moe_dispatch (topk_weights NULL, input_scale NULL), moe_dispatch_gated
+ * (topk_weights = the gates) or moe_dispatch_scaled (MOE_FMT_NVFP4_B16:
+ * input_scale required, topk_weights must be NULL), byte for byte.  NKI
+ * permute_a2av API reference, description: one call computes the layout
+ * from the routing and permutes the rows into it.  Problems with at most
+ * 2048 (token, k) pairs and no fixed expert capacity run as one launch, in
+ * which every workgroup computes the plan in LDS before its share of the
+ * dispatch (decode shapes: one launch instead of two); larger ones run the
+ * plan and dispatch launches.  workspace: moe_workspace_bytes(p) bytes (none
+ * for the one-launch sizes).  Arguments, layouts and errors as in the calls
+ * it replaces. */
+MOE_API int moe_plan_and_dispatch(const moe_problem *p, const int32_t *topk_ids,
+                                  const moe_plan *plan, const uint16_t *hidden,
+                                  const float *topk_weights, const float *input_scale,
+                                  void *payload, void *scales, void *workspace,
+                                  void *stream);
+
 /* Combine: out[t][c] = bf16_rne( fp32 fused multiply-add chain, starting
  * from +0 and running over j = 0..k-1 in order, of
  * topk_weights[t][j] * expert_out[slot[t][j]][c] ), skipping slots < 0.

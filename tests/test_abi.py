@@ -109,6 +109,33 @@ def test_null_and_misaligned_pointers_rejected(moe):
     assert moe.lib.moe_combine(ctypes.byref(p), ctypes.byref(full), None, fake, fake, None) == -1
 
 
+def test_plan_and_dispatch_rejections(moe):
+    """Every call below fails its checks before anything is launched."""
+    ref = ctypes.byref
+    fake = 1 << 20
+    full = moe.Plan(*([fake] * 7))
+    p = moe.problem(64, 256, 2, 8, 4)
+    call = moe.lib.moe_plan_and_dispatch
+    # a global scale only with NVFP4, where it is required and gates are not
+    assert call(ref(p), fake, ref(full), fake, None, fake, fake, None, None, None) == -1
+    pn = moe.problem(64, 256, 2, 8, 4, fmt="nvfp4")
+    assert call(ref(pn), fake, ref(full), fake, None, None, fake, fake, None, None) == -1
+    assert call(ref(pn), fake, ref(full), fake, fake, fake, fake, fake, None, None) == -1
+    # null plan field, null ids, null hidden, scales for bf16
+    part = moe.Plan(*([fake] * 6 + [0]))
+    assert call(ref(p), fake, ref(part), fake, None, None, fake, None, None, None) == -1
+    assert call(ref(p), None, ref(full), fake, None, None, fake, None, None, None) == -1
+    assert call(ref(p), fake, ref(full), None, None, None, fake, None, None, None) == -1
+    assert call(ref(p), fake, ref(full), fake, None, None, fake, fake, None, None) == -1
+    # misaligned rows, IDs and gates
+    assert call(ref(p), fake, ref(full), fake + 8, None, None, fake, None, None, None) == -2
+    assert call(ref(p), fake + 2, ref(full), fake, None, None, fake, None, None, None) == -2
+    assert call(ref(p), fake, ref(full), fake, fake + 2, None, fake, None, None, None) == -2
+    # a problem past one launch needs the plan workspace
+    big = moe.problem(16384, 4096, 8, 128, 16, pad_multiple=128)
+    assert call(ref(big), fake, ref(full), fake, None, None, fake, None, None, None) == -1
+
+
 def test_workspace_required_only_for_multi_tile_plans(moe):
     small = moe.problem(128, 7168, 8, 256, 8)          # 1024 pairs: one block
     big = moe.problem(16384, 4096, 8, 128, 16, pad_multiple=128)

@@ -1,6 +1,7 @@
-"""HIP-graph capture of the exchange, fixed-capacity and NVFP4 paths: every
-replay, with eager work and synchronisation between replays, reproduces the
-eager outputs, and the eager outputs equal the oracle's.  (No call clears
+"""HIP-graph capture of the exchange, fixed-capacity, NVFP4 and one-launch
+plan-and-dispatch paths: every replay, with eager work and synchronisation
+between replays, reproduces the eager outputs, and the eager outputs equal
+the oracle's.  (No call clears
 memory with memset nodes; the exchange's multi-block plan keeps its scratch
 in the caller's workspace.)"""
 import numpy as np
@@ -8,7 +9,7 @@ import pytest
 import torch
 
 import oracle
-from combine_topk_ids_amd.workloads import random_bf16, random_routing
+from combine_topk_ids_amd.workloads import WORKLOADS, make_inputs, random_bf16, random_routing
 from gpu_helpers import assert_combine_close, say, to_dev_bf16, u16
 
 pytestmark = pytest.mark.gpu
@@ -115,3 +116,42 @@ def test_graph_capacity_and_nvfp4(moe):
     assert np.array_equal(payload.cpu().numpy(), pay) and np.array_equal(scales.cpu().numpy(), sc)
     ref = oracle.combine(pl["slot"], wts, (y.view(torch.int16).cpu().numpy().view(np.uint16)))
     assert_combine_close(u16(out), ref)
+
+
+def test_graph_plan_and_dispatch(moe):
+    """The one-launch plan and dispatch of a decode shape with a combine."""
+    w = WORKLOADS["decode_mxfp4_n128"]
+    say(f"[graph plan+dispatch] {w.describe()}")
+    inp = make_inputs(w, seed=1, expert_rows=oracle.max_rows(w.n, w.k, w.e, w.a))
+    p = moe.problem(w.n, w.h, w.k, w.e, w.ep, recv_capacity=w.capacity, pad_multiple=w.a,
+                    fmt=w.fmt)
+    plan = moe.alloc_plan(p)
+    payload, scales = moe.alloc_payload(p)
+    x_d, y_d = to_dev_bf16(inp["hidden"]), to_dev_bf16(inp["expert_out"])
+    ids_d, w_d = torch.from_numpy(inp["ids"]).cuda(), torch.from_numpy(inp["weights"]).cuda()
+    out = torch.empty((w.n, w.h), dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        moe.moe_plan_and_dispatch(p, ids_d, plan, x_d, payload, scales)
+        moe.moe_combine(p, plan, y_d, w_d, out)
+
+    outs = [plan.slot, plan.packed_src, plan.expert_offsets, plan.rank_table, plan.status,
+            payload, scales, out]
+
+    def scribble():
+        for t in (plan.slot, plan.packed_src, plan.expert_offsets, plan.rank_table, plan.status):
+            t.fill_(-3)
+        payload.fill_(0xEE)
+        scales.fill_(0xEE)
+        out.fill_(7.0)
+
+    ref = capture_and_replay(step, outs, scribble)
+    pl = oracle.plan(inp["ids"], w.e, w.ep, w.a, w.capacity, w.h)
+    pay, sc = oracle.dispatch(w.fmt, inp["hidden"], pl)
+    assert np.array_equal(ref[0].cpu().numpy(), pl["slot"])
+    assert np.array_equal(ref[5].cpu().numpy().view(np.uint8).reshape(pay.shape[0], -1),
+                          pay.view(np.uint8).reshape(pay.shape[0], -1))
+    assert np.array_equal(ref[6].cpu().numpy().view(np.uint8).reshape(sc.shape[0], -1),
+                          sc.view(np.uint8).reshape(sc.shape[0], -1))
+    assert assert_combine_close(u16(ref[7]), oracle.combine(pl["slot"], inp["weights"],
+                                                             inp["expert_out"])) == 0
