@@ -199,14 +199,13 @@ __device__ uint32_t small_plan(const SmallPlanArgs &g, const SmallPlanLds &s, co
       int sl = -1;
       if (e >= 0) {
         int r = s.before[e];
-        if (j <= 16) {  // up to 16 earlier own pairs, read together
+        // equal IDs among the own earlier pairs, 16 LDS reads in flight at a time
+        for (int q0 = 0; q0 < j; q0 += 16) {
           int w[16];
 #pragma unroll
-          for (int q = 0; q < 16; ++q) w[q] = q < j ? s.ids[p0 + q] : -1;
+          for (int q = 0; q < 16; ++q) w[q] = q0 + q < j ? s.ids[p0 + q0 + q] : -1;
 #pragma unroll
           for (int q = 0; q < 16; ++q) r += w[q] == e ? 1 : 0;
-        } else {
-          for (int q = p0; q < pr; ++q) r += s.ids[q] == e ? 1 : 0;
         }
         sl = s.off[e] + r;
       }
