@@ -634,7 +634,7 @@ __global__ __launch_bounds__(kThreads) void plan_dispatch_kernel(PlanDispatchArg
       g.offsets[E] = s.off[E];
       *g.status = fl;
     }
-    const int L = E / g.sp.ep;
+    const int L = g.sp.l;
     for (int rk = tid; rk < g.sp.ep; rk += kThreads) {
       const int lo = rk * L, hi = lo + L;
       const int S = s.cpre[hi] - s.cpre[lo];
@@ -786,6 +786,7 @@ hipError_t launch_plan_dispatch(const moe_problem &p, const int32_t *ids, const 
   g.sp.e = p.n_experts;
   g.sp.ep = p.ep;
   g.sp.a = p.pad_multiple;
+  g.sp.l = p.n_experts / p.ep;
   g.sp.cap = p.recv_capacity;
   g.counts = plan.expert_counts;
   g.offsets = plan.expert_offsets;

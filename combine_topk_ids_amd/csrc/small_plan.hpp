@@ -40,6 +40,7 @@ static_assert(kSmallTargets >= kSmallWaves * kMaxTopK, "own pairs: up to one tok
 struct SmallPlanArgs {
   const int32_t *ids;  // [n][k]
   int n, k, e, ep, a;
+  int l;               // E / EP, experts per destination
   int64_t cap;         // recv_capacity (rows per destination)
 };
 
@@ -155,7 +156,8 @@ __device__ uint32_t small_plan(const SmallPlanArgs &g, const SmallPlanLds &s, co
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       c[q] = e0 + q < E ? s.cnt[e0 + q] + s.before[e0 + q] : 0;
-      p[q] = ((c[q] + g.a - 1) / g.a) * g.a;
+      // no integer division when there is no padding (a long dependent chain)
+      p[q] = g.a == 1 ? c[q] : ((c[q] + g.a - 1) / g.a) * g.a;
       sc += c[q];
       sp += p[q];
     }
@@ -212,7 +214,7 @@ __device__ uint32_t small_plan(const SmallPlanArgs &g, const SmallPlanLds &s, co
       s.tslot[j] = sl;
     }
   }
-  const int L = E / g.ep;
+  const int L = g.l;
   for (int r = tid; r < g.ep; r += kSmallThreads)
     if (s.cpre[(r + 1) * L] - s.cpre[r * L] > g.cap) fl |= MOE_STATUS_CAPACITY;
   const uint64_t b0 = ballot(fl & MOE_STATUS_BAD_ID), b1 = ballot(fl & MOE_STATUS_DUP_ID),
