@@ -21,13 +21,19 @@
 // routing is.  In the quantising formats a lane encodes 8 consecutive values
 // (a 512-value slab per wave: the division-heavy FP8 encode wants many
 // waves); an FP8 1x128 block spans one 16-lane DPP row (block maximum by
-// quad, half-row and row mirrors), an MX 32-value block one quad.  Pad rows are zeroed by a second
-// range of workgroups in the same launch, the optional tail by a third.
+// quad, half-row and row mirrors), an MX 32-value block one quad.  Pad rows
+// are zeroed by a second range of workgroups in the same launch, the
+// optional tail by a third.
 //
 // The simulated expert-parallel exchange reuses the token waves unchanged:
 // there the slot of a pair is its row in the stacked receive buffers of all
 // ranks, and the third range writes the zero rows that end every receive
 // buffer (NKI permute_a2av API reference, :return:).
+//
+// For problems of at most 2048 pairs, plan_dispatch_kernel plans and
+// dispatches in one launch (NKI permute_a2av API reference, description:
+// one call both lays out and permutes): each workgroup computes in LDS the
+// part of the plan it needs (small_plan.hpp) while its slabs load.
 #include "moe_device.hpp"
 #include "moe_kernels.hpp"
 #include "small_plan.hpp"

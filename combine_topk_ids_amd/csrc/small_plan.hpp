@@ -22,7 +22,7 @@
 // 4 tokens, so at most 256 pairs: a pair's slot is its expert's offset, plus
 // the earlier pairs of that expert before the workgroup's tokens, plus those
 // among the workgroup's own earlier pairs).  One LDS atomic per ID, no
-// ballots, four barriers.
+// ballots, five barriers.
 #pragma once
 
 #include "moe_device.hpp"
