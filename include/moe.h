@@ -68,7 +68,7 @@ extern "C" {
 #define MOE_EOVERFLOW (-3) /* R_max*H >= 2^32 (table) or rows >= 2^31       */
 #define MOE_EHIP (-4)      /* the HIP runtime reported a launch error       */
 
-/* ---- bits of plan->status (device, written by moe_dispatch_plan and by   
+/* ---- bits of plan->status (device, written by moe_dispatch_plan and by
  *      moe_plan_and_dispatch) ------------------------------------------ */
 #define MOE_STATUS_BAD_ID 1u   /* an ID outside [-1, E): treated as masked   */
 #define MOE_STATUS_DUP_ID 2u   /* an ID repeated within one token: routed    */
