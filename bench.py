@@ -1,9 +1,12 @@
 #!/usr/bin/env python3
 """Benchmark: MoE dispatch + combine on one MI355X.
 
-One step = the whole path on one batch: moe_dispatch_plan, moe_dispatch,
-moe_combine (identity experts for bf16 workloads: the combine reads the
-packed rows the dispatch wrote; random bf16 expert outputs otherwise).
+One step = the whole path on one batch: moe_plan_and_dispatch_begin (the
+launches that need only the IDs), moe_plan_and_dispatch_end (the one launch
+that writes the payload), moe_combine (identity experts for bf16 workloads:
+the combine reads the packed rows the dispatch wrote; random bf16 expert
+outputs otherwise).  Depending on the problem (moe_plan_and_dispatch_mode),
+_begin launches nothing, the plan's counting kernel, or the whole plan.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME]
 
@@ -14,8 +17,9 @@ rotate over several copies of all buffers so that a step does not find its
 inputs in the 256 MB last-level cache from the step before.
 
 Per-kernel durations for the roofline (means, and p10/p50/p90 of each phase
-and of the step) come from HIP events recorded around every launch on the
-stream the kernels run on, in a second pass over the same number of steps.
+and of the step) come from HIP events recorded around every call on the
+stream the kernels run on, in a second pass over the same number of steps:
+"plan" is _begin, "dispatch" is _end (one kernel), "combine" the combine.
 ``payload_only`` repeats the rate counting only packed rows that hold a
 token.
 """
@@ -132,29 +136,39 @@ class Path:
     def step(self, i, ev=None):
         s = self.sets[i % len(self.sets)]
         m, p = self.moe, self.p
+        gs = self.gs if self.w.fmt == "nvfp4" else None
         if ev is not None:
             ev[0].record()
-        m.moe_dispatch_plan(p, s["ids"], s["plan"])
+        m.moe_plan_and_dispatch_begin(p, s["ids"], s["plan"])
         if ev is not None:
             ev[1].record()
-        if self.w.fmt == "nvfp4":
-            m.moe_dispatch_scaled(p, s["plan"], s["x"], self.gs, s["payload"], s["scales"])
-        else:
-            m.moe_dispatch(p, s["plan"], s["x"], s["payload"], s["scales"])
+        m.moe_plan_and_dispatch_end(p, s["ids"], s["plan"], s["x"], s["payload"], s["scales"],
+                                    input_scale=gs)
         if ev is not None:
             ev[2].record()
         m.moe_combine(p, s["plan"], s["y"], s["w"], s["out"])
         if ev is not None:
             ev[3].record()
 
-    def step_one_launch(self, i):
-        """The same step with the plan and the dispatch in one call (one launch
-        for problems of at most 2048 pairs)."""
+    def step_three_calls(self, i):
+        """The same step as moe_dispatch_plan, moe_dispatch, moe_combine (the
+        plan's kernels, then the dispatch kernel)."""
         s = self.sets[i % len(self.sets)]
-        gs = self.gs if self.w.fmt == "nvfp4" else None
-        self.moe.moe_plan_and_dispatch(self.p, s["ids"], s["plan"], s["x"], s["payload"],
-                                       s["scales"], input_scale=gs)
-        self.moe.moe_combine(self.p, s["plan"], s["y"], s["w"], s["out"])
+        m, p = self.moe, self.p
+        m.moe_dispatch_plan(p, s["ids"], s["plan"])
+        if self.w.fmt == "nvfp4":
+            m.moe_dispatch_scaled(p, s["plan"], s["x"], self.gs, s["payload"], s["scales"])
+        else:
+            m.moe_dispatch(p, s["plan"], s["x"], s["payload"], s["scales"])
+        m.moe_combine(p, s["plan"], s["y"], s["w"], s["out"])
+
+    def mode(self):
+        return {self.moe.PD_ONE_LAUNCH: "one_launch", self.moe.PD_TILED: "tiled",
+                self.moe.PD_SEPARATE: "separate"}[self.moe.moe_plan_and_dispatch_mode(self.p)]
+
+    def dispatch_kernel(self):
+        """The kernel _end launches."""
+        return "dispatch_kernel" if self.mode() == "separate" else "plan_dispatch_kernel"
 
     def r_used(self):
         return int(self.sets[0]["plan"].expert_offsets[-1].item())
@@ -214,6 +228,10 @@ class ExchangePath:
         if ev is not None:
             ev[3].record()
 
+    def dispatch_kernel(self):
+        """The kernel of the dispatch call."""
+        return "dispatch_kernel"
+
     def r_used(self):
         rows = self.sets[0]["xb"].recv_rows.clamp(max=self.w.capacity)
         return int(rows.sum().item())
@@ -231,6 +249,17 @@ class _SameSet:
 
     def step(self, i, ev=None):
         self.path.step(0, ev)
+
+
+class _ThreeCalls:
+    """A single-buffer path stepped as moe_dispatch_plan, moe_dispatch,
+    moe_combine."""
+
+    def __init__(self, path):
+        self.path = path
+
+    def step(self, i, ev=None):
+        self.path.step_three_calls(i)
 
 
 def time_steps(torch, path, steps, warmup):
@@ -291,14 +320,16 @@ def decode_latency(moe, torch, w, inp, iters=200, per_graph=16):
     back-to-back calls from Python (host-bound: each call costs a few µs of
     Python and ctypes), one HIP graph per step, and one HIP graph holding
     `per_graph` steps (closest to the GPU's own time per step).  For a single
-    packed buffer the same is reported with the plan and the dispatch in one
-    call (``one_launch_plan_dispatch``)."""
+    packed buffer the same is reported for the step made of the three
+    separate calls (``three_calls``: the plan's kernel, then the dispatch)."""
     path = (ExchangePath if w.exchange else Path)(moe, torch, w, inp, copies=1)
     out = dict(workload=w.name)
+    if isinstance(path, Path):
+        out["plan_and_dispatch"] = path.mode()
     out.update(_latencies(torch, path, lambda: path.step(0), iters, per_graph))
-    if isinstance(path, Path) and not path.expert_cap:
-        out["one_launch_plan_dispatch"] = _latencies(torch, path, lambda: path.step_one_launch(0),
-                                                     iters, per_graph)
+    if isinstance(path, Path):
+        out["three_calls"] = _latencies(torch, path, lambda: path.step_three_calls(0), iters,
+                                        per_graph)
     return out
 
 
@@ -471,6 +502,11 @@ def main():
     # context: the same buffer set every step, so inputs may stay in the caches
     warm_ms, _ = time_steps(torch, _SameSet(path), args.steps, args.warmup)
     log(f"[bench] warm (one buffer set): {warm_ms * 1e3:.2f} us/step")
+    three_ms = None
+    if not w.exchange:
+        # context: the same step as the plan call, the dispatch call, the combine
+        three_ms, _ = time_steps(torch, _ThreeCalls(path), args.steps, args.warmup)
+        log(f"[bench] plan_and_dispatch {path.mode()}; as three calls: {three_ms * 1e3:.2f} us/step")
     kt = time_kernels(torch, path, args.steps)
     log(f"[bench] per-kernel means (us): plan {kt['plan'] * 1e3:.2f} dispatch "
         f"{kt['dispatch'] * 1e3:.2f} combine {kt['combine'] * 1e3:.2f}")
@@ -489,12 +525,18 @@ def main():
                         gbps=round((b["plan"] + disp_live + b["combine"]) / (ms * 1e-3) / 1e9, 1))
 
     dom = "dispatch" if kt["dispatch"] >= kt["combine"] else "combine"
-    achieved = b[dom] / (kt[dom] * 1e-3) / 1e9
-    kname = {"dispatch": "dispatch_kernel", "combine": "combine_kernel"}[dom]
+    kname = "combine_kernel"
+    dom_bytes = b[dom]
+    if dom == "dispatch":
+        kname = path.dispatch_kernel()
+        if kname == "plan_dispatch_kernel":
+            # it also reads the IDs and writes slot and packed_src
+            dom_bytes = b["dispatch"] + b["plan"]
+    achieved = dom_bytes / (kt[dom] * 1e-3) / 1e9
     traffic = traffic_from_profile(w.name, kname)
     roofline = dict(bound="hbm", kernel=kname, achieved=round(achieved, 1),
                     peak=PEAK_HBM_GBPS, unit="GB/s", frac=round(achieved / PEAK_HBM_GBPS, 4),
-                    traffic=traffic, algorithmic_bytes=b[dom],
+                    traffic=traffic, algorithmic_bytes=dom_bytes,
                     avg_launch_us=round(kt[dom] * 1e3, 2))
 
     extra = {}
@@ -516,6 +558,8 @@ def main():
               "top_k": w.k, "ep_ranks_simulated": w.ep, "pad_multiple": w.a,
               "format": w.fmt, "routing": w.routing, "r_used": ru, "r_max": r_max,
               "buffer_sets": copies}
+    if not w.exchange:
+        config["plan_and_dispatch"] = path.mode()
     if w.exchange:
         config.update(source_ranks=w.ranks, recv_capacity=w.capacity,
                       path="exchange: source-major receive buffers of C rows per rank")
@@ -542,6 +586,7 @@ def main():
         "bytes_per_step": b,
         "payload_only": payload_only,
         "warm_us_per_step": round(warm_ms * 1e3, 2),
+        "three_calls_us_per_step": None if three_ms is None else round(three_ms * 1e3, 2),
         "kernel_us": {k: round(v * 1e3, 2) for k, v in kt.items()},
         "roofline": roofline,
         "cpu_baseline": cpu,

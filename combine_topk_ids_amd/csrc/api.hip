@@ -63,6 +63,72 @@ int check_exchange(const moe_problem *p) {
 
 int launched(hipError_t err) { return err == hipSuccess ? MOE_OK : MOE_EHIP; }
 
+// Arguments of a plan: moe_dispatch_plan and both halves of
+// moe_plan_and_dispatch.
+int check_plan_args(const moe_problem *p, const int32_t *topk_ids, const moe_plan *plan,
+                    const void *workspace) {
+  const int rc = check(p);
+  if (rc != MOE_OK) return rc;
+  if (!plan || !plan->expert_counts || !plan->expert_offsets || !plan->dest_counts ||
+      !plan->rank_table || !plan->status)
+    return MOE_EINVAL;
+  const int64_t npairs = p->n_tokens * p->top_k;
+  if (npairs > 0 && (!topk_ids || !plan->slot)) return MOE_EINVAL;
+  if (max_rows_unchecked(*p) > 0 && !plan->packed_src) return MOE_EINVAL;
+  if (moe::plan_workspace_bytes(*p) > 0 && !workspace) return MOE_EINVAL;
+  if (!aligned(topk_ids, 4) || !aligned(plan->expert_counts, 4) || !aligned(plan->expert_offsets, 4) ||
+      !aligned(plan->dest_counts, 4) || !aligned(plan->rank_table, 4) || !aligned(plan->slot, 4) ||
+      !aligned(plan->packed_src, 4) || !aligned(plan->status, 4) || !aligned(workspace, 256))
+    return MOE_EALIGN;
+  return MOE_OK;
+}
+
+// The dispatch arguments of moe_plan_and_dispatch (after check_plan_args):
+// a global scale only for NVFP4, which takes no gates.
+int check_pd_dispatch_args(const moe_problem *p, const uint16_t *hidden, const float *topk_weights,
+                           const float *input_scale, const void *payload, const void *scales) {
+  const bool nvfp4 = p->fmt == MOE_FMT_NVFP4_B16;
+  if (nvfp4 != (input_scale != nullptr) || (nvfp4 && topk_weights)) return MOE_EINVAL;
+  if (p->n_tokens > 0 && !hidden) return MOE_EINVAL;
+  const bool quant = p->fmt != MOE_FMT_BF16;
+  if (max_rows_unchecked(*p) > 0 && (!payload || (quant && !scales))) return MOE_EINVAL;
+  if (!quant && scales) return MOE_EINVAL;
+  if (!aligned(hidden, 16) || !aligned(payload, 16) || !aligned(topk_weights, 4) ||
+      !aligned(input_scale, 4) || (p->fmt == MOE_FMT_FP8_E4M3_B128 && !aligned(scales, 4)))
+    return MOE_EALIGN;
+  return MOE_OK;
+}
+
+int pd_mode(const moe_problem &p) {
+  switch (moe::plan_dispatch_mode(p)) {
+    case moe::PlanDispatchMode::kOneLaunch: return MOE_PD_ONE_LAUNCH;
+    case moe::PlanDispatchMode::kTiled: return MOE_PD_TILED;
+    default: return MOE_PD_SEPARATE;
+  }
+}
+
+// The launches of moe_plan_and_dispatch that need only topk_ids.
+int pd_begin(const moe_problem &p, const int32_t *ids, const moe_plan &plan, void *workspace,
+             hipStream_t s) {
+  switch (moe::plan_dispatch_mode(p)) {
+    case moe::PlanDispatchMode::kOneLaunch: return MOE_OK;
+    case moe::PlanDispatchMode::kTiled: return launched(moe::launch_plan_count(p, ids, workspace, s));
+    default: return launched(moe::launch_plan(p, ids, plan, workspace, s));
+  }
+}
+
+// The launch of moe_plan_and_dispatch that writes the payload.
+int pd_end(const moe_problem &p, const int32_t *ids, const moe_plan &plan, const uint16_t *hidden,
+           const float *topk_weights, const float *input_scale, void *payload, void *scales,
+           void *workspace, hipStream_t s) {
+  // a null weight pointer selects the ungated kernels
+  const float *w = p.n_tokens > 0 ? topk_weights : nullptr;
+  if (moe::plan_dispatch_mode(p) == moe::PlanDispatchMode::kSeparate)
+    return launched(moe::launch_dispatch(p, plan, hidden, w, input_scale, payload, scales, s));
+  return launched(moe::launch_plan_dispatch(p, ids, plan, hidden, w, input_scale, payload, scales,
+                                            workspace, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -108,19 +174,8 @@ MOE_API size_t moe_workspace_bytes(const moe_problem *p) {
 
 MOE_API int moe_dispatch_plan(const moe_problem *p, const int32_t *topk_ids, const moe_plan *plan,
                               void *workspace, void *stream) {
-  const int rc = check(p);
+  const int rc = check_plan_args(p, topk_ids, plan, workspace);
   if (rc != MOE_OK) return rc;
-  if (!plan || !plan->expert_counts || !plan->expert_offsets || !plan->dest_counts ||
-      !plan->rank_table || !plan->status)
-    return MOE_EINVAL;
-  const int64_t npairs = p->n_tokens * p->top_k;
-  if (npairs > 0 && (!topk_ids || !plan->slot)) return MOE_EINVAL;
-  if (max_rows_unchecked(*p) > 0 && !plan->packed_src) return MOE_EINVAL;
-  if (moe::plan_workspace_bytes(*p) > 0 && !workspace) return MOE_EINVAL;
-  if (!aligned(topk_ids, 4) || !aligned(plan->expert_counts, 4) || !aligned(plan->expert_offsets, 4) ||
-      !aligned(plan->dest_counts, 4) || !aligned(plan->rank_table, 4) || !aligned(plan->slot, 4) ||
-      !aligned(plan->packed_src, 4) || !aligned(plan->status, 4) || !aligned(workspace, 256))
-    return MOE_EALIGN;
   return launched(moe::launch_plan(*p, topk_ids, *plan, workspace, static_cast<hipStream_t>(stream)));
 }
 
@@ -177,41 +232,41 @@ MOE_API int moe_dispatch_gated(const moe_problem *p, const moe_plan *plan, const
                                        static_cast<hipStream_t>(stream)));
 }
 
+MOE_API int moe_plan_and_dispatch_mode(const moe_problem *p) {
+  const int rc = check(p);
+  if (rc != MOE_OK) return rc;
+  return pd_mode(*p);
+}
+
+MOE_API int moe_plan_and_dispatch_begin(const moe_problem *p, const int32_t *topk_ids, const moe_plan *plan,
+                                        void *workspace, void *stream) {
+  const int rc = check_plan_args(p, topk_ids, plan, workspace);
+  if (rc != MOE_OK) return rc;
+  return pd_begin(*p, topk_ids, *plan, workspace, static_cast<hipStream_t>(stream));
+}
+
+MOE_API int moe_plan_and_dispatch_end(const moe_problem *p, const int32_t *topk_ids, const moe_plan *plan,
+                                      const uint16_t *hidden, const float *topk_weights,
+                                      const float *input_scale, void *payload, void *scales, void *workspace,
+                                      void *stream) {
+  int rc = check_plan_args(p, topk_ids, plan, workspace);
+  if (rc == MOE_OK) rc = check_pd_dispatch_args(p, hidden, topk_weights, input_scale, payload, scales);
+  if (rc != MOE_OK) return rc;
+  return pd_end(*p, topk_ids, *plan, hidden, topk_weights, input_scale, payload, scales, workspace,
+                static_cast<hipStream_t>(stream));
+}
+
 MOE_API int moe_plan_and_dispatch(const moe_problem *p, const int32_t *topk_ids, const moe_plan *plan,
                                   const uint16_t *hidden, const float *topk_weights,
                                   const float *input_scale, void *payload, void *scales, void *workspace,
                                   void *stream) {
-  const int rc = check(p);
+  int rc = check_plan_args(p, topk_ids, plan, workspace);
+  if (rc == MOE_OK) rc = check_pd_dispatch_args(p, hidden, topk_weights, input_scale, payload, scales);
   if (rc != MOE_OK) return rc;
-  // the plan's arguments, as moe_dispatch_plan checks them
-  if (!plan || !plan->expert_counts || !plan->expert_offsets || !plan->dest_counts ||
-      !plan->rank_table || !plan->status)
-    return MOE_EINVAL;
-  const int64_t npairs = p->n_tokens * p->top_k;
-  if (npairs > 0 && (!topk_ids || !plan->slot)) return MOE_EINVAL;
-  if (max_rows_unchecked(*p) > 0 && !plan->packed_src) return MOE_EINVAL;
-  if (moe::plan_workspace_bytes(*p) > 0 && !workspace) return MOE_EINVAL;
-  // the dispatch's arguments: global scale only for NVFP4, which takes no gates
-  const bool nvfp4 = p->fmt == MOE_FMT_NVFP4_B16;
-  if (nvfp4 != (input_scale != nullptr) || (nvfp4 && topk_weights)) return MOE_EINVAL;
-  if (p->n_tokens > 0 && !hidden) return MOE_EINVAL;
-  const bool quant = p->fmt != MOE_FMT_BF16;
-  if (max_rows_unchecked(*p) > 0 && (!payload || (quant && !scales))) return MOE_EINVAL;
-  if (!quant && scales) return MOE_EINVAL;
-  if (!aligned(topk_ids, 4) || !aligned(plan->expert_counts, 4) || !aligned(plan->expert_offsets, 4) ||
-      !aligned(plan->dest_counts, 4) || !aligned(plan->rank_table, 4) || !aligned(plan->slot, 4) ||
-      !aligned(plan->packed_src, 4) || !aligned(plan->status, 4) || !aligned(workspace, 256) ||
-      !aligned(hidden, 16) || !aligned(payload, 16) || !aligned(topk_weights, 4) ||
-      !aligned(input_scale, 4) || (p->fmt == MOE_FMT_FP8_E4M3_B128 && !aligned(scales, 4)))
-    return MOE_EALIGN;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  // a null weight pointer selects the ungated kernels
-  const float *w = p->n_tokens > 0 ? topk_weights : nullptr;
-  if (moe::plan_dispatch_fits(*p))
-    return launched(moe::launch_plan_dispatch(*p, topk_ids, *plan, hidden, w, input_scale, payload, scales, s));
-  const int rp = launched(moe::launch_plan(*p, topk_ids, *plan, workspace, s));
-  if (rp != MOE_OK) return rp;
-  return launched(moe::launch_dispatch(*p, *plan, hidden, w, input_scale, payload, scales, s));
+  rc = pd_begin(*p, topk_ids, *plan, workspace, s);
+  if (rc != MOE_OK) return rc;
+  return pd_end(*p, topk_ids, *plan, hidden, topk_weights, input_scale, payload, scales, workspace, s);
 }
 
 MOE_API int moe_combine(const moe_problem *p, const moe_plan *plan, const uint16_t *expert_out,

@@ -30,10 +30,11 @@
 // ranks, and the third range writes the zero rows that end every receive
 // buffer (NKI permute_a2av API reference, :return:).
 //
-// For problems of at most 2048 pairs, plan_dispatch_kernel plans and
-// dispatches in one launch (NKI permute_a2av API reference, description:
-// one call both lays out and permutes): each workgroup computes in LDS the
-// part of the plan it needs (small_plan.hpp) while its slabs load.
+// plan_dispatch_kernel plans and dispatches in one launch (NKI permute_a2av
+// API reference, description: one call both lays out and permutes): each
+// workgroup computes in LDS the part of the plan it needs (small_plan.hpp)
+// while its slabs load, from all the IDs (at most 2048 pairs) or from the
+// tile histograms of the plan's counting kernel (tiled mode).
 #include "moe_device.hpp"
 #include "moe_kernels.hpp"
 #include "small_plan.hpp"
@@ -72,6 +73,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #ifndef MOE_TAIL_NT
 #define MOE_TAIL_NT 1
 #endif
+
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
@@ -163,6 +165,38 @@ __device__ __forceinline__ RawSlab load_slab(const DispatchArgs &g, int64_t t, i
     }
   }
   r.w = GATED && lane < g.k ? g.w[t * g.k + lane] : 0.0f;
+  return r;
+}
+
+// load_slab through bounds-checked buffer loads, issued whether or not the
+// wave has a token (live): a wave without one reads nothing and gets zeros.
+// No branch surrounds the loads, so a kernel that issues other loads before
+// these can wait for those alone.
+template <int FMT, bool GATED>
+__device__ __forceinline__ RawSlab load_slab_buf(const DispatchArgs &g, int64_t t, int slab, bool live) {
+  const int lane = lane_id();
+  const auto row = buffer_rsrc(live ? g.x + t * g.h : g.x, live ? 2u * static_cast<uint32_t>(g.h) : 0u);
+  RawSlab r;
+  if (FMT == MOE_FMT_BF16) {
+    const int v0 = slab * kWave * kBf16Vec;
+#pragma unroll
+    for (int u = 0; u < kBf16Vec; ++u)
+      r.v[u] = __builtin_amdgcn_raw_buffer_load_b128(row, (v0 + u * kWave + lane) * 16, 0, kLoadNT);
+  } else {
+#pragma unroll
+    for (int c = 0; c < kQC; ++c) {
+      const int elem = slab * kQuantSlab + c * kWave * kLE + lane * kLE;
+#pragma unroll
+      for (int q = 0; q < kLE / 8; ++q)
+        r.v[c * (kLE / 8) + q] = __builtin_amdgcn_raw_buffer_load_b128(row, (elem / 8 + q) * 16, 0, kLoadNT);
+    }
+  }
+  if (GATED) {
+    const auto w = buffer_rsrc(g.w + (live ? t * g.k : 0), live ? 4u * static_cast<uint32_t>(g.k) : 0u);
+    r.w = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(w, lane * 4, 0, kLoadDefault));
+  } else {
+    r.w = 0.0f;
+  }
   return r;
 }
 
@@ -577,10 +611,15 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(DispatchArgs g) {
   dispatch_body<FMT, NT, GATED>(g, blockIdx.x, __builtin_amdgcn_readfirstlane(threadIdx.x / kWave));
 }
 
-// ---- plan and dispatch in one launch (at most kSmallPairs pairs) ----------
+// ---- plan and dispatch in one launch ---------------------------------------
 // Every workgroup issues the loads of the IDs and of its token slabs, then
 // computes in LDS the part of the plan it needs (small_plan.hpp) while the
 // slabs arrive, and encodes and stores its slabs with the slots it found.
+// Small mode (at most kSmallPairs pairs): the plan from all the IDs.  Tiled
+// mode (after plan_count_kernel): the plan from the tile histograms and the
+// IDs of the workgroup's own count tile.  The loads are bounds-checked
+// buffer loads with no branch around them, so the plan waits for its IDs
+// alone and runs while the slabs are still in flight.
 // Workgroup 0 writes the counts, offsets, table and status; the wave that
 // holds slab 0 of a token writes that token's slots and packed_src rows;
 // all workgroups stride over the pad and tail rows of packed_src; the
@@ -598,27 +637,18 @@ struct PlanDispatchArgs {
 static_assert(kThreads == kSmallThreads, "one small plan per dispatch workgroup");
 static_assert(MOE_TAIL_FIRST == 0, "the one-launch kernel places the token workgroups first");
 
-template <int FMT, bool NT, bool GATED>
+template <int FMT, bool NT, bool GATED, bool TILED>
 __global__ __launch_bounds__(kThreads) void plan_dispatch_kernel(PlanDispatchArgs g) {
   extern __shared__ int smem[];
-  const int E = g.sp.e, k = g.sp.k, np = g.sp.n * g.sp.k;
+  const int E = g.sp.e, k = g.sp.k;
   const int b = blockIdx.x, tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const DispatchArgs &d = g.d;
   const SmallPlanLds s = small_plan_lds(smem, E);
 
-  // the IDs, then this wave's token slab: all loads in flight during the plan
-  int v[kSmallLoads];
-  small_plan_load(g.sp, v);
   const bool tok = b < d.token_blocks;
   const int blk = tok && FMT != MOE_FMT_BF16 ? xcd_local_block(b, d.token_blocks) : b;
-  const int q = blk * kWaves + wave;  // the grid size keeps q within int
-  const int t = tok ? q / d.slabs : 0;
-  const int slab = q - t * d.slabs;
-  const bool live = tok && t < g.sp.n;
-  RawSlab r{};
-  if (live) r = load_slab<FMT, GATED>(d, t, slab);
   // the workgroup's own pairs: every pair of its (at most kWaves) tokens
   int p0 = 0, p1 = 0;
   if (tok) {
@@ -629,7 +659,30 @@ __global__ __launch_bounds__(kThreads) void plan_dispatch_kernel(PlanDispatchArg
       p1 = (t1 + 1) * k;
     }
   }
-  const uint32_t fl = small_plan(g.sp, s, v, p0, p1, b == 0);
+  // tiled: pairs from the start of the count tile that holds p0
+  const int c0 = TILED ? (p0 / k) / g.sp.tile_tokens : 0;
+  const int tlo = c0 * g.sp.tile_tokens * k;
+
+  // the IDs (and histograms), then this wave's token slab: all loads in
+  // flight during the plan
+  int v[kSmallLoads];
+  TileLoads tl;
+  if constexpr (TILED)
+    tile_plan_load(g.sp, tlo, p1 - tlo, tl);
+  else
+    small_plan_load(g.sp, v);
+  const int q = blk * kWaves + wave;  // the grid size keeps q within int
+  const int t = tok ? q / d.slabs : 0;
+  const int slab = q - t * d.slabs;
+  const bool live = tok && t < g.sp.n;
+  const RawSlab r = load_slab_buf<FMT, GATED>(d, t, slab, live);
+  // the plan waits for its own loads only: the slab may still be in flight
+  if constexpr (TILED) tile_plan_stage(g.sp, s, tl, p1 - tlo);
+  uint32_t fl;
+  if constexpr (TILED)
+    fl = tile_plan(g.sp, s, tl, tlo, p0, p1, c0);
+  else
+    fl = small_plan(g.sp, s, v, p0, p1, b == 0);
 
   if (b == 0) {
     for (int e = tid; e < E; e += kThreads) {
@@ -757,13 +810,21 @@ DispatchArgs single_buffer_args(const moe_problem &p, const int32_t *slot, const
   return g;
 }
 
-template <int FMT>
+template <int FMT, bool TILED>
 void launch_plan_dispatch_fmt(const PlanDispatchArgs &g, int grid, size_t lds, hipStream_t stream) {
   constexpr bool kNT = MOE_DISPATCH_NT_STORE != 0;
   if (FMT != MOE_FMT_NVFP4_B16 && g.d.w)
-    plan_dispatch_kernel<FMT, kNT, FMT != MOE_FMT_NVFP4_B16><<<grid, kThreads, lds, stream>>>(g);
+    plan_dispatch_kernel<FMT, kNT, FMT != MOE_FMT_NVFP4_B16, TILED><<<grid, kThreads, lds, stream>>>(g);
   else
-    plan_dispatch_kernel<FMT, kNT, false><<<grid, kThreads, lds, stream>>>(g);
+    plan_dispatch_kernel<FMT, kNT, false, TILED><<<grid, kThreads, lds, stream>>>(g);
+}
+
+template <bool TILED>
+void launch_plan_dispatch_any(const PlanDispatchArgs &g, int fmt, int grid, size_t lds, hipStream_t stream) {
+  if (fmt == MOE_FMT_BF16) launch_plan_dispatch_fmt<MOE_FMT_BF16, TILED>(g, grid, lds, stream);
+  else if (fmt == MOE_FMT_FP8_E4M3_B128) launch_plan_dispatch_fmt<MOE_FMT_FP8_E4M3_B128, TILED>(g, grid, lds, stream);
+  else if (fmt == MOE_FMT_NVFP4_B16) launch_plan_dispatch_fmt<MOE_FMT_NVFP4_B16, TILED>(g, grid, lds, stream);
+  else launch_plan_dispatch_fmt<MOE_FMT_MXFP4_B32, TILED>(g, grid, lds, stream);
 }
 
 }  // namespace
@@ -776,13 +837,20 @@ hipError_t launch_dispatch(const moe_problem &p, const moe_plan &plan, const uin
   return launch_args(g, p.fmt, stream);
 }
 
-bool plan_dispatch_fits(const moe_problem &p) {
-  return p.n_tokens * p.top_k <= kSmallPairs && p.expert_capacity == 0;
+PlanDispatchMode plan_dispatch_mode(const moe_problem &p) {
+  if (p.expert_capacity != 0) return PlanDispatchMode::kSeparate;
+  const int64_t npairs = p.n_tokens * p.top_k;
+  if (npairs <= kSmallPairs) return PlanDispatchMode::kOneLaunch;
+  const PlanGeom geo = plan_geometry(p);
+  if (static_cast<int64_t>(geo.ntiles) * p.n_experts <= kTileHist && max_rows(p) <= INT32_MAX)
+    return PlanDispatchMode::kTiled;
+  return PlanDispatchMode::kSeparate;
 }
 
 hipError_t launch_plan_dispatch(const moe_problem &p, const int32_t *ids, const moe_plan &plan,
                                 const uint16_t *hidden, const float *gates, const float *gscale,
-                                void *payload, void *scales, hipStream_t stream) {
+                                void *payload, void *scales, void *workspace, hipStream_t stream) {
+  const PlanDispatchMode mode = plan_dispatch_mode(p);
   PlanDispatchArgs g{};
   // plan pointers are taken from LDS inside the kernel
   g.d = single_buffer_args(p, nullptr, nullptr, nullptr, hidden, gates, gscale, payload, scales);
@@ -806,10 +874,17 @@ hipError_t launch_plan_dispatch(const moe_problem &p, const int32_t *ids, const 
   g.dispatch_blocks = g.d.token_blocks + g.d.pad_blocks + g.d.tail_blocks;
   const int grid = max(g.dispatch_blocks, 1);  // N = 0 still writes the plan
   const size_t lds = small_plan_lds_bytes(p.n_experts);
-  if (p.fmt == MOE_FMT_BF16) launch_plan_dispatch_fmt<MOE_FMT_BF16>(g, grid, lds, stream);
-  else if (p.fmt == MOE_FMT_FP8_E4M3_B128) launch_plan_dispatch_fmt<MOE_FMT_FP8_E4M3_B128>(g, grid, lds, stream);
-  else if (p.fmt == MOE_FMT_NVFP4_B16) launch_plan_dispatch_fmt<MOE_FMT_NVFP4_B16>(g, grid, lds, stream);
-  else launch_plan_dispatch_fmt<MOE_FMT_MXFP4_B32>(g, grid, lds, stream);
+  if (mode == PlanDispatchMode::kOneLaunch) {
+    launch_plan_dispatch_any<false>(g, p.fmt, grid, lds, stream);
+    return hipGetLastError();
+  }
+  // tiled: the counting kernel has written the histograms and fault bits
+  const PlanGeom geo = plan_geometry(p);
+  g.sp.hist = static_cast<const int32_t *>(workspace);
+  g.sp.tflags = reinterpret_cast<const uint32_t *>(g.sp.hist + static_cast<int64_t>(geo.ntiles) * p.n_experts);
+  g.sp.ntiles = geo.ntiles;
+  g.sp.tile_tokens = geo.tile_tokens;
+  launch_plan_dispatch_any<true>(g, p.fmt, grid, lds, stream);
   return hipGetLastError();
 }
 

@@ -20,6 +20,26 @@ namespace moe {
 
 constexpr int kWave = 64;
 
+// -------------------------------------------------------------- buffers ---
+
+// Raw (unstructured) buffer resource over `bytes` bytes at `base`.  Loads
+// through it are bounds-checked by the hardware: a load at or past `bytes`
+// returns zero and touches no memory (bytes = 0: no load touches memory).
+// Kernels use them where a load is optional per lane or per wave: the
+// load is then issued unconditionally, with no branch around it, so the
+// compiler can wait for each load on its own instead of for all of them.
+// Third-dword configuration of gfx9 raw buffers: 32-bit data format.
+constexpr int kRawBufferConfig = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, static_cast<int>(bytes),
+                                           kRawBufferConfig);
+}
+
+// Cache-policy bits of a buffer load: streaming (non-temporal), or default.
+constexpr int kLoadNT = 2;
+constexpr int kLoadDefault = 0;
+
 // ---------------------------------------------------------------- waves ---
 
 __device__ __forceinline__ int lane_id() {

@@ -73,11 +73,23 @@ hipError_t launch_dispatch(const moe_problem &p, const moe_plan &plan, const uin
                            const float *gates, const float *gscale, void *payload, void *scales,
                            hipStream_t stream);
 
-// Plan and dispatch in one launch; only where plan_dispatch_fits(p).
-bool plan_dispatch_fits(const moe_problem &p);
+// The plan's counting kernel alone: tile histograms and fault bits into
+// the plan workspace (problems of more than one count tile).
+hipError_t launch_plan_count(const moe_problem &p, const int32_t *ids, void *workspace,
+                             hipStream_t stream);
+
+// How moe_plan_and_dispatch runs a problem: one launch (at most 2048 pairs),
+// tiled (the counting kernel, then one launch that finishes the plan and
+// dispatches; at most 2048 histogram entries), or the plan's kernels then
+// the dispatch.  The first two take no fixed expert capacity.
+enum class PlanDispatchMode { kOneLaunch, kTiled, kSeparate };
+PlanDispatchMode plan_dispatch_mode(const moe_problem &p);
+// The launch that plans (or, tiled, finishes the plan after
+// launch_plan_count) and dispatches; only where plan_dispatch_mode(p) is
+// kOneLaunch or kTiled.
 hipError_t launch_plan_dispatch(const moe_problem &p, const int32_t *ids, const moe_plan &plan,
                                 const uint16_t *hidden, const float *gates, const float *gscale,
-                                void *payload, void *scales, hipStream_t stream);
+                                void *payload, void *scales, void *workspace, hipStream_t stream);
 
 hipError_t launch_combine(const moe_problem &p, const moe_plan &plan, const uint16_t *expert_out,
                           const float *weights, uint16_t *out, hipStream_t stream);

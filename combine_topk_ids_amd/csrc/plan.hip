@@ -456,10 +456,13 @@ __global__ __launch_bounds__(kThreads) void plan_assign_kernel(PlanArgs g) {
 }
 
 template <int KC>
-void launch_k(const PlanArgs &g, bool fused, int e, int ranks, hipStream_t stream) {
+void launch_k(const PlanArgs &g, bool fused, int e, int ranks, hipStream_t stream, bool count_only) {
   const size_t assign_lds =
       (static_cast<size_t>(4 + kWaves) * e + 2 + kTilePairs + 2 * kThreads) * sizeof(int);
-  if (fused) {
+  if (count_only) {
+    const size_t count_lds = (static_cast<size_t>(e) + kTilePairs) * sizeof(int);
+    plan_count_kernel<KC><<<dim3(g.ntiles, ranks), kThreads, count_lds, stream>>>(g);
+  } else if (fused) {
     plan_assign_kernel<KC, true><<<dim3(g.nblocks, ranks), kThreads, assign_lds, stream>>>(g);
   } else {
     const size_t count_lds = (static_cast<size_t>(e) + kTilePairs) * sizeof(int);
@@ -494,9 +497,10 @@ size_t plan_workspace_bytes(const moe_problem &p) {
   return (bytes + 255) & ~static_cast<size_t>(255);
 }
 
-hipError_t launch_plan_ranks(const moe_problem &p, int ranks, const int32_t *ids,
-                             const moe_plan &plan, const PlanStrides &st, void *workspace,
-                             hipStream_t stream) {
+namespace {
+
+hipError_t launch_plan_impl(const moe_problem &p, int ranks, const int32_t *ids, const moe_plan &plan,
+                            const PlanStrides &st, void *workspace, hipStream_t stream, bool count_only) {
   const PlanGeom geo = plan_geometry(p);
   PlanArgs g;
   g.ids = ids;
@@ -533,14 +537,28 @@ hipError_t launch_plan_ranks(const moe_problem &p, int ranks, const int32_t *ids
   g.st_dest = st.dest;
   g.st_table = st.table;
   switch (p.top_k) {
-    case 1: launch_k<1>(g, geo.single, p.n_experts, ranks, stream); break;
-    case 2: launch_k<2>(g, geo.single, p.n_experts, ranks, stream); break;
-    case 4: launch_k<4>(g, geo.single, p.n_experts, ranks, stream); break;
-    case 6: launch_k<6>(g, geo.single, p.n_experts, ranks, stream); break;
-    case 8: launch_k<8>(g, geo.single, p.n_experts, ranks, stream); break;
-    default: launch_k<0>(g, geo.single, p.n_experts, ranks, stream); break;
+    case 1: launch_k<1>(g, geo.single, p.n_experts, ranks, stream, count_only); break;
+    case 2: launch_k<2>(g, geo.single, p.n_experts, ranks, stream, count_only); break;
+    case 4: launch_k<4>(g, geo.single, p.n_experts, ranks, stream, count_only); break;
+    case 6: launch_k<6>(g, geo.single, p.n_experts, ranks, stream, count_only); break;
+    case 8: launch_k<8>(g, geo.single, p.n_experts, ranks, stream, count_only); break;
+    default: launch_k<0>(g, geo.single, p.n_experts, ranks, stream, count_only); break;
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_plan_ranks(const moe_problem &p, int ranks, const int32_t *ids,
+                             const moe_plan &plan, const PlanStrides &st, void *workspace,
+                             hipStream_t stream) {
+  return launch_plan_impl(p, ranks, ids, plan, st, workspace, stream, false);
+}
+
+hipError_t launch_plan_count(const moe_problem &p, const int32_t *ids, void *workspace,
+                             hipStream_t stream) {
+  // only the workspace and the IDs are touched; the plan arrays stay unset
+  return launch_plan_impl(p, 1, ids, moe_plan{}, PlanStrides{}, workspace, stream, true);
 }
 
 hipError_t launch_plan(const moe_problem &p, const int32_t *ids, const moe_plan &plan,

@@ -23,6 +23,14 @@
 // the earlier pairs of that expert before the workgroup's tokens, plus those
 // among the workgroup's own earlier pairs).  One LDS atomic per ID, no
 // ballots, five barriers.
+//
+// Tiled mode (larger problems, two launches).  The counting kernel of
+// plan.hip first writes one histogram per count tile of T pairs (whole
+// tokens) and the tile's fault bits.  A workgroup then needs no more than
+// the histograms (each expert's total, and its count in the tiles before
+// the workgroup's own tile) and the IDs of its own tile up to the end of its
+// own pairs: at most T - 1 earlier pairs plus its own pairs.  The steps
+// after the counting are the same in both modes.
 #pragma once
 
 #include "moe_device.hpp"
@@ -34,6 +42,10 @@ constexpr int kSmallThreads = 256;   // one workgroup
 constexpr int kSmallWaves = kSmallThreads / kWave;
 constexpr int kSmallLoads = kSmallPairs / kSmallThreads;  // IDs per thread
 constexpr int kSmallTargets = kSmallThreads;              // own pairs, one per thread
+constexpr int kSmallIds = kSmallPairs + kSmallTargets;    // LDS IDs: tiled mode reads up to this many
+constexpr int kTileLoads = kSmallIds / kSmallThreads;     // IDs per thread in tiled mode
+constexpr int kTileHist = 2048;                           // histogram entries (tiles * E) a tiled plan reads
+constexpr int kTileHistLoads = kTileHist / kSmallThreads;
 static_assert(kMaxExperts <= 4 * kSmallThreads, "the expert scan gives each thread four experts");
 static_assert(kSmallTargets >= kSmallWaves * kMaxTopK, "own pairs: up to one token per wave");
 
@@ -42,27 +54,31 @@ struct SmallPlanArgs {
   int n, k, e, ep, a;
   int l;               // E / EP, experts per destination
   int64_t cap;         // recv_capacity (rows per destination)
+  // tiled mode only
+  const int32_t *hist;      // [ntiles][E] pairs per expert in each count tile
+  const uint32_t *tflags;   // [ntiles]    BAD_ID / DUP_ID bits of each tile
+  int ntiles, tile_tokens;  // ntiles * E <= kTileHist
 };
 
 // LDS arrays of a small plan (ints).
 struct SmallPlanLds {
-  int *ids;     // [kSmallPairs]   valid ID or -1
+  int *ids;     // [kSmallIds]     valid ID or -1, pairs lo .. (lo = 0 in small mode)
   int *tslot;   // [kSmallTargets] packed row of own pair p0 + j, or -1
-  int *cnt;     // [E]   pairs per expert
+  int *cnt;     // [E]   pairs per expert (while counting: those not before p0)
   int *before;  // [E]   pairs per expert before p0
   int *off;     // [E+1] padded exclusive cumsum, off[E] = R_used
   int *cpre;    // [E+1] unpadded exclusive cumsum
 };
 
 __host__ __device__ constexpr size_t small_plan_lds_bytes(int e) {
-  return (static_cast<size_t>(kSmallPairs) + kSmallTargets + 4 * static_cast<size_t>(e) + 2) *
+  return (static_cast<size_t>(kSmallIds) + kSmallTargets + 4 * static_cast<size_t>(e) + 2) *
          sizeof(int);
 }
 
 __device__ __forceinline__ SmallPlanLds small_plan_lds(int *smem, int e) {
   SmallPlanLds s;
   s.ids = smem;
-  s.tslot = s.ids + kSmallPairs;
+  s.tslot = s.ids + kSmallIds;
   s.cnt = s.tslot + kSmallTargets;
   s.before = s.cnt + e;
   s.off = s.before + e;
@@ -73,14 +89,146 @@ __device__ __forceinline__ SmallPlanLds small_plan_lds(int *smem, int e) {
 // Every ID of the problem, thread tid holding pairs u * 256 + tid (-1 past
 // the end).  Separate from small_plan so that a caller can issue other loads
 // before the IDs are first used.
+// Bounds-checked buffer loads, so no branch surrounds them.
 __device__ __forceinline__ void small_plan_load(const SmallPlanArgs &g, int (&v)[kSmallLoads]) {
   const int np = g.n * g.k;
+  const auto ids = buffer_rsrc(g.ids, static_cast<uint32_t>(np) * 4u);
 #pragma unroll
   for (int u = 0; u < kSmallLoads; ++u) {
     const int i = u * kSmallThreads + threadIdx.x;
-    v[u] = i < np ? g.ids[i] : -1;
+    const int x = __builtin_amdgcn_raw_buffer_load_b32(ids, i * 4, 0, kLoadDefault);
+    v[u] = i < np ? x : -1;
   }
 }
+
+// Tiled mode: the IDs of pairs lo .. lo+len-1 (len <= kSmallIds), every
+// tile histogram and every tile's fault bits.
+struct TileLoads {
+  int v[kTileLoads];
+  int h[kTileHistLoads];
+  uint32_t fl;
+};
+
+// Bounds-checked buffer loads (zero past each array's end), so no branch
+// surrounds them.
+__device__ __forceinline__ void tile_plan_load(const SmallPlanArgs &g, int lo, int len, TileLoads &l) {
+  const int tid = threadIdx.x;
+  const auto ids = buffer_rsrc(g.ids + lo, static_cast<uint32_t>(len) * 4u);
+#pragma unroll
+  for (int u = 0; u < kTileLoads; ++u) {
+    const int i = u * kSmallThreads + tid;
+    const int x = __builtin_amdgcn_raw_buffer_load_b32(ids, i * 4, 0, kLoadDefault);
+    l.v[u] = i < len ? x : -1;
+  }
+  const auto hist = buffer_rsrc(g.hist, static_cast<uint32_t>(g.ntiles * g.e) * 4u);
+#pragma unroll
+  for (int u = 0; u < kTileHistLoads; ++u)
+    l.h[u] = __builtin_amdgcn_raw_buffer_load_b32(hist, (u * kSmallThreads + tid) * 4, 0, kLoadDefault);
+  const auto tfl = buffer_rsrc(g.tflags, static_cast<uint32_t>(g.ntiles) * 4u);
+  uint32_t fl = 0;
+#pragma unroll
+  for (int u = 0; u < kTileHistLoads; ++u)  // ntiles <= kTileHist
+    fl |= __builtin_amdgcn_raw_buffer_load_b32(tfl, (u * kSmallThreads + tid) * 4, 0, kLoadDefault);
+  l.fl = fl;
+}
+
+namespace detail {
+
+// Common end of both modes, after before[e] holds the pairs of expert e
+// ahead of p0 and cnt[e] its total (TOTAL) or its pairs from p0 on, and
+// ids[p - lo] the IDs of the own pairs [p0, p1): padded and unpadded scans,
+// own slots, capacity, status.  `fl` holds this thread's fault bits so far.
+// Starts and ends with a barrier.
+template <bool TOTAL>
+__device__ uint32_t plan_finish(const SmallPlanArgs &g, const SmallPlanLds &s, int lo, int p0, int p1,
+                                uint32_t fl) {
+  __shared__ int s_scan[2][kSmallWaves];
+  __shared__ uint32_t s_fl;
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int E = g.e;
+  if (tid == 0) s_fl = 0;
+  __syncthreads();
+
+  // ---- totals; padded and unpadded exclusive scans (4 experts a thread) ---
+  {
+    const int e0 = 4 * tid;
+    int c[4], p[4], sc = 0, sp = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      c[q] = e0 + q < E ? s.cnt[e0 + q] + (TOTAL ? 0 : s.before[e0 + q]) : 0;
+      // no integer division when there is no padding (a long dependent chain)
+      p[q] = g.a == 1 ? c[q] : ((c[q] + g.a - 1) / g.a) * g.a;
+      sc += c[q];
+      sp += p[q];
+    }
+    const int ip = wave_incl_scan(sp), ic = wave_incl_scan(sc);
+    if (lane == kWave - 1) {
+      s_scan[0][wave] = ip;
+      s_scan[1][wave] = ic;
+    }
+    __syncthreads();
+    int xp = ip - sp, xc = ic - sc, tp = 0, tc = 0;
+#pragma unroll
+    for (int w = 0; w < kSmallWaves; ++w) {
+      xp += w < wave ? s_scan[0][w] : 0;
+      xc += w < wave ? s_scan[1][w] : 0;
+      tp += s_scan[0][w];
+      tc += s_scan[1][w];
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (e0 + q < E) {
+        s.cnt[e0 + q] = c[q];  // each thread rewrites only the experts it read
+        s.off[e0 + q] = xp;
+        s.cpre[e0 + q] = xc;
+      }
+      xp += p[q];
+      xc += c[q];
+    }
+    if (tid == 0) {
+      s.off[E] = tp;
+      s.cpre[E] = tc;
+    }
+  }
+  __syncthreads();
+
+  // ---- slots of the own pairs; capacity of every destination --------------
+  {
+    const int j = tid;
+    if (j < p1 - p0) {
+      const int *own = s.ids + (p0 - lo);
+      const int e = own[j];
+      int sl = -1;
+      if (e >= 0) {
+        int r = s.before[e];
+        // equal IDs among the own earlier pairs, 16 LDS reads in flight at a time
+        for (int q0 = 0; q0 < j; q0 += 16) {
+          int w[16];
+#pragma unroll
+          for (int q = 0; q < 16; ++q) w[q] = q0 + q < j ? own[q0 + q] : -1;
+#pragma unroll
+          for (int q = 0; q < 16; ++q) r += w[q] == e ? 1 : 0;
+        }
+        sl = s.off[e] + r;
+      }
+      s.tslot[j] = sl;
+    }
+  }
+  const int L = g.l;
+  for (int r = tid; r < g.ep; r += kSmallThreads)
+    if (s.cpre[(r + 1) * L] - s.cpre[r * L] > g.cap) fl |= MOE_STATUS_CAPACITY;
+  const uint64_t b0 = ballot(fl & MOE_STATUS_BAD_ID), b1 = ballot(fl & MOE_STATUS_DUP_ID),
+                 b2 = ballot(fl & MOE_STATUS_CAPACITY);
+  const uint32_t wfl = (b0 ? MOE_STATUS_BAD_ID : 0u) | (b1 ? MOE_STATUS_DUP_ID : 0u) |
+                       (b2 ? MOE_STATUS_CAPACITY : 0u);
+  if (lane == 0 && wfl) atomicOr(&s_fl, wfl);
+  __syncthreads();
+  return s_fl;
+}
+
+}  // namespace detail
 
 // Fills cnt, off, cpre and ids for the whole problem and tslot[0 .. p1-p0)
 // for the workgroup's own pairs [p0, p1) (p1 - p0 <= kSmallTargets, whole
@@ -88,11 +236,7 @@ __device__ __forceinline__ void small_plan_load(const SmallPlanArgs &g, int (&v)
 // check_dup), the same for every thread.  Ends with a barrier.
 __device__ uint32_t small_plan(const SmallPlanArgs &g, const SmallPlanLds &s, const int (&v)[kSmallLoads],
                                int p0, int p1, bool check_dup) {
-  __shared__ uint32_t s_fl;
-  __shared__ int s_scan[2][kSmallWaves];
   const int tid = threadIdx.x;
-  const int lane = lane_id();
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int E = g.e;
   const int np = g.n * g.k;
 
@@ -100,7 +244,6 @@ __device__ uint32_t small_plan(const SmallPlanArgs &g, const SmallPlanLds &s, co
     s.cnt[e] = 0;
     s.before[e] = 0;
   }
-  if (tid == 0) s_fl = 0;
   uint32_t fl = 0;
   int e_own[kSmallLoads];
 #pragma unroll
@@ -147,83 +290,67 @@ __device__ uint32_t small_plan(const SmallPlanArgs &g, const SmallPlanLds &s, co
       }
     }
   }
-  __syncthreads();
+  return detail::plan_finish<false>(g, s, 0, p0, p1, fl);
+}
 
-  // ---- totals; padded and unpadded exclusive scans (4 experts a thread) ---
-  {
-    const int e0 = 4 * tid;
-    int c[4], p[4], sc = 0, sp = 0;
+__device__ __forceinline__ int tile_id(const SmallPlanArgs &g, int v) {
+  return v < -1 || v >= g.e ? -1 : v;  // counted as masked (the tile's bits say BAD_ID)
+}
+
+// Tiled mode, first step: clears the counters and stores the IDs loaded by
+// tile_plan_load(g, lo, len, l) into ids.  Ends with a barrier, so the IDs
+// have arrived when it returns.
+__device__ void tile_plan_stage(const SmallPlanArgs &g, const SmallPlanLds &s, const TileLoads &l, int len) {
+  const int tid = threadIdx.x;
+  for (int e = tid; e < g.e; e += kSmallThreads) {
+    s.cnt[e] = 0;
+    s.before[e] = 0;
+  }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      c[q] = e0 + q < E ? s.cnt[e0 + q] + s.before[e0 + q] : 0;
-      // no integer division when there is no padding (a long dependent chain)
-      p[q] = g.a == 1 ? c[q] : ((c[q] + g.a - 1) / g.a) * g.a;
-      sc += c[q];
-      sp += p[q];
-    }
-    const int ip = wave_incl_scan(sp), ic = wave_incl_scan(sc);
-    if (lane == kWave - 1) {
-      s_scan[0][wave] = ip;
-      s_scan[1][wave] = ic;
-    }
-    __syncthreads();
-    int xp = ip - sp, xc = ic - sc, tp = 0, tc = 0;
-#pragma unroll
-    for (int w = 0; w < kSmallWaves; ++w) {
-      xp += w < wave ? s_scan[0][w] : 0;
-      xc += w < wave ? s_scan[1][w] : 0;
-      tp += s_scan[0][w];
-      tc += s_scan[1][w];
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if (e0 + q < E) {
-        s.cnt[e0 + q] = c[q];  // each thread rewrites only the experts it read
-        s.off[e0 + q] = xp;
-        s.cpre[e0 + q] = xc;
-      }
-      xp += p[q];
-      xc += c[q];
-    }
-    if (tid == 0) {
-      s.off[E] = tp;
-      s.cpre[E] = tc;
-    }
+  for (int u = 0; u < kTileLoads; ++u) {
+    const int i = u * kSmallThreads + tid;
+    if (i < len) s.ids[i] = tile_id(g, l.v[u]);
   }
   __syncthreads();
+}
 
-  // ---- slots of the own pairs; capacity of every destination --------------
-  {
-    const int j = tid;
-    if (j < p1 - p0) {
-      const int pr = p0 + j;
-      const int e = s.ids[pr];
-      int sl = -1;
-      if (e >= 0) {
-        int r = s.before[e];
-        // equal IDs among the own earlier pairs, 16 LDS reads in flight at a time
-        for (int q0 = 0; q0 < j; q0 += 16) {
-          int w[16];
+// Tiled mode, after tile_plan_stage: lo is the first pair of count tile c0,
+// the tile that holds pair p0 (p0 - lo < T, so p1 - lo <= kSmallIds).
+// Fills the same arrays as small_plan, with ids holding pairs lo .. p1-1.
+// The status bits are those of every tile (BAD_ID, DUP_ID) and CAPACITY.
+// Ends with a barrier.
+__device__ uint32_t tile_plan(const SmallPlanArgs &g, const SmallPlanLds &s, const TileLoads &l, int lo,
+                              int p0, int p1, int c0) {
+  const int tid = threadIdx.x;
+  const int E = g.e;
+
+  // ---- totals from the histograms, and the count before tile c0; then the
+  // pairs of tile c0 ahead of p0 ------------------------------------------
+  // entry i = u * 256 + tid of [ntiles][E] is (tile i / E, expert i % E)
+  const int dq = kSmallThreads / E, dr = kSmallThreads - dq * E;
+  int tt = tid / E, e = tid - tt * E;
 #pragma unroll
-          for (int q = 0; q < 16; ++q) w[q] = q0 + q < j ? s.ids[p0 + q0 + q] : -1;
-#pragma unroll
-          for (int q = 0; q < 16; ++q) r += w[q] == e ? 1 : 0;
-        }
-        sl = s.off[e] + r;
-      }
-      s.tslot[j] = sl;
+  for (int u = 0; u < kTileHistLoads; ++u) {
+    const int c = l.h[u];  // 0 past the last entry
+    if (c != 0) {
+      atomicAdd(&s.cnt[e], c);
+      if (tt < c0) atomicAdd(&s.before[e], c);
+    }
+    e += dr;
+    tt += dq;
+    if (e >= E) {
+      e -= E;
+      ++tt;
     }
   }
-  const int L = g.l;
-  for (int r = tid; r < g.ep; r += kSmallThreads)
-    if (s.cpre[(r + 1) * L] - s.cpre[r * L] > g.cap) fl |= MOE_STATUS_CAPACITY;
-  const uint64_t b0 = ballot(fl & MOE_STATUS_BAD_ID), b1 = ballot(fl & MOE_STATUS_DUP_ID),
-                 b2 = ballot(fl & MOE_STATUS_CAPACITY);
-  const uint32_t wfl = (b0 ? MOE_STATUS_BAD_ID : 0u) | (b1 ? MOE_STATUS_DUP_ID : 0u) |
-                       (b2 ? MOE_STATUS_CAPACITY : 0u);
-  if (lane == 0 && wfl) atomicOr(&s_fl, wfl);
-  __syncthreads();
-  return s_fl;
+  const int ahead = p0 - lo;
+#pragma unroll
+  for (int u = 0; u < kTileLoads; ++u) {
+    const int i = u * kSmallThreads + tid;
+    const int ev = tile_id(g, l.v[u]);
+    if (i < ahead && ev >= 0) atomicAdd(&s.before[ev], 1);
+  }
+  return detail::plan_finish<true>(g, s, lo, p0, p1, l.fl);
 }
 
 }  // namespace moe

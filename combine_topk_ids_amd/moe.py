@@ -23,12 +23,15 @@ MOE_OK, MOE_EINVAL, MOE_EALIGN, MOE_EOVERFLOW, MOE_EHIP = 0, -1, -2, -3, -4
 STATUS_BAD_ID, STATUS_DUP_ID, STATUS_CAPACITY, STATUS_MAP_OVERFLOW, STATUS_DROPPED = 1, 2, 4, 8, 16
 FMT = {"bf16": 0, "fp8": 1, "mxfp4": 2, "nvfp4": 3}
 FLAG_ZERO_TAIL = 1
+# how moe_plan_and_dispatch runs a problem (moe_plan_and_dispatch_mode)
+PD_ONE_LAUNCH, PD_TILED, PD_SEPARATE = 1, 2, 3
 
 # every symbol include/moe.h declares
 EXPORTS = ("moe_check_problem", "moe_max_rows", "moe_expert_capacity", "moe_payload_row_bytes",
            "moe_scale_row_bytes", "moe_workspace_bytes", "moe_dispatch_plan",
            "moe_dispatch", "moe_dispatch_scaled", "moe_dispatch_gated", "moe_plan_and_dispatch",
-           "moe_combine",
+           "moe_plan_and_dispatch_mode", "moe_plan_and_dispatch_begin",
+           "moe_plan_and_dispatch_end", "moe_combine",
            "moe_check_exchange", "moe_exchange_workspace_bytes", "moe_exchange_plan",
            "moe_exchange_dispatch", "moe_exchange_dispatch_scaled", "moe_exchange_dispatch_gated",
            "moe_exchange_combine", "moe_map_workspace_bytes",
@@ -80,6 +83,9 @@ def _load() -> ctypes.CDLL:
         "moe_dispatch": (ctypes.c_int, [P, ctypes.POINTER(Plan), V, V, V, V]),
         "moe_dispatch_gated": (ctypes.c_int, [P, ctypes.POINTER(Plan), V, V, V, V, V]),
         "moe_plan_and_dispatch": (ctypes.c_int, [P, V, ctypes.POINTER(Plan), V, V, V, V, V, V, V]),
+        "moe_plan_and_dispatch_mode": (ctypes.c_int, [P]),
+        "moe_plan_and_dispatch_begin": (ctypes.c_int, [P, V, ctypes.POINTER(Plan), V, V]),
+        "moe_plan_and_dispatch_end": (ctypes.c_int, [P, V, ctypes.POINTER(Plan), V, V, V, V, V, V, V]),
         "moe_dispatch_scaled": (ctypes.c_int, [P, ctypes.POINTER(Plan), V, V, V, V, V]),
         "moe_exchange_dispatch_scaled": (ctypes.c_int, [P, ctypes.POINTER(Exchange), V, V, V, V, V]),
         "moe_combine": (ctypes.c_int, [P, ctypes.POINTER(Plan), V, V, V, V]),
@@ -318,13 +324,8 @@ def moe_dispatch_gated(p: Problem, plan: PlanBuffers, hidden: torch.Tensor,
     _checked(rc, "moe_dispatch_gated")
 
 
-def moe_plan_and_dispatch(p: Problem, topk_ids: torch.Tensor, plan: PlanBuffers,
-                          hidden: torch.Tensor, payload: torch.Tensor, scales: torch.Tensor | None,
-                          topk_weights: torch.Tensor | None = None,
-                          input_scale: torch.Tensor | None = None, stream=None) -> None:
-    """moe_dispatch_plan then moe_dispatch (or the gated dispatch with
-    topk_weights, or the NVFP4 dispatch with input_scale), in one launch for
-    problems of at most 2048 pairs."""
+def _pd_args(p: Problem, topk_ids, plan: PlanBuffers, hidden, payload, scales, topk_weights,
+             input_scale):
     r_max, pb, sb, ws = _sizes(p)
     npairs = p.n_tokens * p.top_k
     ids = _dev(topk_ids, "topk_ids", (torch.int32,), npairs)
@@ -340,9 +341,49 @@ def moe_plan_and_dispatch(p: Problem, topk_ids: torch.Tensor, plan: PlanBuffers,
         raise ValueError("scales is smaller than R_max rows")
     pay = _dev(payload, "payload", _PAYLOAD)
     sc = _dev(scales, "scales", (torch.float32, torch.uint8))
-    rc = lib.moe_plan_and_dispatch(ctypes.byref(p), ids, ctypes.byref(plan.as_struct()), x, w, gs,
-                                   pay, sc or None, plan.workspace.data_ptr(), _stream(stream))
-    _checked(rc, "moe_plan_and_dispatch")
+    return (ctypes.byref(p), ids, ctypes.byref(plan.as_struct()), x, w, gs, pay, sc or None,
+            plan.workspace.data_ptr())
+
+
+def moe_plan_and_dispatch(p: Problem, topk_ids: torch.Tensor, plan: PlanBuffers,
+                          hidden: torch.Tensor, payload: torch.Tensor, scales: torch.Tensor | None,
+                          topk_weights: torch.Tensor | None = None,
+                          input_scale: torch.Tensor | None = None, stream=None) -> None:
+    """moe_dispatch_plan then moe_dispatch (or the gated dispatch with
+    topk_weights, or the NVFP4 dispatch with input_scale), in one or two
+    launches (moe_plan_and_dispatch_mode) where the problem allows."""
+    args = _pd_args(p, topk_ids, plan, hidden, payload, scales, topk_weights, input_scale)
+    _checked(lib.moe_plan_and_dispatch(*args, _stream(stream)), "moe_plan_and_dispatch")
+
+
+def moe_plan_and_dispatch_mode(p: Problem) -> int:
+    """PD_ONE_LAUNCH, PD_TILED or PD_SEPARATE."""
+    return _checked(lib.moe_plan_and_dispatch_mode(ctypes.byref(p)),
+                    "moe_plan_and_dispatch_mode")
+
+
+def moe_plan_and_dispatch_begin(p: Problem, topk_ids: torch.Tensor, plan: PlanBuffers,
+                                stream=None) -> None:
+    """The launches of moe_plan_and_dispatch that need only topk_ids."""
+    r_max, _, _, ws = _sizes(p)
+    npairs = p.n_tokens * p.top_k
+    ids = _dev(topk_ids, "topk_ids", (torch.int32,), npairs)
+    _dev(plan.slot, "plan.slot", (torch.int32,), npairs)
+    _dev(plan.packed_src, "plan.packed_src", (torch.int32,), r_max)
+    _dev(plan.workspace, "plan.workspace", (torch.uint8,), ws)
+    rc = lib.moe_plan_and_dispatch_begin(ctypes.byref(p), ids, ctypes.byref(plan.as_struct()),
+                                         plan.workspace.data_ptr(), _stream(stream))
+    _checked(rc, "moe_plan_and_dispatch_begin")
+
+
+def moe_plan_and_dispatch_end(p: Problem, topk_ids: torch.Tensor, plan: PlanBuffers,
+                              hidden: torch.Tensor, payload: torch.Tensor,
+                              scales: torch.Tensor | None, topk_weights: torch.Tensor | None = None,
+                              input_scale: torch.Tensor | None = None, stream=None) -> None:
+    """The launch of moe_plan_and_dispatch that writes the payload, after
+    moe_plan_and_dispatch_begin on the same stream."""
+    args = _pd_args(p, topk_ids, plan, hidden, payload, scales, topk_weights, input_scale)
+    _checked(lib.moe_plan_and_dispatch_end(*args, _stream(stream)), "moe_plan_and_dispatch_end")
 
 
 def moe_combine(p: Problem, plan: PlanBuffers, expert_out: torch.Tensor,

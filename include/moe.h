@@ -238,18 +238,51 @@ MOE_API int moe_dispatch_gated(const moe_problem *p, const moe_plan *plan,
  * (topk_weights = the gates) or moe_dispatch_scaled (MOE_FMT_NVFP4_B16:
  * input_scale required, topk_weights must be NULL), byte for byte.  NKI
  * permute_a2av API reference, description: one call computes the layout
- * from the routing and permutes the rows into it.  Problems with at most
- * 2048 (token, k) pairs and no fixed expert capacity run as one launch, in
- * which every workgroup computes the plan in LDS before its share of the
- * dispatch (decode shapes: one launch instead of two); larger ones run the
- * plan and dispatch launches.  workspace: moe_workspace_bytes(p) bytes (none
- * for the one-launch sizes).  Arguments, layouts and errors as in the calls
- * it replaces. */
+ * from the routing and permutes the rows into it.  How it runs
+ * (moe_plan_and_dispatch_mode): problems with at most 2048 (token, k) pairs
+ * and no fixed expert capacity run as one launch, in which every workgroup
+ * computes the plan in LDS before its share of the dispatch; larger ones
+ * without a fixed capacity whose count tiles times E is at most 2048 run
+ * the plan's counting kernel and then one launch in which every workgroup
+ * finishes the plan it needs from the tile histograms and dispatches; the
+ * rest run the plan's kernels and then the dispatch.  Equivalent to
+ * moe_plan_and_dispatch_begin followed by moe_plan_and_dispatch_end.
+ * workspace: moe_workspace_bytes(p) bytes (none for the one-launch sizes).
+ * Arguments, layouts and errors as in the calls it replaces. */
 MOE_API int moe_plan_and_dispatch(const moe_problem *p, const int32_t *topk_ids,
                                   const moe_plan *plan, const uint16_t *hidden,
                                   const float *topk_weights, const float *input_scale,
                                   void *payload, void *scales, void *workspace,
                                   void *stream);
+
+/* How moe_plan_and_dispatch runs problem p, as launches of its two halves
+ * (negative error code for an invalid problem):                           */
+#define MOE_PD_ONE_LAUNCH 1 /* _begin: nothing; _end: one launch that plans
+                               and dispatches                               */
+#define MOE_PD_TILED 2      /* _begin: the counting kernel (tile histograms
+                               into workspace); _end: one launch that
+                               finishes the plan and dispatches             */
+#define MOE_PD_SEPARATE 3   /* _begin: the plan (as moe_dispatch_plan);
+                               _end: the dispatch                           */
+MOE_API int moe_plan_and_dispatch_mode(const moe_problem *p);
+
+/* moe_plan_and_dispatch in two calls on one stream: _begin launches the
+ * work that needs only topk_ids, _end the launch that reads hidden and
+ * writes the payload (a single kernel, or none when there is nothing to
+ * write).  _begin can therefore be issued as soon as the router has written
+ * topk_ids.  Between the two, topk_ids, the plan arrays and the workspace
+ * must not be changed (for MOE_PD_TILED the workspace carries the tile
+ * histograms from _begin to _end).  The plan is complete only after _end.
+ * Both take the arguments of moe_plan_and_dispatch that they name and check
+ * them as it does. */
+MOE_API int moe_plan_and_dispatch_begin(const moe_problem *p, const int32_t *topk_ids,
+                                        const moe_plan *plan, void *workspace,
+                                        void *stream);
+MOE_API int moe_plan_and_dispatch_end(const moe_problem *p, const int32_t *topk_ids,
+                                      const moe_plan *plan, const uint16_t *hidden,
+                                      const float *topk_weights, const float *input_scale,
+                                      void *payload, void *scales, void *workspace,
+                                      void *stream);
 
 /* Combine: out[t][c] = bf16_rne( fp32 fused multiply-add chain, starting
  * from +0 and running over j = 0..k-1 in order, of

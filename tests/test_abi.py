@@ -136,6 +136,56 @@ def test_plan_and_dispatch_rejections(moe):
     assert call(ref(big), fake, ref(full), fake, None, None, fake, None, None, None) == -1
 
 
+def test_plan_and_dispatch_halves_reject_as_the_whole(moe):
+    """_begin checks the plan's arguments, _end those of the whole call; each
+    call below fails before anything is launched."""
+    ref = ctypes.byref
+    fake = 1 << 20
+    full = moe.Plan(*([fake] * 7))
+    part = moe.Plan(*([fake] * 6 + [0]))
+    p = moe.problem(64, 256, 2, 8, 4)
+    big = moe.problem(4096, 4096, 6, 64, 8)  # tiled: needs the workspace
+    begin, end = moe.lib.moe_plan_and_dispatch_begin, moe.lib.moe_plan_and_dispatch_end
+    assert begin(None, fake, ref(full), None, None) == -1
+    assert begin(ref(p), fake, ref(part), None, None) == -1
+    assert begin(ref(p), None, ref(full), None, None) == -1
+    assert begin(ref(p), fake + 2, ref(full), None, None) == -2
+    assert begin(ref(big), fake, ref(full), None, None) == -1
+    assert begin(ref(big), fake, ref(full), fake + 64, None) == -2
+    # end: the plan's checks, then the dispatch's
+    assert end(ref(p), fake, ref(part), fake, None, None, fake, None, None, None) == -1
+    assert end(ref(big), fake, ref(full), fake, None, None, fake, None, None, None) == -1
+    assert end(ref(p), fake, ref(full), None, None, None, fake, None, None, None) == -1
+    assert end(ref(p), fake, ref(full), fake, None, fake, fake, None, None, None) == -1
+    assert end(ref(p), fake, ref(full), fake, None, None, fake, fake, None, None) == -1
+    assert end(ref(p), fake, ref(full), fake + 8, None, None, fake, None, None, None) == -2
+    pn = moe.problem(64, 256, 2, 8, 4, fmt="nvfp4")
+    assert end(ref(pn), fake, ref(full), fake, None, None, fake, fake, None, None) == -1
+    assert end(ref(pn), fake, ref(full), fake, fake, fake, fake, fake, None, None) == -1
+
+
+def test_plan_and_dispatch_mode(moe):
+    """One launch up to 2048 pairs; tiled while (count tiles of
+    floor(2048 / k) tokens) x E <= 2048; the plan's kernels then the
+    dispatch otherwise, and always with a fixed expert capacity."""
+    one, tiled, sep = moe.PD_ONE_LAUNCH, moe.PD_TILED, moe.PD_SEPARATE
+    mode = moe.moe_plan_and_dispatch_mode
+    assert mode(moe.problem(0, 64, 2, 4, 2)) == one
+    assert mode(moe.problem(256, 7168, 8, 256, 8)) == one             # 2048 pairs
+    assert mode(moe.problem(257, 7168, 8, 256, 8)) == tiled           # 2 tiles x 256
+    assert mode(moe.problem(4096, 4096, 6, 64, 8)) == tiled           # 13 tiles x 64
+    assert mode(moe.problem(300, 256, 8, 1024, 64)) == tiled          # 2 x 1024 = 2048
+    assert mode(moe.problem(513, 256, 8, 1024, 64)) == sep            # 3 x 1024
+    assert mode(moe.problem(2048 * 8, 64, 1, 8, 2)) == tiled          # k = 1: 8 tiles x 8
+    assert mode(moe.problem(8192, 7168, 8, 256, 8)) == sep            # 32 x 256
+    assert mode(moe.problem(16384, 4096, 8, 128, 16)) == sep          # 64 x 128
+    assert mode(moe.problem(100, 256, 4, 8, 2, expert_capacity=60)) == sep
+    assert mode(moe.problem(4096, 4096, 6, 64, 8, expert_capacity=384)) == sep
+    bad = moe.problem(64, 256, 2, 8, 4)
+    bad.hidden = 7
+    assert moe.lib.moe_plan_and_dispatch_mode(ctypes.byref(bad)) == -1
+
+
 def test_workspace_required_only_for_multi_tile_plans(moe):
     small = moe.problem(128, 7168, 8, 256, 8)          # 1024 pairs: one block
     big = moe.problem(16384, 4096, 8, 128, 16, pad_multiple=128)

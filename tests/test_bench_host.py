@@ -74,3 +74,9 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_paths_name_their_dispatch_kernel():
+    """The roofline names the kernel of the dispatch call on either path."""
+    for cls in (bench.Path, bench.ExchangePath):
+        assert callable(getattr(cls, "dispatch_kernel", None)), cls.__name__

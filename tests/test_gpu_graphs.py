@@ -1,4 +1,4 @@
-"""HIP-graph capture of the exchange, fixed-capacity, NVFP4 and one-launch
+"""HIP-graph capture of the exchange, fixed-capacity, NVFP4, one-launch and tiled
 plan-and-dispatch paths: every replay, with eager work and synchronisation
 between replays, reproduces the eager outputs, and the eager outputs equal
 the oracle's.  (No call clears
@@ -155,3 +155,47 @@ def test_graph_plan_and_dispatch(moe):
                           sc.view(np.uint8).reshape(sc.shape[0], -1))
     assert assert_combine_close(u16(ref[7]), oracle.combine(pl["slot"], inp["weights"],
                                                              inp["expert_out"])) == 0
+
+
+def test_graph_plan_and_dispatch_tiled(moe):
+    """The two halves of a tiled plan and dispatch (the counting kernel, then
+    one launch that finishes the plan and dispatches) with a combine."""
+    n, h, e, k, ep, a = 1500, 512, 64, 6, 8, 128
+    say(f"[graph plan+dispatch tiled] N={n} H={h} E={e} k={k} A={a} bf16")
+    rng = np.random.default_rng(12)
+    ids, wts = random_routing(rng, n, e, k, masked_frac=0.05)
+    x = random_bf16(rng, (n, h))
+    cap = n * min(k, e // ep)
+    r_max = oracle.max_rows(n, k, e, a)
+    y = random_bf16(rng, (r_max, h))
+    # every packed row is written (the tail too), so no scribbled byte survives
+    p = moe.problem(n, h, k, e, ep, recv_capacity=cap, pad_multiple=a, zero_tail=True)
+    assert moe.moe_plan_and_dispatch_mode(p) == moe.PD_TILED
+    plan = moe.alloc_plan(p)
+    payload, scales = moe.alloc_payload(p)
+    x_d, y_d = to_dev_bf16(x), to_dev_bf16(y)
+    ids_d, w_d = torch.from_numpy(ids).cuda(), torch.from_numpy(wts).cuda()
+    out = torch.empty((n, h), dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        moe.moe_plan_and_dispatch_begin(p, ids_d, plan)
+        moe.moe_plan_and_dispatch_end(p, ids_d, plan, x_d, payload, scales)
+        moe.moe_combine(p, plan, y_d, w_d, out)
+
+    outs = [plan.slot, plan.packed_src, plan.expert_offsets, plan.rank_table, plan.status,
+            payload, out]
+
+    def scribble():
+        for t in (plan.slot, plan.packed_src, plan.expert_offsets, plan.rank_table, plan.status):
+            t.fill_(-3)
+        payload.view(torch.uint8).fill_(0xEE)
+        out.fill_(7.0)
+
+    ref = capture_and_replay(step, outs, scribble)
+    pl = oracle.plan(ids, e, ep, a, cap, h)
+    pay, _ = oracle.dispatch("bf16", x, pl, zero_tail=True)
+    assert np.array_equal(ref[0].cpu().numpy(), pl["slot"])
+    assert np.array_equal(ref[1].cpu().numpy(), pl["packed_src"])
+    assert np.array_equal(ref[2].cpu().numpy(), pl["expert_offsets"])
+    assert np.array_equal(u16(ref[5]).reshape(r_max, -1), pay.view(np.uint16).reshape(r_max, -1))
+    assert assert_combine_close(u16(ref[6]), oracle.combine(pl["slot"], wts, y)) == 0

@@ -1,6 +1,8 @@
 """GPU parity of moe_plan_and_dispatch (the plan and the dispatch in one
-call; one launch for problems of at most 2048 pairs) against the CPU oracle,
-and against the two-call path byte for byte.
+call: one launch for problems of at most 2048 pairs; the counting kernel and
+one launch for problems of at most 2048 histogram entries (count tiles x
+experts); the plan's kernels and the dispatch otherwise) against the CPU
+oracle, and against the two-call path byte for byte.
 
 Bar: every plan array, the status word, every packed row (payload and
 scales, live, pad and tail rows) bit-exact.  Inputs come from the seeded
@@ -27,7 +29,7 @@ def moe():
 
 
 def run_pd(moe, *, ids, hidden, e, ep, a, fmt, cap, gates=None, gs=None, zero_tail=True,
-           two_calls=False):
+           two_calls=False, halves=False):
     n, k = ids.shape
     h = hidden.shape[1]
     p = moe.problem(n, h, k, e, ep, recv_capacity=cap, pad_multiple=a, fmt=fmt,
@@ -52,6 +54,10 @@ def run_pd(moe, *, ids, hidden, e, ep, a, fmt, cap, gates=None, gs=None, zero_ta
             moe.moe_dispatch_gated(p, plan, x_d, w_d, payload, scales)
         else:
             moe.moe_dispatch(p, plan, x_d, payload, scales)
+    elif halves:
+        moe.moe_plan_and_dispatch_begin(p, ids_d, plan)
+        moe.moe_plan_and_dispatch_end(p, ids_d, plan, x_d, payload, scales, topk_weights=w_d,
+                                      input_scale=gs_d)
     else:
         moe.moe_plan_and_dispatch(p, ids_d, plan, x_d, payload, scales, topk_weights=w_d,
                                   input_scale=gs_d)
@@ -101,12 +107,14 @@ def check_pd(moe, *, ids, hidden, e, ep, a, fmt, cap=None, gates=None, gs=None, 
             assert np.array_equal(g[ru:], x[ru:])
         else:
             assert np.all(g[ru:] == SENTINEL)
-    two = run_pd(moe, zero_tail=zero_tail, two_calls=True, **kw)
-    for key in PLAN_KEYS + ("status", "payload", "scales"):
-        if got[key] is None:
-            assert two[key] is None
-        else:
-            assert np.array_equal(np.asarray(got[key]), np.asarray(two[key])), key
+    # the plan and dispatch calls, and the two halves, give the same bytes
+    for other in (dict(two_calls=True), dict(halves=True)):
+        two = run_pd(moe, zero_tail=zero_tail, **other, **kw)
+        for key in PLAN_KEYS + ("status", "payload", "scales"):
+            if got[key] is None:
+                assert two[key] is None
+            else:
+                assert np.array_equal(np.asarray(got[key]), np.asarray(two[key])), (key, other)
     return got, pl
 
 
@@ -134,8 +142,15 @@ SHAPES = [
     (32, 64, 128, 64, 8, 2, "bf16", 0.1, True, True),     # k = 64
     (2000, 64, 12, 1, 3, 3, "bf16", 0.0, False, False),   # k = 1, 8 slot workgroups
     (77, 384, 32, 5, 4, 7, "fp8", 0.3, False, True),
-    (257, 256, 16, 8, 4, 1, "fp8", 0.0, False, True),     # 2056 pairs: plan and dispatch launches
-    (4096, 256, 64, 6, 8, 128, "bf16", 0.0, True, True),  # many count tiles: two launches
+    (257, 256, 16, 8, 4, 1, "fp8", 0.0, False, True),     # 2056 pairs: 2 count tiles, tiled
+    (4096, 256, 64, 6, 8, 128, "bf16", 0.0, True, True),  # 13 count tiles, tiled
+    (700, 6144, 8, 3, 4, 2, "bf16", 0.1, False, True),    # 3 slabs: a workgroup straddles two tiles
+    (5000, 64, 4, 1, 2, 1, "bf16", 0.0, True, False),     # k = 1: 2048-token tiles
+    (100, 128, 64, 64, 8, 2, "bf16", 0.1, False, True),   # k = 64: 32-token tiles
+    (300, 256, 1024, 8, 64, 1, "mxfp4", 0.1, False, True),  # 2 x 1024 = 2048 entries: the most tiled
+    (600, 256, 1024, 8, 64, 3, "bf16", 0.0, False, True),   # 3 x 1024 entries: separate launches
+    (3000, 384, 32, 5, 4, 7, "fp8", 0.3, True, True),     # tiled, quantised workgroup order
+    (2500, 1024, 128, 8, 8, 128, "mxfp4", 0.05, True, False),  # tiled, 128-row pads
 ]
 
 
@@ -155,7 +170,7 @@ def test_plan_and_dispatch_shapes(moe, idx):
 def test_plan_and_dispatch_nvfp4_shapes(moe):
     rng = np.random.default_rng(44)
     for n, h, e, k, ep, a, gs in ((128, 256, 32, 8, 4, 2, 3.0), (40, 64, 8, 3, 2, 5, 0.01),
-                                  (300, 96, 64, 6, 8, 1, 400.0)):
+                                  (300, 96, 64, 6, 8, 1, 400.0), (1500, 96, 64, 6, 8, 2, 7.0)):
         say(f"[plan+dispatch] nvfp4 N={n} H={h} E={e} k={k} A={a} gs={gs}")
         ids, _ = random_routing(rng, n, e, k, masked_frac=0.1)
         check_pd(moe, ids=ids, hidden=random_bf16(rng, (n, h)), e=e, ep=ep, a=a, fmt="nvfp4",
@@ -172,6 +187,15 @@ def test_plan_and_dispatch_faults_and_empty(moe):
     say("[plan+dispatch] DUP, BAD and CAPACITY in one launch")
     got, pl = check_pd(moe, ids=ids, hidden=random_bf16(rng, (n, 64)), e=e, ep=4, a=2,
                        fmt="bf16", cap=100)
+    assert got["status"] == 1 | 2 | 4
+    say("[plan+dispatch] DUP, BAD and CAPACITY, tiled (two count tiles)")
+    n = 1000
+    ids, _ = random_routing(rng, n, e, k)
+    ids[n - 1, 2] = ids[n - 1, 1]
+    ids[700, 0] = 99
+    ids[3, 3] = -2
+    got, pl = check_pd(moe, ids=ids, hidden=random_bf16(rng, (n, 64)), e=e, ep=4, a=2,
+                       fmt="bf16", cap=900)
     assert got["status"] == 1 | 2 | 4
     say("[plan+dispatch] N = 0 with pad rows and a zero tail")
     check_pd(moe, ids=np.zeros((0, 2), np.int32), hidden=np.zeros((0, 64), np.uint16), e=4,
