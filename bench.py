@@ -339,16 +339,21 @@ def _latencies(torch, path, step, iters, per_graph):
     torch.cuda.synchronize()
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
-    def clock(fn, reps):
+    def clock(fn, reps, rounds=5):
+        # median of `rounds` timed runs: the host-bound figures jump between runs
         for _ in range(5):
             fn()
         torch.cuda.synchronize()
-        s.record()
-        for _ in range(reps):
-            fn()
-        e.record()
-        torch.cuda.synchronize()
-        return s.elapsed_time(e) / reps * 1e3
+        per = max(reps // rounds, 1)
+        out = []
+        for _ in range(rounds):
+            s.record()
+            for _ in range(per):
+                fn()
+            e.record()
+            torch.cuda.synchronize()
+            out.append(s.elapsed_time(e) / per * 1e3)
+        return float(np.median(out))
 
     plain = clock(step, iters)
     ref = path.sets[0]["out"].clone()
