@@ -27,8 +27,10 @@ def moe():
 
 
 def run_path(moe, *, ids, weights, hidden, e, ep, a, fmt, cap=None, expert_out=None,
-             zero_tail=True, stream=None):
-    """plan + dispatch + combine on the GPU; identity experts if expert_out is None."""
+             zero_tail=True, stream=None, halves=False):
+    """plan + dispatch + combine on the GPU; identity experts if expert_out is None.
+    halves: the plan and dispatch as moe_plan_and_dispatch_begin + _end (the
+    calls bench.py times) instead of moe_dispatch_plan + moe_dispatch."""
     n, k = ids.shape
     h = hidden.shape[1]
     p = moe.problem(n, h, k, e, ep, recv_capacity=cap, pad_multiple=a, fmt=fmt,
@@ -47,8 +49,12 @@ def run_path(moe, *, ids, weights, hidden, e, ep, a, fmt, cap=None, expert_out=N
     out = torch.full((n, h), 7.0, dtype=torch.bfloat16, device="cuda")
     ctx = torch.cuda.stream(stream) if stream is not None else torch.cuda.stream(torch.cuda.current_stream())
     with ctx:
-        moe.moe_dispatch_plan(p, ids_d, plan)
-        moe.moe_dispatch(p, plan, x_d, payload, scales)
+        if halves:
+            moe.moe_plan_and_dispatch_begin(p, ids_d, plan)
+            moe.moe_plan_and_dispatch_end(p, ids_d, plan, x_d, payload, scales)
+        else:
+            moe.moe_dispatch_plan(p, ids_d, plan)
+            moe.moe_dispatch(p, plan, x_d, payload, scales)
         if expert_out is None:
             assert fmt == "bf16"
             y_d = payload
@@ -85,13 +91,14 @@ def payload_bytes_ref(fmt, x, pl, zero_tail):
 
 
 def check_full(moe, *, ids, weights, hidden, e, ep, a, fmt, cap=None, expert_out=None,
-               zero_tail=True, stream=None):
+               zero_tail=True, stream=None, halves=False):
     n, k = ids.shape
     h = hidden.shape[1]
     if cap is None:
         cap = n * min(k, e // ep)
     got = run_path(moe, ids=ids, weights=weights, hidden=hidden, e=e, ep=ep, a=a, fmt=fmt,
-                   cap=cap, expert_out=expert_out, zero_tail=zero_tail, stream=stream)
+                   cap=cap, expert_out=expert_out, zero_tail=zero_tail, stream=stream,
+                   halves=halves)
     pl = oracle.plan(ids, e, ep, a, cap, h)
     assert_plan_equal(got, pl)
     pay, sc = payload_bytes_ref(fmt, hidden, pl, zero_tail=True)
@@ -137,6 +144,28 @@ def test_workload_full_parity(moe, name):
         x = inp["hidden"]
         negz = x == 0x8000
         assert np.array_equal(got["out"][~negz], x[~negz])
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_workload_full_parity_bench_calls(moe, name):
+    """The same, through the calls and flags bench.py times: the plan and the
+    dispatch as moe_plan_and_dispatch_begin + _end (one launch, tiled or
+    separate by size), no zero tail (rows past R_used keep their bytes)."""
+    w = WORKLOADS[name]
+    p = moe.problem(w.n, w.h, w.k, w.e, w.ep, recv_capacity=w.capacity, pad_multiple=w.a,
+                    fmt=w.fmt)
+    mode = moe.moe_plan_and_dispatch_mode(p)
+    say(f"[parity halves] {name}: {w.describe()}; mode {mode}")
+    r_max = oracle.max_rows(w.n, w.k, w.e, w.a)
+    inp = make_inputs(w, seed=0, expert_rows=r_max)
+    got, pl, nonexact = check_full(moe, ids=inp["ids"], weights=inp["weights"],
+                                   hidden=inp["hidden"], e=w.e, ep=w.ep, a=w.a, fmt=w.fmt,
+                                   cap=w.capacity, expert_out=inp.get("expert_out"),
+                                   zero_tail=False, halves=True)
+    assert got["status"] == 0
+    assert nonexact == 0, f"{nonexact} combine outputs differ by one ulp"
+    if name == "uniform_bf16_n4096":
+        assert mode == moe.PD_TILED
 
 
 def test_fp8_workload_sampled_parity(moe):
