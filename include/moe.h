@@ -270,11 +270,13 @@ MOE_API int moe_plan_and_dispatch_mode(const moe_problem *p);
  * work that needs only topk_ids, _end the launch that reads hidden and
  * writes the payload (a single kernel, or none when there is nothing to
  * write).  _begin can therefore be issued as soon as the router has written
- * topk_ids.  Between the two, topk_ids, the plan arrays and the workspace
- * must not be changed (for MOE_PD_TILED the workspace carries the tile
- * histograms from _begin to _end).  The plan is complete only after _end.
- * Both take the arguments of moe_plan_and_dispatch that they name and check
- * them as it does. */
+ * topk_ids.  _end must follow a _begin of the same problem and arguments
+ * on the same stream: it reads what _begin wrote, and without it its
+ * results are undefined.  Between the two, topk_ids, the plan arrays and
+ * the workspace must not be changed (for MOE_PD_TILED the workspace carries
+ * the tile histograms from _begin to _end).  The plan is complete only
+ * after _end.  Both take the arguments of moe_plan_and_dispatch that they
+ * name and check them as it does. */
 MOE_API int moe_plan_and_dispatch_begin(const moe_problem *p, const int32_t *topk_ids,
                                         const moe_plan *plan, void *workspace,
                                         void *stream);
