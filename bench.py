@@ -326,6 +326,11 @@ def decode_latency(moe, torch, w, inp, iters=200, per_graph=16):
     out = dict(workload=w.name)
     if isinstance(path, Path):
         out["plan_and_dispatch"] = path.mode()
+    # discarded passes first: the first graph figures measured in a process
+    # came out high (up to twice the later ones), whatever the graph held
+    _latencies(torch, path, lambda: path.step(0), iters, per_graph)
+    if isinstance(path, Path):
+        _latencies(torch, path, lambda: path.step_three_calls(0), iters, per_graph)
     out.update(_latencies(torch, path, lambda: path.step(0), iters, per_graph))
     if isinstance(path, Path):
         out["three_calls"] = _latencies(torch, path, lambda: path.step_three_calls(0), iters,
