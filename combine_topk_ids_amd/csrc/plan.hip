@@ -34,6 +34,9 @@
 //                block 0 also writes counts, offsets, table and status.
 // Plans of at most 2048 pairs (decode shapes) skip plan_count: the whole
 // problem is one count tile that every plan_assign block counts itself.
+// plan_count alone (launch_plan_count) also serves the tiled mode of the
+// plan-and-dispatch call, whose dispatch workgroups then finish the plan
+// from its histograms (small_plan.hpp) instead of plan_assign.
 //
 // Latency matters more than bandwidth here (the whole plan moves < 2 MB):
 // each kernel issues its global loads first, keeps every intermediate in LDS

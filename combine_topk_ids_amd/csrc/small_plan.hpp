@@ -1,6 +1,8 @@
-// small_plan.hpp -- the routing plan of a small problem (at most 2048
-// (token, k) pairs) computed inside one 256-thread workgroup, in LDS, so
-// that a kernel can plan and dispatch in one launch.
+// small_plan.hpp -- the part of the routing plan one 256-thread workgroup
+// needs, computed in LDS, so that a kernel can plan and dispatch in one
+// launch: from all the IDs of a small problem (at most 2048 (token, k)
+// pairs), or in tiled mode from the tile histograms of plan.hip's counting
+// kernel.
 //
 // What is computed is the plan of plan.hip, for problems without a fixed
 // expert capacity (pages cited by title and section):
@@ -64,7 +66,7 @@ struct SmallPlanArgs {
 struct SmallPlanLds {
   int *ids;     // [kSmallIds]     valid ID or -1, pairs lo .. (lo = 0 in small mode)
   int *tslot;   // [kSmallTargets] packed row of own pair p0 + j, or -1
-  int *cnt;     // [E]   pairs per expert (while counting: those not before p0)
+  int *cnt;     // [E]   pairs per expert (while counting, small mode: those from p0 on)
   int *before;  // [E]   pairs per expert before p0
   int *off;     // [E+1] padded exclusive cumsum, off[E] = R_used
   int *cpre;    // [E+1] unpadded exclusive cumsum
@@ -88,8 +90,8 @@ __device__ __forceinline__ SmallPlanLds small_plan_lds(int *smem, int e) {
 
 // Every ID of the problem, thread tid holding pairs u * 256 + tid (-1 past
 // the end).  Separate from small_plan so that a caller can issue other loads
-// before the IDs are first used.
-// Bounds-checked buffer loads, so no branch surrounds them.
+// before the IDs are first used.  Bounds-checked buffer loads, so no branch
+// surrounds them.
 __device__ __forceinline__ void small_plan_load(const SmallPlanArgs &g, int (&v)[kSmallLoads]) {
   const int np = g.n * g.k;
   const auto ids = buffer_rsrc(g.ids, static_cast<uint32_t>(np) * 4u);
