@@ -151,6 +151,8 @@ SHAPES = [
     (600, 256, 1024, 8, 64, 3, "bf16", 0.0, False, True),   # 3 x 1024 entries: separate launches
     (3000, 384, 32, 5, 4, 7, "fp8", 0.3, True, True),     # tiled, quantised workgroup order
     (2500, 1024, 128, 8, 8, 128, "mxfp4", 0.05, True, False),  # tiled, 128-row pads
+    (3000, 128, 100, 4, 5, 3, "bf16", 0.1, False, True),  # tiled, E = 100 (does not divide 256)
+    (4000, 128, 12, 2, 3, 1, "fp8", 0.0, True, False),    # tiled, E = 12
 ]
 
 
