@@ -16,12 +16,15 @@
 // Without weights (rows gated at dispatch: DeepSpeed v0.19.4 function index,
 // page 15, pre-multiplying by router scores) every w is 1.
 //
-// Design for gfx950.  One wave64 per (token, 1024-column slab); each lane
-// owns 8 consecutive columns (one 16-byte bf16 vector) of two 512-column
-// chunks.  The token's k slots and gate weights are loaded once, one per
+// Design for gfx950.  One wave64 per (token, column slab); each lane owns 8
+// consecutive columns (one 16-byte bf16 vector) of every 512-column chunk of
+// the slab.  Slabs are 1024 columns when the expert rows are read with
+// cache-allocating loads and 2048 columns when they are streamed (longer
+// runs of each row per wave measured faster there, and slower on the cached
+// path).  The token's k slots and gate weights are loaded once, one per
 // lane, and broadcast with readlane; all k row loads of the slab are issued
 // before the first FMA, so each wave makes two round trips to memory (index
-// loads, then row loads) and keeps k x 2 KiB in flight.
+// loads, then row loads) and keeps k x 2 or 4 KiB in flight.
 #include "moe_device.hpp"
 #include "moe_kernels.hpp"
 
@@ -31,13 +34,17 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Tuning knobs (build-time): 16-byte vectors per lane in a slab (columns
-// per wave = 512 * MOE_COMBINE_VEC); the footprint of expert rows up to
-// which they are read with ordinary (cache-allocating) loads -- rows written
-// just before, e.g. by the expert GEMM or, for identity experts, by the
-// dispatch, are then still in the 256 MB Infinity Cache -- and beyond which
-// with non-temporal loads that do not churn the caches.
+// per wave = 512 * vectors) with cache-allocating and with non-temporal row
+// loads; the footprint of expert rows up to which they are read with
+// ordinary (cache-allocating) loads -- rows written just before, e.g. by the
+// expert GEMM or, for identity experts, by the dispatch, are then still in
+// the 256 MB Infinity Cache -- and beyond which with non-temporal loads that
+// do not churn the caches.
 #ifndef MOE_COMBINE_VEC
 #define MOE_COMBINE_VEC 2
+#endif
+#ifndef MOE_COMBINE_VEC_NT
+#define MOE_COMBINE_VEC_NT 4
 #endif
 #ifndef MOE_COMBINE_CACHED_BYTES
 #define MOE_COMBINE_CACHED_BYTES (256ll << 20)
@@ -45,7 +52,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kVec = MOE_COMBINE_VEC;  // 16-byte vectors per lane per slab
+// 16-byte vectors per lane per slab, by load kind
+template <bool NT>
+constexpr int vec_of() { return NT ? MOE_COMBINE_VEC_NT : MOE_COMBINE_VEC; }
 constexpr int kBatch = 8;   // top-k slots whose loads are issued together
 
 struct CombineArgs {
@@ -82,6 +91,7 @@ __device__ __forceinline__ u32x4 pack8(const float (&a)[8]) {
 // NT: non-temporal expert-row loads.
 template <int KC, bool NT>
 __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs g) {
+  constexpr int kVec = vec_of<NT>();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int q = blockIdx.x * kWaves + wave;  // the grid size keeps q within int
   const int t = q / g.slabs;
@@ -160,17 +170,18 @@ hipError_t launch_combine(const moe_problem &p, const moe_plan &plan, const uint
   g.n = p.n_tokens;
   g.k = p.top_k;
   g.h = p.hidden;
-  const int slab_cols = kWave * kVec * 8;
+  // bytes of expert rows this launch reads (one row per valid pair at most)
+  const int64_t rows_bytes = p.n_tokens * p.top_k * 2 * static_cast<int64_t>(p.hidden);
+  const bool nt = rows_bytes > MOE_COMBINE_CACHED_BYTES;
+  const int slab_cols = kWave * (nt ? vec_of<true>() : vec_of<false>()) * 8;
   g.slabs = (p.hidden + slab_cols - 1) / slab_cols;
   const int64_t waves = p.n_tokens * g.slabs;
   const int grid = static_cast<int>((waves + kWaves - 1) / kWaves);
   if (grid == 0) return hipSuccess;
-  // bytes of expert rows this launch reads (one row per valid pair at most)
-  const int64_t rows_bytes = p.n_tokens * p.top_k * 2 * static_cast<int64_t>(p.hidden);
-  if (rows_bytes <= MOE_COMBINE_CACHED_BYTES)
-    launch_k<false>(g, p.top_k, grid, stream);
-  else
+  if (nt)
     launch_k<true>(g, p.top_k, grid, stream);
+  else
+    launch_k<false>(g, p.top_k, grid, stream);
   return hipGetLastError();
 }
 
