@@ -168,16 +168,19 @@ def test_workload_full_parity_bench_calls(moe, name):
         assert mode == moe.PD_TILED
 
 
-def test_fp8_workload_sampled_parity(moe):
+@pytest.mark.parametrize("halves", [False, True], ids=["three_calls", "bench_calls"])
+def test_fp8_workload_sampled_parity(moe, halves):
     """FP8 1x128 workload at full size (N=8192, H=7168, E=256, k=8, EP=32):
-    whole plan, and sampled tokens' packed rows, scales and combine rows."""
+    whole plan, and sampled tokens' packed rows, scales and combine rows;
+    through the three calls, and through the calls and flags bench.py times
+    (moe_plan_and_dispatch_begin + _end, no zero tail)."""
     w = WORKLOADS["fp8_b128_n8192"]
-    say(f"[parity] {w.name}: {w.describe()}")
+    say(f"[parity] {w.name}: {w.describe()}; halves={halves}")
     r_max = oracle.max_rows(w.n, w.k, w.e, w.a)
     inp = make_inputs(w, seed=0, expert_rows=r_max)
     got = run_path(moe, ids=inp["ids"], weights=inp["weights"], hidden=inp["hidden"], e=w.e,
                    ep=w.ep, a=w.a, fmt="fp8", cap=w.capacity, expert_out=inp["expert_out"],
-                   zero_tail=True)
+                   zero_tail=not halves, halves=halves)
     pl = oracle.plan(inp["ids"], w.e, w.ep, w.a, w.capacity, w.h)
     assert_plan_equal(got, pl)
     assert got["status"] == 0
