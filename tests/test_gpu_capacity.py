@@ -28,7 +28,10 @@ def moe():
     return m
 
 
-def run_capacity(moe, *, ids, weights, hidden, e, ep, fmt, cap, rcap, expert_out=None):
+def run_capacity(moe, *, ids, weights, hidden, e, ep, fmt, cap, rcap, expert_out=None,
+                 halves=False):
+    """halves: the plan and dispatch as moe_plan_and_dispatch_begin + _end
+    (the calls bench.py times) instead of moe_dispatch_plan + moe_dispatch."""
     n, k = ids.shape
     h = hidden.shape[1]
     p = moe.problem(n, h, k, e, ep, recv_capacity=rcap, fmt=fmt, expert_capacity=cap)
@@ -40,8 +43,13 @@ def run_capacity(moe, *, ids, weights, hidden, e, ep, fmt, cap, rcap, expert_out
     if scales is not None:
         scales.view(torch.uint8).fill_(SENTINEL)
     out = torch.full((n, h), 7.0, dtype=torch.bfloat16, device="cuda")
-    moe.moe_dispatch_plan(p, torch.from_numpy(ids).cuda(), plan)
-    moe.moe_dispatch(p, plan, to_dev_bf16(hidden), payload, scales)
+    ids_d, x_d = torch.from_numpy(ids).cuda(), to_dev_bf16(hidden)
+    if halves:
+        moe.moe_plan_and_dispatch_begin(p, ids_d, plan)
+        moe.moe_plan_and_dispatch_end(p, ids_d, plan, x_d, payload, scales)
+    else:
+        moe.moe_dispatch_plan(p, ids_d, plan)
+        moe.moe_dispatch(p, plan, x_d, payload, scales)
     y = payload if expert_out is None else to_dev_bf16(expert_out)
     moe.moe_combine(p, plan, y, torch.from_numpy(weights).cuda(), out)
     torch.cuda.synchronize()
@@ -56,14 +64,14 @@ def run_capacity(moe, *, ids, weights, hidden, e, ep, fmt, cap, rcap, expert_out
 
 
 def check_capacity(moe, *, ids, weights, hidden, e, ep, fmt, cf, rcap=None, expert_out=None,
-                   sample_rows=None):
+                   sample_rows=None, halves=False):
     n, k = ids.shape
     h = hidden.shape[1]
     cap = oracle.expert_capacity(n, k, e, cf)
     assert moe.moe_expert_capacity(n, k, e, cf) == cap
     rcap = n * k if rcap is None else rcap
     got = run_capacity(moe, ids=ids, weights=weights, hidden=hidden, e=e, ep=ep, fmt=fmt,
-                       cap=cap, rcap=rcap, expert_out=expert_out)
+                       cap=cap, rcap=rcap, expert_out=expert_out, halves=halves)
     pl = oracle.capacity_plan(ids, e, ep, cap, rcap, h)
     for f in PLAN_KEYS:
         assert np.array_equal(got[f], pl[f]), f
@@ -86,20 +94,22 @@ def check_capacity(moe, *, ids, weights, hidden, e, ep, fmt, cf, rcap=None, expe
     return got, pl, assert_combine_close(got["out"], ref)
 
 
-def test_capacity_bf16_workload(moe):
+@pytest.mark.parametrize("halves", [False, True], ids=["three_calls", "bench_calls"])
+def test_capacity_bf16_workload(moe, halves):
     w = WORKLOADS["capacity_bf16_n4096"]
-    say(f"[capacity parity] {w.name}: {w.describe()}")
+    say(f"[capacity parity] {w.name}: {w.describe()}; halves={halves}")
     inp = make_inputs(w, seed=0)
     got, pl, nonexact = check_capacity(moe, ids=inp["ids"], weights=inp["weights"],
                                        hidden=inp["hidden"], e=w.e, ep=w.ep, fmt="bf16",
-                                       cf=w.capacity_factor, rcap=w.capacity)
+                                       cf=w.capacity_factor, rcap=w.capacity, halves=halves)
     assert got["status"] & 16  # factor 1.0: the busiest experts drop pairs
     assert nonexact == 0
 
 
-def test_capacity_fp8_workload_sampled(moe):
+@pytest.mark.parametrize("halves", [False, True], ids=["three_calls", "bench_calls"])
+def test_capacity_fp8_workload_sampled(moe, halves):
     w = WORKLOADS["capacity_fp8_n8192"]
-    say(f"[capacity parity] {w.name}: {w.describe()}")
+    say(f"[capacity parity] {w.name}: {w.describe()}; halves={halves}")
     cap = oracle.expert_capacity(w.n, w.k, w.e, w.capacity_factor)
     inp = make_inputs(w, seed=0, expert_rows=w.e * cap)
     rng = np.random.default_rng(99)
@@ -109,7 +119,7 @@ def test_capacity_fp8_workload_sampled(moe):
         return np.unique(np.concatenate([live[:2], live[-2:], rng.choice(live, 508, replace=False)]))
     check_capacity(moe, ids=inp["ids"], weights=inp["weights"], hidden=inp["hidden"], e=w.e,
                    ep=w.ep, fmt="fp8", cf=w.capacity_factor, rcap=w.capacity,
-                   expert_out=inp["expert_out"], sample_rows=sample)
+                   expert_out=inp["expert_out"], sample_rows=sample, halves=halves)
 
 
 # n, h, e, k, ep, fmt, capacity factor, masked fraction

@@ -24,7 +24,11 @@ def moe():
     return m
 
 
-def run_nvfp4(moe, *, ids, weights, hidden, e, ep, a, gs, expert_out, zero_tail=True):
+def run_nvfp4(moe, *, ids, weights, hidden, e, ep, a, gs, expert_out, zero_tail=True,
+              halves=False):
+    """halves: the plan and dispatch as moe_plan_and_dispatch_begin + _end
+    (the calls bench.py times) instead of moe_dispatch_plan +
+    moe_dispatch_scaled."""
     n, k = ids.shape
     h = hidden.shape[1]
     p = moe.problem(n, h, k, e, ep, pad_multiple=a, fmt="nvfp4", zero_tail=zero_tail)
@@ -34,8 +38,13 @@ def run_nvfp4(moe, *, ids, weights, hidden, e, ep, a, gs, expert_out, zero_tail=
     scales.fill_(SENTINEL)
     out = torch.full((n, h), 7.0, dtype=torch.bfloat16, device="cuda")
     gs_d = torch.tensor([gs], dtype=torch.float32, device="cuda")
-    moe.moe_dispatch_plan(p, torch.from_numpy(ids).cuda(), plan)
-    moe.moe_dispatch_scaled(p, plan, to_dev_bf16(hidden), gs_d, payload, scales)
+    ids_d, x_d = torch.from_numpy(ids).cuda(), to_dev_bf16(hidden)
+    if halves:
+        moe.moe_plan_and_dispatch_begin(p, ids_d, plan)
+        moe.moe_plan_and_dispatch_end(p, ids_d, plan, x_d, payload, scales, input_scale=gs_d)
+    else:
+        moe.moe_dispatch_plan(p, ids_d, plan)
+        moe.moe_dispatch_scaled(p, plan, x_d, gs_d, payload, scales)
     moe.moe_combine(p, plan, to_dev_bf16(expert_out), torch.from_numpy(weights).cuda(), out)
     torch.cuda.synchronize()
     return dict(slot=plan.slot.cpu().numpy(), payload=payload.cpu().numpy(),
@@ -43,11 +52,11 @@ def run_nvfp4(moe, *, ids, weights, hidden, e, ep, a, gs, expert_out, zero_tail=
                 status=int(plan.status.cpu().numpy().view(np.uint32)[0]))
 
 
-def check_nvfp4(moe, *, ids, weights, hidden, e, ep, a, gs, expert_out):
+def check_nvfp4(moe, *, ids, weights, hidden, e, ep, a, gs, expert_out, halves=False):
     n, k = ids.shape
     h = hidden.shape[1]
     got = run_nvfp4(moe, ids=ids, weights=weights, hidden=hidden, e=e, ep=ep, a=a, gs=gs,
-                    expert_out=expert_out)
+                    expert_out=expert_out, halves=halves)
     pl = oracle.plan(ids, e, ep, a, n * min(k, e // ep), h)
     assert np.array_equal(got["slot"], pl["slot"])
     pay, sc = oracle.dispatch_nvfp4(hidden, pl, gs, zero_tail=True)
@@ -57,16 +66,18 @@ def check_nvfp4(moe, *, ids, weights, hidden, e, ep, a, gs, expert_out):
     return got, assert_combine_close(got["out"], ref)
 
 
+@pytest.mark.parametrize("halves", [False, True], ids=["three_calls", "bench_calls"])
 @pytest.mark.parametrize("name", ["decode_nvfp4_n128", "nvfp4_b16_n8192"])
-def test_nvfp4_workload_parity(moe, name):
-    """Every packed row of the workload at full size."""
+def test_nvfp4_workload_parity(moe, name, halves):
+    """Every packed row of the workload at full size, through the three calls
+    and through the plan-and-dispatch halves bench.py times."""
     w = WORKLOADS[name]
-    say(f"[nvfp4 parity] {name}: {w.describe()}, gs={w.input_scale}")
+    say(f"[nvfp4 parity] {name}: {w.describe()}, gs={w.input_scale}; halves={halves}")
     r_max = oracle.max_rows(w.n, w.k, w.e, w.a)
     inp = make_inputs(w, seed=0, expert_rows=r_max)
     got, nonexact = check_nvfp4(moe, ids=inp["ids"], weights=inp["weights"], hidden=inp["hidden"],
                                 e=w.e, ep=w.ep, a=w.a, gs=w.input_scale,
-                                expert_out=inp["expert_out"])
+                                expert_out=inp["expert_out"], halves=halves)
     assert got["status"] == 0 and nonexact == 0
 
 
