@@ -334,10 +334,15 @@ def combine(slot: np.ndarray, w: np.ndarray | None, y: np.ndarray) -> np.ndarray
     y = np.ascontiguousarray(y, dtype=np.uint16)
     n, k = slot.shape
     h = y.shape[1]
+    # the C loop indexes y by slot: reject rows it does not have
+    if slot.size and slot.max() >= y.shape[0]:
+        raise ValueError(f"slot {int(slot.max())} names a row past the {y.shape[0]} rows of y")
     out = np.zeros((n, h), np.uint16)
     wp = None
     if w is not None:
         w = np.ascontiguousarray(w, dtype=np.float32)
+        if w.shape != slot.shape:
+            raise ValueError(f"weights {w.shape} do not match slot {slot.shape}")
         wp = _ptr(w)
     _load().oracle_combine(n, k, h, _ptr(slot), wp, _ptr(y), _ptr(out))
     return out

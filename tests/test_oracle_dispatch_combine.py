@@ -241,3 +241,15 @@ def test_combine_gather_cases(orc):
     yneg = np.full((1, h), 0x8000, np.uint16)  # -0.0
     out = orc.combine(np.zeros((2, 1), np.int32), np.ones((2, 1), np.float32), yneg)
     assert np.all(out == 0)
+
+
+def test_combine_rejects_rows_it_does_not_have(orc):
+    """The oracle's combine indexes y by slot; a slot past y's rows, or
+    weights of another shape, is refused before the C loop runs."""
+    rng = np.random.default_rng(8)
+    y = random_bf16(rng, (10, 16))
+    with pytest.raises(ValueError):
+        orc.combine(np.array([[3, 10]], np.int32), np.ones((1, 2), np.float32), y)
+    with pytest.raises(ValueError):
+        orc.combine(np.array([[3, 4]], np.int32), np.ones((1, 3), np.float32), y)
+    orc.combine(np.array([[3, 9]], np.int32), np.ones((1, 2), np.float32), y)  # in range
