@@ -18,10 +18,10 @@
 //
 // Design for gfx950.  One wave64 per (token, column slab); each lane owns 8
 // consecutive columns (one 16-byte bf16 vector) of every 512-column chunk of
-// the slab.  Slabs are 1024 columns when the expert rows are read with
-// cache-allocating loads and 2048 columns when they are streamed (longer
-// runs of each row per wave measured faster there, and slower on the cached
-// path).  The token's k slots and gate weights are loaded once, one per
+// the slab.  Slabs are 2048 columns when the expert rows are streamed
+// (longer runs of each row per wave measured faster there), 1024 when they
+// are read with cache-allocating loads, and 512 when 1024-column slabs would
+// give the launch too few waves to fill the GPU (decode shapes).  The token's k slots and gate weights are loaded once, one per
 // lane, and broadcast with readlane; all k row loads of the slab are issued
 // before the first FMA, so each wave makes two round trips to memory (index
 // loads, then row loads) and keeps k x 2 or 4 KiB in flight.
@@ -46,15 +46,16 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #ifndef MOE_COMBINE_VEC_NT
 #define MOE_COMBINE_VEC_NT 4
 #endif
+// fewest waves a cached-path launch should have; below it the slabs halve
+#ifndef MOE_COMBINE_MIN_WAVES
+#define MOE_COMBINE_MIN_WAVES 8192
+#endif
 #ifndef MOE_COMBINE_CACHED_BYTES
 #define MOE_COMBINE_CACHED_BYTES (256ll << 20)
 #endif
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-// 16-byte vectors per lane per slab, by load kind
-template <bool NT>
-constexpr int vec_of() { return NT ? MOE_COMBINE_VEC_NT : MOE_COMBINE_VEC; }
 constexpr int kBatch = 8;   // top-k slots whose loads are issued together
 
 struct CombineArgs {
@@ -88,10 +89,11 @@ __device__ __forceinline__ u32x4 pack8(const float (&a)[8]) {
 }
 
 // KC > 0: k is the compile-time constant KC; KC == 0: runtime k, in batches.
-// NT: non-temporal expert-row loads.
-template <int KC, bool NT>
+// NT: non-temporal expert-row loads.  VEC: 16-byte vectors per lane per
+// slab (512 * VEC columns per wave).
+template <int KC, bool NT, int VEC>
 __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs g) {
-  constexpr int kVec = vec_of<NT>();
+  constexpr int kVec = VEC;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int q = blockIdx.x * kWaves + wave;  // the grid size keeps q within int
   const int t = q / g.slabs;
@@ -146,15 +148,15 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs g) {
   }
 }
 
-template <bool NT>
+template <bool NT, int VEC>
 void launch_k(const CombineArgs &g, int k, int grid, hipStream_t stream) {
   switch (k) {
-    case 1: combine_kernel<1, NT><<<grid, kThreads, 0, stream>>>(g); break;
-    case 2: combine_kernel<2, NT><<<grid, kThreads, 0, stream>>>(g); break;
-    case 4: combine_kernel<4, NT><<<grid, kThreads, 0, stream>>>(g); break;
-    case 6: combine_kernel<6, NT><<<grid, kThreads, 0, stream>>>(g); break;
-    case 8: combine_kernel<8, NT><<<grid, kThreads, 0, stream>>>(g); break;
-    default: combine_kernel<0, NT><<<grid, kThreads, 0, stream>>>(g); break;
+    case 1: combine_kernel<1, NT, VEC><<<grid, kThreads, 0, stream>>>(g); break;
+    case 2: combine_kernel<2, NT, VEC><<<grid, kThreads, 0, stream>>>(g); break;
+    case 4: combine_kernel<4, NT, VEC><<<grid, kThreads, 0, stream>>>(g); break;
+    case 6: combine_kernel<6, NT, VEC><<<grid, kThreads, 0, stream>>>(g); break;
+    case 8: combine_kernel<8, NT, VEC><<<grid, kThreads, 0, stream>>>(g); break;
+    default: combine_kernel<0, NT, VEC><<<grid, kThreads, 0, stream>>>(g); break;
   }
 }
 
@@ -173,15 +175,19 @@ hipError_t launch_combine(const moe_problem &p, const moe_plan &plan, const uint
   // bytes of expert rows this launch reads (one row per valid pair at most)
   const int64_t rows_bytes = p.n_tokens * p.top_k * 2 * static_cast<int64_t>(p.hidden);
   const bool nt = rows_bytes > MOE_COMBINE_CACHED_BYTES;
-  const int slab_cols = kWave * (nt ? vec_of<true>() : vec_of<false>()) * 8;
-  g.slabs = (p.hidden + slab_cols - 1) / slab_cols;
+  auto slabs_of = [&](int vec) { return (p.hidden + kWave * vec * 8 - 1) / (kWave * vec * 8); };
+  int vec = nt ? MOE_COMBINE_VEC_NT : MOE_COMBINE_VEC;
+  if (!nt && vec > 1 && p.n_tokens * slabs_of(vec) < MOE_COMBINE_MIN_WAVES) vec = 1;
+  g.slabs = slabs_of(vec);
   const int64_t waves = p.n_tokens * g.slabs;
   const int grid = static_cast<int>((waves + kWaves - 1) / kWaves);
   if (grid == 0) return hipSuccess;
   if (nt)
-    launch_k<true>(g, p.top_k, grid, stream);
+    launch_k<true, MOE_COMBINE_VEC_NT>(g, p.top_k, grid, stream);
+  else if (vec == 1)
+    launch_k<false, 1>(g, p.top_k, grid, stream);
   else
-    launch_k<false>(g, p.top_k, grid, stream);
+    launch_k<false, MOE_COMBINE_VEC>(g, p.top_k, grid, stream);
   return hipGetLastError();
 }
 
