@@ -3,10 +3,12 @@
  * Instinct MI355X (gfx950).
  *
  * The library turns top-k expert IDs into a routing plan, packs token rows
- * into an expert-major buffer (optionally quantised to blockwise FP8 or
- * MX-FP4 on the way) and combines expert outputs back into token order,
- * weighted by the gate values.  Expert-parallel destination ranks are
- * simulated as contiguous segments of the one packed buffer.
+ * into an expert-major buffer (optionally quantised to blockwise FP8,
+ * MX-FP4 or NVFP4 on the way) and combines expert outputs back into token
+ * order, weighted by the gate values.  Expert-parallel destination ranks
+ * are simulated as contiguous segments of the one packed buffer, or, with
+ * the moe_exchange_* calls, as separate receive buffers of several
+ * simulated source ranks.
  *
  * Conventions for every entry point
  *   - Pointers named in a moe_plan, and every data pointer argument, are
