@@ -94,6 +94,19 @@ def _ptr(a: np.ndarray):
     return ctypes.c_void_p(a.ctypes.data)
 
 
+def _check_rows(idx: np.ndarray, n_rows: int, what: str) -> None:
+    """The C loops index an array of n_rows rows by idx (-1 skips)."""
+    if idx.size and (int(idx.max()) >= n_rows or int(idx.min()) < -1):
+        raise ValueError(f"{what} holds {int(idx.min())}..{int(idx.max())}, outside -1..{n_rows - 1}")
+
+
+def _check_buf(a: np.ndarray, shape, dtype, what: str) -> None:
+    """A caller-given output array the C loop writes whole."""
+    if a.shape != tuple(shape) or a.dtype != np.dtype(dtype) or not a.flags.c_contiguous:
+        raise ValueError(f"{what} must be a contiguous {np.dtype(dtype)} array of shape "
+                         f"{tuple(shape)}, not {a.dtype} {a.shape}")
+
+
 def max_rows(n: int, k: int, e: int, a: int) -> int:
     """R_max = N*k + E*(A-1)."""
     return int(_load().oracle_max_rows(n, k, e, a))
@@ -238,13 +251,20 @@ def dispatch(fmt: str, x: np.ndarray, pl: dict, zero_tail: bool = True,
     x = np.ascontiguousarray(x, dtype=np.uint16)
     h = x.shape[1]
     r_max = pl["r_max"]
+    src = np.ascontiguousarray(pl["packed_src"], dtype=np.int32)
+    if src.size < r_max:
+        raise ValueError(f"packed_src has {src.size} rows, fewer than R_max = {r_max}")
+    _check_rows(src[:r_max], x.shape[0], "packed_src")
     pdt, pshape, sdt, sshape = payload_shape(fmt, r_max, h)
     if payload is None:
         payload = np.zeros(pshape, pdt)
+    _check_buf(payload, pshape, pdt, "payload")
     if scales is None:
         scales = np.zeros(sshape, sdt if sdt is not None else np.uint8)
+    elif sdt is not None:
+        _check_buf(scales, sshape, sdt, "scales")
     _load().oracle_dispatch(FMT[fmt], h, r_max, pl["r_used"],
-                            _ptr(pl["packed_src"]), _ptr(x), _ptr(payload),
+                            _ptr(src), _ptr(x), _ptr(payload),
                             _ptr(scales), int(zero_tail))
     return payload, (scales if sdt is not None else None)
 
@@ -259,11 +279,17 @@ def dispatch_gated(fmt: str, x: np.ndarray, pl: dict, w: np.ndarray, zero_tail: 
     n, h = x.shape
     k = slot.shape[1]
     r_max = pl["r_max"]
+    if slot.shape[0] != n or w.shape != slot.shape:
+        raise ValueError(f"slot {slot.shape} and gates {w.shape} must both be [{n}, k]")
+    _check_rows(slot, r_max, "slot")
     pdt, pshape, sdt, sshape = payload_shape(fmt, r_max, h)
     if payload is None:
         payload = np.zeros(pshape, pdt)
+    _check_buf(payload, pshape, pdt, "payload")
     if scales is None:
         scales = np.zeros(sshape, sdt if sdt is not None else np.uint8)
+    elif sdt is not None:
+        _check_buf(scales, sshape, sdt, "scales")
     _load().oracle_dispatch_gated(FMT[fmt], n, k, h, r_max, pl["r_used"], _ptr(slot), _ptr(w),
                                   _ptr(x), _ptr(payload), _ptr(scales), int(zero_tail))
     return payload, (scales if sdt is not None else None)
@@ -291,6 +317,8 @@ def routing_map_to_topk(routing_map: np.ndarray, probs: np.ndarray | None, k: in
     m = np.ascontiguousarray(routing_map != 0, dtype=np.uint8)
     n, e = m.shape
     pr = None if probs is None else np.ascontiguousarray(probs, dtype=np.float32)
+    if pr is not None and pr.shape != m.shape:
+        raise ValueError(f"probs {pr.shape} must match the map {m.shape}")
     ids = np.zeros((n, k), np.int32)
     w = np.zeros((n, k), np.float32)
     st = np.zeros(1, np.uint32)
@@ -319,9 +347,13 @@ def dispatch_nvfp4(x: np.ndarray, pl: dict, gs: float, zero_tail: bool = True):
     x = np.ascontiguousarray(x, dtype=np.uint16)
     h = x.shape[1]
     r_max = pl["r_max"]
+    src = np.ascontiguousarray(pl["packed_src"], dtype=np.int32)
+    if src.size < r_max:
+        raise ValueError(f"packed_src has {src.size} rows, fewer than R_max = {r_max}")
+    _check_rows(src[:r_max], x.shape[0], "packed_src")
     pay = np.zeros((r_max, h // 2), np.uint8)
     sc = np.zeros((r_max, h // 16), np.uint8)
-    _load().oracle_dispatch_nvfp4(h, r_max, pl["r_used"], _ptr(np.ascontiguousarray(pl["packed_src"])),
+    _load().oracle_dispatch_nvfp4(h, r_max, pl["r_used"], _ptr(src),
                                   _ptr(x), float(gs), _ptr(pay), _ptr(sc), int(zero_tail))
     return pay, sc
 

@@ -253,3 +253,31 @@ def test_combine_rejects_rows_it_does_not_have(orc):
     with pytest.raises(ValueError):
         orc.combine(np.array([[3, 4]], np.int32), np.ones((1, 3), np.float32), y)
     orc.combine(np.array([[3, 9]], np.int32), np.ones((1, 2), np.float32), y)  # in range
+
+
+def test_dispatch_rejects_inputs_it_would_read_past(orc):
+    """packed_src naming a token x does not have, a short packed_src, gates of
+    another shape, or a caller payload of the wrong shape is refused before
+    the C loop runs."""
+    rng = np.random.default_rng(9)
+    x = random_bf16(rng, (4, 16))
+    pl = dict(packed_src=np.array([0, 3, -1, 4], np.int32), r_max=4, r_used=4,
+              slot=np.array([[0], [1], [3], [-1]], np.int32))
+    with pytest.raises(ValueError):
+        orc.dispatch("bf16", x, pl)
+    with pytest.raises(ValueError):
+        orc.dispatch("bf16", x, dict(pl, packed_src=np.array([0, 1], np.int32)))
+    with pytest.raises(ValueError):
+        orc.dispatch_nvfp4(random_bf16(rng, (4, 32)), pl, 1.0)
+    with pytest.raises(ValueError):
+        orc.dispatch_gated("bf16", x, pl, np.ones((4, 2), np.float32))
+    with pytest.raises(ValueError):
+        orc.dispatch_gated("bf16", x, dict(pl, slot=np.array([[0], [1], [4], [-1]], np.int32)),
+                           np.ones((4, 1), np.float32))
+    ok = dict(pl, packed_src=np.array([0, 3, -1, 2], np.int32))
+    with pytest.raises(ValueError):
+        orc.dispatch("bf16", x, ok, payload=np.zeros((3, 16), np.uint16))
+    pay, _ = orc.dispatch("bf16", x, ok)
+    assert np.array_equal(pay[1], x[3]) and np.all(pay[2] == 0)
+    with pytest.raises(ValueError):
+        orc.routing_map_to_topk(np.ones((2, 4), np.uint8), np.ones((2, 3), np.float32), 2)
