@@ -678,11 +678,12 @@ __global__ __launch_bounds__(kThreads) void plan_dispatch_kernel(PlanDispatchArg
   const RawSlab r = load_slab_buf<FMT, GATED>(d, t, slab, live);
   // the plan waits for its own loads only: the slab may still be in flight
   if constexpr (TILED) tile_plan_stage(g.sp, s, tl, p1 - tlo);
+  // only workgroup 0 reports the status
   uint32_t fl;
   if constexpr (TILED)
-    fl = tile_plan(g.sp, s, tl, tlo, p0, p1, c0);
+    fl = tile_plan(g.sp, s, tl, tlo, p0, c0, b == 0);
   else
-    fl = small_plan(g.sp, s, v, p0, p1, b == 0);
+    fl = small_plan(g.sp, s, v, p0, b == 0);
 
   if (b == 0) {
     for (int e = tid; e < E; e += kThreads) {
@@ -704,8 +705,9 @@ __global__ __launch_bounds__(kThreads) void plan_dispatch_kernel(PlanDispatchArg
       g.table[3 * g.sp.ep + rk] = static_cast<uint32_t>(s.off[lo]) * g.h;
     }
   }
-  // a token's slots and packed_src rows: written by the wave of its slab 0
-  const int my_slot = live && lane < k ? s.tslot[t * k + lane - p0] : -1;
+  // the wave's own token's slots, found by the wave itself; they and the
+  // token's packed_src rows are written by the wave of its slab 0
+  const int my_slot = live && lane < k ? own_slot(s, TILED ? tlo : 0, p0, t * k + lane) : -1;
   if (live && slab == 0 && lane < k) {
     g.slot[t * k + lane] = my_slot;
     if (my_slot >= 0) g.packed_src[my_slot] = t;

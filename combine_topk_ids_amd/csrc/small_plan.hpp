@@ -23,8 +23,11 @@
 // and unpadded offsets, and the slots of its own tokens' pairs only (at most
 // 4 tokens, so at most 256 pairs: a pair's slot is its expert's offset, plus
 // the earlier pairs of that expert before the workgroup's tokens, plus those
-// among the workgroup's own earlier pairs).  One LDS atomic per ID, no
-// ballots, five barriers.
+// among the workgroup's own earlier pairs).  Each wave finds the slots of
+// its own token's pairs itself (own_slot), so they need no barrier; only the
+// workgroup that reports the status gathers fault bits.  One LDS atomic per
+// ID, no ballots, three barriers: one more in the workgroup that reports
+// the status, and one more where E > 256.
 //
 // Tiled mode (larger problems, two launches).  The counting kernel of
 // plan.hip first writes one histogram per count tile of T pairs (whole
@@ -64,8 +67,7 @@ struct SmallPlanArgs {
 
 // LDS arrays of a small plan (ints).
 struct SmallPlanLds {
-  int *ids;     // [kSmallIds]     valid ID or -1, pairs lo .. (lo = 0 in small mode)
-  int *tslot;   // [kSmallTargets] packed row of own pair p0 + j, or -1
+  int *ids;     // [kSmallIds] valid ID or -1, pairs lo .. (lo = 0 in small mode)
   int *cnt;     // [E]   pairs per expert (while counting, small mode: those from p0 on)
   int *before;  // [E]   pairs per expert before p0
   int *off;     // [E+1] padded exclusive cumsum, off[E] = R_used
@@ -73,15 +75,13 @@ struct SmallPlanLds {
 };
 
 __host__ __device__ constexpr size_t small_plan_lds_bytes(int e) {
-  return (static_cast<size_t>(kSmallIds) + kSmallTargets + 4 * static_cast<size_t>(e) + 2) *
-         sizeof(int);
+  return (static_cast<size_t>(kSmallIds) + 4 * static_cast<size_t>(e) + 2) * sizeof(int);
 }
 
 __device__ __forceinline__ SmallPlanLds small_plan_lds(int *smem, int e) {
   SmallPlanLds s;
   s.ids = smem;
-  s.tslot = s.ids + kSmallIds;
-  s.cnt = s.tslot + kSmallTargets;
+  s.cnt = s.ids + kSmallIds;
   s.before = s.cnt + e;
   s.off = s.before + e;
   s.cpre = s.off + e + 1;
@@ -137,13 +137,12 @@ __device__ __forceinline__ void tile_plan_load(const SmallPlanArgs &g, int lo, i
 namespace detail {
 
 // Common end of both modes, after before[e] holds the pairs of expert e
-// ahead of p0 and cnt[e] its total (TOTAL) or its pairs from p0 on, and
-// ids[p - lo] the IDs of the own pairs [p0, p1): padded and unpadded scans,
-// own slots, capacity, status.  `fl` holds this thread's fault bits so far.
-// Starts and ends with a barrier.
+// ahead of p0 and cnt[e] its total (TOTAL) or its pairs from p0 on: padded
+// and unpadded scans, and, where `status`, capacity and the status bits (0
+// otherwise).  `fl` holds this thread's fault bits so far.  Starts and ends
+// with a barrier.
 template <bool TOTAL>
-__device__ uint32_t plan_finish(const SmallPlanArgs &g, const SmallPlanLds &s, int lo, int p0, int p1,
-                                uint32_t fl) {
+__device__ uint32_t plan_finish(const SmallPlanArgs &g, const SmallPlanLds &s, uint32_t fl, bool status) {
   __shared__ int s_scan[2][kSmallWaves];
   __shared__ uint32_t s_fl;
   const int tid = threadIdx.x;
@@ -166,18 +165,26 @@ __device__ uint32_t plan_finish(const SmallPlanArgs &g, const SmallPlanLds &s, i
       sp += p[q];
     }
     const int ip = wave_incl_scan(sp), ic = wave_incl_scan(sc);
-    if (lane == kWave - 1) {
-      s_scan[0][wave] = ip;
-      s_scan[1][wave] = ic;
-    }
-    __syncthreads();
-    int xp = ip - sp, xc = ic - sc, tp = 0, tc = 0;
+    int xp = ip - sp, xc = ic - sc, tp, tc;
+    if (E <= 4 * kWave) {
+      // wave 0 holds every expert: its totals are the problem's, and no
+      // other wave's scan is needed (E is the same for the whole workgroup)
+      tp = __builtin_amdgcn_readlane(ip, kWave - 1);
+      tc = __builtin_amdgcn_readlane(ic, kWave - 1);
+    } else {
+      if (lane == kWave - 1) {
+        s_scan[0][wave] = ip;
+        s_scan[1][wave] = ic;
+      }
+      __syncthreads();
+      tp = tc = 0;
 #pragma unroll
-    for (int w = 0; w < kSmallWaves; ++w) {
-      xp += w < wave ? s_scan[0][w] : 0;
-      xc += w < wave ? s_scan[1][w] : 0;
-      tp += s_scan[0][w];
-      tc += s_scan[1][w];
+      for (int w = 0; w < kSmallWaves; ++w) {
+        xp += w < wave ? s_scan[0][w] : 0;
+        xc += w < wave ? s_scan[1][w] : 0;
+        tp += s_scan[0][w];
+        tc += s_scan[1][w];
+      }
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -196,28 +203,8 @@ __device__ uint32_t plan_finish(const SmallPlanArgs &g, const SmallPlanLds &s, i
   }
   __syncthreads();
 
-  // ---- slots of the own pairs; capacity of every destination --------------
-  {
-    const int j = tid;
-    if (j < p1 - p0) {
-      const int *own = s.ids + (p0 - lo);
-      const int e = own[j];
-      int sl = -1;
-      if (e >= 0) {
-        int r = s.before[e];
-        // equal IDs among the own earlier pairs, 16 LDS reads in flight at a time
-        for (int q0 = 0; q0 < j; q0 += 16) {
-          int w[16];
-#pragma unroll
-          for (int q = 0; q < 16; ++q) w[q] = q0 + q < j ? own[q0 + q] : -1;
-#pragma unroll
-          for (int q = 0; q < 16; ++q) r += w[q] == e ? 1 : 0;
-        }
-        sl = s.off[e] + r;
-      }
-      s.tslot[j] = sl;
-    }
-  }
+  // ---- capacity of every destination; status --------------------------
+  if (!status) return 0;  // uniform: the whole workgroup skips the gather
   const int L = g.l;
   for (int r = tid; r < g.ep; r += kSmallThreads)
     if (s.cpre[(r + 1) * L] - s.cpre[r * L] > g.cap) fl |= MOE_STATUS_CAPACITY;
@@ -232,12 +219,36 @@ __device__ uint32_t plan_finish(const SmallPlanArgs &g, const SmallPlanLds &s, i
 
 }  // namespace detail
 
-// Fills cnt, off, cpre and ids for the whole problem and tslot[0 .. p1-p0)
-// for the workgroup's own pairs [p0, p1) (p1 - p0 <= kSmallTargets, whole
-// tokens).  Returns the status bits (BAD_ID, CAPACITY, and DUP_ID when
-// check_dup), the same for every thread.  Ends with a barrier.
+// Packed row of own pair p (p0 <= p < p1) after small_plan or tile_plan, or
+// -1 for a masked or invalid pair: its expert's offset, plus that expert's
+// pairs before p0, plus its equal IDs among the own pairs ahead of p.  Reads
+// only LDS that the plan's last barrier published, so a wave calls it for
+// its own token's pairs with no further barrier.
+__device__ __forceinline__ int own_slot(const SmallPlanLds &s, int lo, int p0, int p) {
+  const int e = s.ids[p - lo];
+  if (e < 0) return -1;
+  const int *own = s.ids + (p0 - lo);
+  const int j = p - p0;
+  int r = s.before[e];
+  // 16 LDS reads in flight at a time
+  for (int q0 = 0; q0 < j; q0 += 16) {
+    int w[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) w[q] = q0 + q < j ? own[q0 + q] : -1;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) r += w[q] == e ? 1 : 0;
+  }
+  return s.off[e] + r;
+}
+
+// Fills cnt, off, cpre and ids for the whole problem and before (each
+// expert's pairs ahead of p0, the workgroup's first pair); own_slot then
+// gives the slots of the own pairs (whole tokens from p0, at most
+// kSmallTargets pairs).  Where `status` (uniform in the workgroup), returns
+// the status bits (BAD_ID, DUP_ID, CAPACITY), the same for every thread; 0
+// otherwise.  Ends with a barrier.
 __device__ uint32_t small_plan(const SmallPlanArgs &g, const SmallPlanLds &s, const int (&v)[kSmallLoads],
-                               int p0, int p1, bool check_dup) {
+                               int p0, bool status) {
   const int tid = threadIdx.x;
   const int E = g.e;
   const int np = g.n * g.k;
@@ -270,7 +281,7 @@ __device__ uint32_t small_plan(const SmallPlanArgs &g, const SmallPlanLds &s, co
   }
   // repeated IDs within a token (only where the status is written); up to
   // 8 IDs a token are read together into registers
-  if (check_dup) {
+  if (status) {
     for (int t = tid; t < g.n; t += kSmallThreads) {
       const int *row = s.ids + t * g.k;
       if (g.k <= 8) {
@@ -292,7 +303,7 @@ __device__ uint32_t small_plan(const SmallPlanArgs &g, const SmallPlanLds &s, co
       }
     }
   }
-  return detail::plan_finish<false>(g, s, 0, p0, p1, fl);
+  return detail::plan_finish<false>(g, s, fl, status);
 }
 
 __device__ __forceinline__ int tile_id(const SmallPlanArgs &g, int v) {
@@ -317,12 +328,13 @@ __device__ void tile_plan_stage(const SmallPlanArgs &g, const SmallPlanLds &s, c
 }
 
 // Tiled mode, after tile_plan_stage: lo is the first pair of count tile c0,
-// the tile that holds pair p0 (p0 - lo < T, so p1 - lo <= kSmallIds).
-// Fills the same arrays as small_plan, with ids holding pairs lo .. p1-1.
-// The status bits are those of every tile (BAD_ID, DUP_ID) and CAPACITY.
-// Ends with a barrier.
+// the tile that holds pair p0 (p0 - lo < T, so the own pairs end at most
+// kSmallIds pairs after lo).  Fills the same arrays as small_plan, with ids
+// holding pairs lo .. p1-1.  Where `status`, the status bits are those of
+// every tile (BAD_ID, DUP_ID) and CAPACITY; 0 otherwise.  Ends with a
+// barrier.
 __device__ uint32_t tile_plan(const SmallPlanArgs &g, const SmallPlanLds &s, const TileLoads &l, int lo,
-                              int p0, int p1, int c0) {
+                              int p0, int c0, bool status) {
   const int tid = threadIdx.x;
   const int E = g.e;
 
@@ -352,7 +364,7 @@ __device__ uint32_t tile_plan(const SmallPlanArgs &g, const SmallPlanLds &s, con
     const int ev = tile_id(g, l.v[u]);
     if (i < ahead && ev >= 0) atomicAdd(&s.before[ev], 1);
   }
-  return detail::plan_finish<true>(g, s, lo, p0, p1, l.fl);
+  return detail::plan_finish<true>(g, s, l.fl, status);
 }
 
 }  // namespace moe

@@ -153,6 +153,8 @@ SHAPES = [
     (2500, 1024, 128, 8, 8, 128, "mxfp4", 0.05, True, False),  # tiled, 128-row pads
     (3000, 128, 100, 4, 5, 3, "bf16", 0.1, False, True),  # tiled, E = 100 (does not divide 256)
     (4000, 128, 12, 2, 3, 1, "fp8", 0.0, True, False),    # tiled, E = 12
+    (150, 128, 257, 8, 257, 2, "bf16", 0.1, False, True),  # E = 257: the scan spans two waves
+    (1000, 128, 260, 4, 4, 2, "fp8", 0.1, True, True),    # tiled, E = 260
 ]
 
 
