@@ -17,8 +17,9 @@ rotate over several copies of all buffers so that a step does not find its
 inputs in the 256 MB last-level cache from the step before.
 
 Per-kernel durations for the roofline (means, and p10/p50/p90 of each phase
-and of the step) come from HIP events recorded around every call on the
-stream the kernels run on, in a second pass over the same number of steps:
+and of the step) come from HIP timing events (no system-scope fence, see
+TimingEvent) recorded around every call on the stream the kernels run on,
+in a second pass over the same number of steps:
 "plan" is _begin, "dispatch" is _end (one kernel), "combine" the combine.
 ``payload_only`` repeats the rate counting only packed rows that hold a
 token.
@@ -277,8 +278,62 @@ def time_steps(torch, path, steps, warmup):
     return start.elapsed_time(end) / steps, wall
 
 
-def time_kernels(torch, path, steps):
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+class TimingEvent:
+    """A HIP event for timing only, recorded on torch's current stream (the
+    stream the library's kernels are launched on).  Created with
+    hipEventDisableSystemFence: recording it does not write back and
+    invalidate the caches at system scope, which a default event does, so
+    an interval between two such events adds about 1 µs to the kernel
+    inside it, against about 3 µs with default events.  The HIP runtime is
+    the one libmoe.so is linked against (the symbols are looked up through
+    its handle)."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000  # hipEventDisableSystemFence
+    _hip = None
+
+    @classmethod
+    def _runtime(cls, moe):
+        if cls._hip is None:
+            import ctypes
+            hip, V = moe.lib, ctypes.c_void_p
+            hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(V), ctypes.c_uint]
+            hip.hipEventRecord.argtypes = [V, V]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), V, V]
+            hip.hipEventDestroy.argtypes = [V]
+            cls._hip = hip
+        return cls._hip
+
+    def __init__(self, moe, torch):
+        import ctypes
+        self._ct, self.torch = ctypes, torch
+        self.hip = self._runtime(moe)
+        self.h = ctypes.c_void_p()
+        self._check(self.hip.hipEventCreateWithFlags(ctypes.byref(self.h), self.DISABLE_SYSTEM_FENCE),
+                    "hipEventCreateWithFlags")
+
+    @staticmethod
+    def _check(rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} failed with HIP error {rc}")
+
+    def record(self):
+        stream = self._ct.c_void_p(self.torch.cuda.current_stream().cuda_stream)
+        self._check(self.hip.hipEventRecord(self.h, stream), "hipEventRecord")
+
+    def elapsed_time(self, end):
+        """Milliseconds from this event to `end` (both recorded and complete)."""
+        ms = self._ct.c_float()
+        self._check(self.hip.hipEventElapsedTime(self._ct.byref(ms), self.h, end.h),
+                    "hipEventElapsedTime")
+        return ms.value
+
+    def __del__(self):
+        if getattr(self, "h", None) and self.h.value:
+            self.hip.hipEventDestroy(self.h)
+
+
+def time_kernels(torch, path, steps, moe):
+    evs = [[TimingEvent(moe, torch) for _ in range(4)] for _ in range(steps)]
     torch.cuda.synchronize()
     for i in range(steps):
         path.step(i, evs[i])
@@ -517,7 +572,7 @@ def main():
         # context: the same step as the plan call, the dispatch call, the combine
         three_ms, _ = time_steps(torch, _ThreeCalls(path), args.steps, args.warmup)
         log(f"[bench] plan_and_dispatch {path.mode()}; as three calls: {three_ms * 1e3:.2f} us/step")
-    kt = time_kernels(torch, path, args.steps)
+    kt = time_kernels(torch, path, args.steps, moe)
     log(f"[bench] per-kernel means (us): plan {kt['plan'] * 1e3:.2f} dispatch "
         f"{kt['dispatch'] * 1e3:.2f} combine {kt['combine'] * 1e3:.2f}")
     log("[bench] p10/p50/p90 (us): " + "; ".join(
