@@ -112,7 +112,8 @@ int pd_begin(const moe_problem &p, const int32_t *ids, const moe_plan &plan, voi
              hipStream_t s) {
   switch (moe::plan_dispatch_mode(p)) {
     case moe::PlanDispatchMode::kOneLaunch: return MOE_OK;
-    case moe::PlanDispatchMode::kTiled: return launched(moe::launch_plan_count(p, ids, workspace, s));
+    case moe::PlanDispatchMode::kTiled:
+      return launched(moe::launch_plan_count(p, ids, plan.status, workspace, s));
     default: return launched(moe::launch_plan(p, ids, plan, workspace, s));
   }
 }
@@ -274,10 +275,13 @@ MOE_API int moe_combine(const moe_problem *p, const moe_plan *plan, const uint16
   const int rc = check(p);
   if (rc != MOE_OK) return rc;
   if (!plan) return MOE_EINVAL;
-  if (p->n_tokens > 0 && (!expert_out || !out || !plan->slot)) return MOE_EINVAL;
+  // expert_out may be NULL only when no slot can name a row (R_max = 0)
+  const int64_t rows = max_rows_unchecked(*p);
+  if (p->n_tokens > 0 && (!out || !plan->slot || (rows > 0 && !expert_out))) return MOE_EINVAL;
   if (!aligned(expert_out, 16) || !aligned(out, 16) || !aligned(topk_weights, 4) || !aligned(plan->slot, 4))
     return MOE_EALIGN;
-  return launched(moe::launch_combine(*p, *plan, expert_out, topk_weights, out, static_cast<hipStream_t>(stream)));
+  return launched(moe::launch_combine(*p, *plan, expert_out, rows, topk_weights, out,
+                                      static_cast<hipStream_t>(stream)));
 }
 
 MOE_API int moe_check_exchange(const moe_problem *p) { return check_exchange(p); }
@@ -363,7 +367,9 @@ MOE_API int moe_exchange_combine(const moe_problem *p, const moe_exchange *x, co
   const int rc = check_exchange(p);
   if (rc != MOE_OK) return rc;
   if (!x) return MOE_EINVAL;
-  if (p->n_tokens > 0 && (!expert_out || !out || !x->recv_slot)) return MOE_EINVAL;
+  // expert_out may be NULL only when no receive row exists (EP * C = 0)
+  const bool no_rows = p->recv_capacity == 0;
+  if (p->n_tokens > 0 && (!out || !x->recv_slot || (!no_rows && !expert_out))) return MOE_EINVAL;
   if (!aligned(expert_out, 16) || !aligned(out, 16) || !aligned(topk_weights, 4) || !aligned(x->recv_slot, 4))
     return MOE_EALIGN;
   return launched(moe::launch_exchange_combine(*p, *x, expert_out, topk_weights, out,

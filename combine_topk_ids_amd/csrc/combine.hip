@@ -21,10 +21,15 @@
 // the slab.  Slabs are 2048 columns when the expert rows are streamed
 // (longer runs of each row per wave measured faster there), 1024 when they
 // are read with cache-allocating loads, and 512 when 1024-column slabs would
-// give the launch too few waves to fill the GPU (decode shapes).  The token's k slots and gate weights are loaded once, one per
-// lane, and broadcast with readlane; all k row loads of the slab are issued
-// before the first FMA, so each wave makes two round trips to memory (index
-// loads, then row loads) and keeps k x 2 or 4 KiB in flight.
+// give the launch too few waves to fill the GPU (decode shapes).  The
+// token's k slots and gate weights are loaded once, one per lane, and
+// broadcast with readlane; all k row loads of the slab are issued before the
+// first FMA, so each wave makes two round trips to memory (index loads, then
+// row loads) and keeps k x 2 or 4 KiB in flight.  Every row is read through
+// a buffer resource that spans that row alone, and a masked slot (or one
+// outside the rows of expert_out) gets a resource of zero bytes: its loads
+// return zeros without touching memory, so no row that no slot names is
+// ever read, and expert_out may be NULL when no slot can name a row.
 #include "moe_device.hpp"
 #include "moe_kernels.hpp"
 
@@ -64,6 +69,7 @@ struct CombineArgs {
   const float *w;
   uint16_t *out;
   int64_t n;
+  int64_t rows;  // rows of y: a slot outside [0, rows) is read as masked
   int k, h;
   int slabs;  // waves per token
 };
@@ -108,7 +114,6 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs g) {
   // no weights: every gate is 1 (the rows were weighted at dispatch), and
   // fma(1, y, acc) is the correctly rounded y + acc
   const float my_w = lane < k ? (g.w ? g.w[pair0 + lane] : 1.0f) : 0.0f;
-  const u32x4 *ybase = reinterpret_cast<const u32x4 *>(g.y);
 
   float acc[kVec][8];
 #pragma unroll
@@ -117,23 +122,26 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs g) {
     for (int i = 0; i < 8; ++i) acc[u][i] = 0.0f;
 
   constexpr int KB = KC > 0 ? KC : kBatch;
+  const uint32_t row_bytes = 2u * static_cast<uint32_t>(g.h);
   for (int j0 = 0; j0 < k; j0 += KB) {
     u32x4 v[KB][kVec];
-    int s[KB];
+    bool live[KB];
 #pragma unroll
     for (int jj = 0; jj < KB; ++jj) {
-      s[jj] = (KC > 0 || j0 + jj < k) ? __builtin_amdgcn_readlane(my_slot, j0 + jj) : -1;
-      const int64_t row = s[jj] >= 0 ? s[jj] : 0;  // masked: harmless in-bounds read
-      const u32x4 *src = ybase + row * nvec;
+      const int s = (KC > 0 || j0 + jj < k) ? __builtin_amdgcn_readlane(my_slot, j0 + jj) : -1;
+      live[jj] = s >= 0 && s < g.rows;
+      // the row alone, or nothing: loads past the resource return zeros and
+      // touch no memory (also the columns past H in the last slab)
+      const auto rsrc = buffer_rsrc(live[jj] ? g.y + static_cast<int64_t>(s) * g.h : g.y,
+                                    live[jj] ? row_bytes : 0u);
 #pragma unroll
-      for (int u = 0; u < kVec; ++u) {
-        const int idx = v0 + u * kWave + lane;
-        if (idx < nvec) v[jj][u] = NT ? __builtin_nontemporal_load(src + idx) : src[idx];
-      }
+      for (int u = 0; u < kVec; ++u)
+        v[jj][u] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (v0 + u * kWave + lane) * 16, 0,
+                                                         NT ? kLoadNT : kLoadDefault);
     }
 #pragma unroll
     for (int jj = 0; jj < KB; ++jj) {
-      if (s[jj] < 0) continue;
+      if (!live[jj]) continue;
       const float wj = __builtin_bit_cast(
           float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_w), j0 + jj));
 #pragma unroll
@@ -163,13 +171,14 @@ void launch_k(const CombineArgs &g, int k, int grid, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_combine(const moe_problem &p, const moe_plan &plan, const uint16_t *expert_out,
-                          const float *weights, uint16_t *out, hipStream_t stream) {
+                          int64_t rows, const float *weights, uint16_t *out, hipStream_t stream) {
   CombineArgs g;
   g.y = expert_out;
   g.slot = plan.slot;
   g.w = weights;
   g.out = out;
   g.n = p.n_tokens;
+  g.rows = expert_out ? rows : 0;
   g.k = p.top_k;
   g.h = p.hidden;
   // bytes of expert rows this launch reads (one row per valid pair at most)

@@ -118,8 +118,10 @@ __device__ __forceinline__ void store(V *p, V v) {
 // loaded once, one per lane, together with the slab's data, and broadcast
 // with readlane, so a wave makes a single round trip to memory before it
 // starts storing.
+// A slot outside the buffer's rows [0, r_max) is skipped like a masked one.
 __device__ __forceinline__ int lane_slot(const DispatchArgs &g, int64_t t, int lane) {
-  return lane < g.k ? g.slot[t * g.k + lane] : -1;
+  const int s = lane < g.k ? g.slot[t * g.k + lane] : -1;
+  return s >= 0 && s < g.r_max ? s : -1;
 }
 
 // ---- bf16: copy the slab to every destination -------------------------------
@@ -542,7 +544,7 @@ template <bool NT>
 __device__ void zero_tails(const DispatchArgs &g, int blk, int wave) {
   const int64_t stride = static_cast<int64_t>(g.tail_blocks) * kWaves;
   for (int d = 0; d < g.nseg; ++d) {
-    const int64_t used = min(static_cast<int64_t>(g.seg_used[d]), g.seg_rows);
+    const int64_t used = max(min(static_cast<int64_t>(g.seg_used[d]), g.seg_rows), int64_t{0});
     const int64_t base = d * g.seg_rows;
     for (int64_t r = used + static_cast<int64_t>(blk) * kWaves + wave; r < g.seg_rows; r += stride)
       zero_row<NT>(g, base + r);
@@ -594,9 +596,10 @@ __device__ __forceinline__ void dispatch_body(const DispatchArgs &g, int blk, in
     if (e >= g.e) return;
     const int grp = q - e * g.pad_groups;
     // unused rows [offsets[e] + counts[e], offsets[e+1]); with a fixed
-    // capacity counts[e] may exceed the expert's rows (int64: no overflow)
-    const int64_t hi = g.offsets[e + 1];
-    const int64_t lo = min(static_cast<int64_t>(g.offsets[e]) + g.counts[e], hi);
+    // capacity counts[e] may exceed the expert's rows (int64: no overflow);
+    // never outside the buffer, whatever the plan arrays hold
+    const int64_t hi = min(static_cast<int64_t>(g.offsets[e + 1]), g.r_max);
+    const int64_t lo = max(min(static_cast<int64_t>(g.offsets[e]) + g.counts[e], hi), int64_t{0});
     const int64_t r0 = lo + static_cast<int64_t>(grp) * kPadRowsPerWave;
     const int64_t r1 = min(r0 + kPadRowsPerWave, hi);
     for (int64_t r = r0; r < r1; ++r) zero_row<NT>(g, r);
@@ -692,7 +695,12 @@ __global__ __launch_bounds__(kThreads) void plan_dispatch_kernel(PlanDispatchArg
     }
     if (tid == 0) {
       g.offsets[E] = s.off[E];
-      *g.status = fl;
+      // tiled: the counting kernel cleared the status word, and other
+      // workgroups may OR BAD_PLAN into it; one launch: written here alone
+      if constexpr (TILED)
+        atomicOr(g.status, fl | (s.off[E] < 0 || s.off[E] > g.r_max ? MOE_STATUS_BAD_PLAN : 0u));
+      else
+        *g.status = fl;
     }
     const int L = g.sp.l;
     for (int rk = tid; rk < g.sp.ep; rk += kThreads) {
@@ -706,21 +714,30 @@ __global__ __launch_bounds__(kThreads) void plan_dispatch_kernel(PlanDispatchArg
     }
   }
   // the wave's own token's slots, found by the wave itself; they and the
-  // token's packed_src rows are written by the wave of its slab 0
-  const int my_slot = live && lane < k ? own_slot(s, TILED ? tlo : 0, p0, t * k + lane) : -1;
-  if (live && slab == 0 && lane < k) {
-    g.slot[t * k + lane] = my_slot;
-    if (my_slot >= 0) g.packed_src[my_slot] = t;
+  // token's packed_src rows are written by the wave of its slab 0.  A pair
+  // the histograms do not account for (tiled mode, a workspace that does
+  // not count these IDs) is left unplaced and reported.
+  int my_slot = live && lane < k ? own_slot(s, TILED ? tlo : 0, p0, t * k + lane, g.r_max) : -1;
+  const bool bad = my_slot == kBadSlot;
+  if (bad) my_slot = -1;
+  if (live && slab == 0) {
+    if (lane < k) {
+      g.slot[t * k + lane] = my_slot;
+      if (my_slot >= 0) g.packed_src[my_slot] = t;
+    }
+    if (TILED && ballot(bad) && lane == 0) atomicOr(g.status, MOE_STATUS_BAD_PLAN);
   }
-  // packed_src = -1 on the unused rows of each expert and on the tail
+  // packed_src = -1 on the unused rows of each expert and on the tail, never
+  // outside the buffer
   const int stride = gridDim.x * kThreads;
   const int per = g.sp.a - 1;
   for (int qq = b * kThreads + tid; qq < E * per; qq += stride) {
     const int e = qq / per;
-    const int row = s.off[e] + s.cnt[e] + (qq - e * per);
-    if (row < s.off[e + 1]) g.packed_src[row] = -1;
+    const int64_t row = static_cast<int64_t>(s.off[e]) + s.cnt[e] + (qq - e * per);
+    if (row < s.off[e + 1] && row >= 0 && row < g.r_max) g.packed_src[row] = -1;
   }
-  for (int row = s.off[E] + b * kThreads + tid; row < g.r_max; row += stride) g.packed_src[row] = -1;
+  for (int row = max(s.off[E], 0) + b * kThreads + tid; row < g.r_max; row += stride)
+    g.packed_src[row] = -1;
 
   if (live) {
     emit_slab<FMT, NT, GATED>(d, slab, my_slot, r);

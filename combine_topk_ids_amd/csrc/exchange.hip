@@ -282,7 +282,7 @@ hipError_t launch_exchange_combine(const moe_problem &p, const moe_exchange &x, 
   all.n_tokens = p.n_tokens * p.ep;
   moe_plan plan{};
   plan.slot = x.recv_slot;
-  return launch_combine(all, plan, expert_out, weights, out, stream);
+  return launch_combine(all, plan, expert_out, p.recv_capacity * p.ep, weights, out, stream);
 }
 
 }  // namespace moe

@@ -74,9 +74,10 @@ hipError_t launch_dispatch(const moe_problem &p, const moe_plan &plan, const uin
                            hipStream_t stream);
 
 // The plan's counting kernel alone: tile histograms and fault bits into
-// the plan workspace (problems of more than one count tile).
-hipError_t launch_plan_count(const moe_problem &p, const int32_t *ids, void *workspace,
-                             hipStream_t stream);
+// the plan workspace (problems of more than one count tile); it also clears
+// *status, into which the launch that finishes the plan ORs its bits.
+hipError_t launch_plan_count(const moe_problem &p, const int32_t *ids, uint32_t *status,
+                             void *workspace, hipStream_t stream);
 
 // How moe_plan_and_dispatch runs a problem: one launch (at most 2048 pairs),
 // tiled (the counting kernel, then one launch that finishes the plan and
@@ -91,7 +92,9 @@ hipError_t launch_plan_dispatch(const moe_problem &p, const int32_t *ids, const 
                                 const uint16_t *hidden, const float *gates, const float *gscale,
                                 void *payload, void *scales, void *workspace, hipStream_t stream);
 
+// rows: rows of expert_out; a slot outside [0, rows) is skipped like a
+// masked one, and no row that no slot names is read
 hipError_t launch_combine(const moe_problem &p, const moe_plan &plan, const uint16_t *expert_out,
-                          const float *weights, uint16_t *out, hipStream_t stream);
+                          int64_t rows, const float *weights, uint16_t *out, hipStream_t stream);
 
 }  // namespace moe

@@ -107,7 +107,8 @@ __device__ __forceinline__ int padded(int c, int a) { return ((c + a - 1) / a) *
 
 __device__ __forceinline__ uint32_t wave_or_bits(uint32_t v) {
   return (ballot(v & 1u) ? 1u : 0u) | (ballot(v & 2u) ? 2u : 0u) | (ballot(v & 4u) ? 4u : 0u) |
-         (ballot(v & MOE_STATUS_DROPPED) ? MOE_STATUS_DROPPED : 0u);
+         (ballot(v & MOE_STATUS_DROPPED) ? MOE_STATUS_DROPPED : 0u) |
+         (ballot(v & MOE_STATUS_BAD_PLAN) ? MOE_STATUS_BAD_PLAN : 0u);
 }
 
 struct Tile {
@@ -210,6 +211,8 @@ __global__ __launch_bounds__(kThreads) void plan_count_kernel(PlanArgs g) {
   int32_t *hrow = g.hist + static_cast<int64_t>(c) * g.e;
   for (int e = threadIdx.x; e < g.e; e += kThreads) hrow[e] = s_cnt[e];
   if (threadIdx.x == 0) g.tflags[c] = s_fl;
+  // the launch after this one ORs its bits into the status word
+  if (c == 0 && threadIdx.x == 0 && g.status) *g.status = 0u;
 }
 
 // kFused: the whole problem is one count tile, counted here by every block.
@@ -407,15 +410,32 @@ __global__ __launch_bounds__(kThreads) void plan_assign_kernel(PlanArgs g) {
   __syncthreads();
 
   // ---- stores only from here on -------------------------------------------
+  // A pair's rank in its expert must lie below the expert's total, and its
+  // row inside the buffer; with histograms that do not count these IDs (a
+  // workspace changed between the two launches) it may not, and then the
+  // pair is left unplaced (slot -1) and BAD_PLAN is set.
+  uint32_t bad = 0;
   if (in) {
     int sl = -1;
     if (valid) {
       sl = cur[ev] + rank;
-      // a fixed capacity keeps the first cap pairs of each expert
-      if (g.ecap > 0 && sl - s_off[ev] >= g.ecap) sl = -1;
+      const int r = sl - s_off[ev];
+      if (!kFused && (r < 0 || r >= s_tot[ev])) {
+        bad = MOE_STATUS_BAD_PLAN;
+        sl = -1;
+      } else if (g.ecap > 0 && r >= g.ecap) {
+        sl = -1;  // a fixed capacity keeps the first cap pairs of each expert
+      } else if (!kFused && (sl < 0 || sl >= g.r_max)) {
+        bad = MOE_STATUS_BAD_PLAN;
+        sl = -1;
+      }
       if (sl >= 0) g.packed_src[sl] = static_cast<int32_t>(t.tok0 + i_loc / k);
     }
     g.slot[t.pair0 + i_loc] = sl;
+  }
+  if (!kFused) {
+    if (b == 0 && tid == 0 && (s_off[E] < 0 || s_off[E] > g.r_max)) bad = MOE_STATUS_BAD_PLAN;
+    if (ballot(bad != 0) && lane == 0) atomicOr(g.status, MOE_STATUS_BAD_PLAN);
   }
 
   // block 0: counts, offsets, per-rank table, status
@@ -426,7 +446,12 @@ __global__ __launch_bounds__(kThreads) void plan_assign_kernel(PlanArgs g) {
     }
     if (tid == 0) {
       g.offsets[E] = s_off[E];
-      *g.status = s_fl;
+      // after the counting kernel, which cleared it, other blocks may OR
+      // BAD_PLAN into the status word; a single-tile plan writes it alone
+      if (kFused)
+        *g.status = s_fl;
+      else
+        atomicOr(g.status, s_fl);
     }
     for (int r = tid; r < g.ep; r += kThreads) {
       const int lo = r * L, hi = lo + L;
@@ -449,11 +474,11 @@ __global__ __launch_bounds__(kThreads) void plan_assign_kernel(PlanArgs g) {
     for (int q = b * kThreads + tid; q < cand; q += g.nblocks * kThreads) {
       const int e = q / per;
       const int used = g.ecap > 0 ? min(s_tot[e], g.ecap) : s_tot[e];
-      const int r = s_off[e] + used + (q - e * per);
-      if (r < s_off[e + 1]) g.packed_src[r] = -1;
+      const int64_t r = static_cast<int64_t>(s_off[e]) + used + (q - e * per);
+      if (r < s_off[e + 1] && r >= 0 && r < g.r_max) g.packed_src[r] = -1;
     }
   }
-  for (int64_t r = s_off[E] + static_cast<int64_t>(b) * kThreads + tid; r < g.r_max;
+  for (int64_t r = max(s_off[E], 0) + static_cast<int64_t>(b) * kThreads + tid; r < g.r_max;
        r += static_cast<int64_t>(g.nblocks) * kThreads)
     g.packed_src[r] = -1;
 }
@@ -558,10 +583,13 @@ hipError_t launch_plan_ranks(const moe_problem &p, int ranks, const int32_t *ids
   return launch_plan_impl(p, ranks, ids, plan, st, workspace, stream, false);
 }
 
-hipError_t launch_plan_count(const moe_problem &p, const int32_t *ids, void *workspace,
-                             hipStream_t stream) {
-  // only the workspace and the IDs are touched; the plan arrays stay unset
-  return launch_plan_impl(p, 1, ids, moe_plan{}, PlanStrides{}, workspace, stream, true);
+hipError_t launch_plan_count(const moe_problem &p, const int32_t *ids, uint32_t *status,
+                             void *workspace, hipStream_t stream) {
+  // the workspace and the status word (cleared) are written; the other plan
+  // arrays stay unset
+  moe_plan plan{};
+  plan.status = status;
+  return launch_plan_impl(p, 1, ids, plan, PlanStrides{}, workspace, stream, true);
 }
 
 hipError_t launch_plan(const moe_problem &p, const int32_t *ids, const moe_plan &plan,

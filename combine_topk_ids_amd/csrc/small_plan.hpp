@@ -224,7 +224,14 @@ __device__ uint32_t plan_finish(const SmallPlanArgs &g, const SmallPlanLds &s, u
 // pairs before p0, plus its equal IDs among the own pairs ahead of p.  Reads
 // only LDS that the plan's last barrier published, so a wave calls it for
 // its own token's pairs with no further barrier.
-__device__ __forceinline__ int own_slot(const SmallPlanLds &s, int lo, int p0, int p) {
+//
+// The pair's rank r in its expert must lie below the expert's count and its
+// row inside the buffer [0, r_max).  From a plan of the IDs themselves it
+// always does; in tiled mode the counts come from histograms in memory,
+// and if those do not count these IDs the pair gets kBadSlot instead.
+constexpr int kBadSlot = -2;
+
+__device__ __forceinline__ int own_slot(const SmallPlanLds &s, int lo, int p0, int p, int r_max) {
   const int e = s.ids[p - lo];
   if (e < 0) return -1;
   const int *own = s.ids + (p0 - lo);
@@ -238,7 +245,8 @@ __device__ __forceinline__ int own_slot(const SmallPlanLds &s, int lo, int p0, i
 #pragma unroll
     for (int q = 0; q < 16; ++q) r += w[q] == e ? 1 : 0;
   }
-  return s.off[e] + r;
+  const int64_t row = static_cast<int64_t>(s.off[e]) + r;
+  return r < 0 || r >= s.cnt[e] || row < 0 || row >= r_max ? kBadSlot : static_cast<int>(row);
 }
 
 // Fills cnt, off, cpre and ids for the whole problem and before (each

@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 
 MOE_OK, MOE_EINVAL, MOE_EALIGN, MOE_EOVERFLOW, MOE_EHIP = 0, -1, -2, -3, -4
 STATUS_BAD_ID, STATUS_DUP_ID, STATUS_CAPACITY, STATUS_MAP_OVERFLOW, STATUS_DROPPED = 1, 2, 4, 8, 16
+STATUS_BAD_PLAN = 32
 FMT = {"bf16": 0, "fp8": 1, "mxfp4": 2, "nvfp4": 3}
 FLAG_ZERO_TAIL = 1
 # how moe_plan_and_dispatch runs a problem (moe_plan_and_dispatch_mode)

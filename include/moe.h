@@ -81,6 +81,13 @@ extern "C" {
 /* (fixed expert capacity) some expert was routed more pairs than its
  * capacity: the later ones were dropped */
 #define MOE_STATUS_DROPPED 16u
+/* The plan's workspace did not describe these IDs: a pair's place, found
+ * from the tile histograms that the counting launch left in the workspace,
+ * fell outside its expert's rows or the buffer (the workspace, topk_ids or
+ * the plan arrays were changed between the launches of one plan).  Such
+ * pairs get slot -1 and nothing is written through them, every store stays
+ * inside the caller's buffers, and the plan and payload are not valid. */
+#define MOE_STATUS_BAD_PLAN 32u
 
 /* ---- payload formats ---------------------------------------------------- */
 typedef enum moe_fmt {
