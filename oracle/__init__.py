@@ -37,7 +37,7 @@ def build(force: bool = True) -> str:
     if force or not os.path.exists(LIB):
         tmp = LIB + ".tmp%d" % os.getpid()
         subprocess.check_call(
-            ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-ffp-contract=off",
+            ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-ffp-contract=off", "-fopenmp",
              "-Wall", "-o", tmp, SRC, "-lm"])
         os.replace(tmp, LIB)
     return LIB
@@ -65,6 +65,8 @@ def _load():
         lib.oracle_dispatch_nvfp4.argtypes = [i64, i64, i64, p, p, ctypes.c_float, p, p, i32]
         lib.oracle_exchange_plan.restype = None
         lib.oracle_exchange_plan.argtypes = [i64, i32, i32, i32, i64, i64] + [p] * 9
+        lib.oracle_encode_rows.restype = None
+        lib.oracle_encode_rows.argtypes = [i32, i64, i64, p, p, p]
         lib.oracle_encode_row.restype = None
         lib.oracle_encode_row.argtypes = [i32, i64, p, p, p]
         lib.oracle_encode_row_f32.restype = None
@@ -85,6 +87,10 @@ def _load():
         lib.oracle_e4m3_value.argtypes = [i32]
         lib.oracle_e2m1_value.restype = ctypes.c_double
         lib.oracle_e2m1_value.argtypes = [i32]
+        lib.oracle_set_threads.restype = None
+        lib.oracle_set_threads.argtypes = [i32]
+        lib.oracle_threads.restype = i32
+        lib.oracle_threads.argtypes = []
         _lib = lib
     return _lib
 
@@ -105,6 +111,15 @@ def _check_buf(a: np.ndarray, shape, dtype, what: str) -> None:
     if a.shape != tuple(shape) or a.dtype != np.dtype(dtype) or not a.flags.c_contiguous:
         raise ValueError(f"{what} must be a contiguous {np.dtype(dtype)} array of shape "
                          f"{tuple(shape)}, not {a.dtype} {a.shape}")
+
+
+def set_threads(n: int) -> None:
+    """Threads the oracle's row loops may use (results do not depend on it)."""
+    _load().oracle_set_threads(int(n))
+
+
+def threads() -> int:
+    return int(_load().oracle_threads())
 
 
 def max_rows(n: int, k: int, e: int, a: int) -> int:
@@ -234,10 +249,8 @@ def encode_rows(fmt: str, x: np.ndarray):
     pdt, pshape, sdt, sshape = payload_shape(fmt, m, h)
     pay = np.zeros(pshape, pdt)
     sc = np.zeros(sshape, sdt if sdt is not None else np.uint8)
-    lib = _load()
-    for r in range(m):
-        lib.oracle_encode_row(FMT[fmt], h, _ptr(x[r]), _ptr(pay[r]),
-                              _ptr(sc[r]) if sdt is not None else None)
+    _load().oracle_encode_rows(FMT[fmt], m, h, _ptr(x), _ptr(pay),
+                               _ptr(sc) if sdt is not None else None)
     return pay, (sc if sdt is not None else None)
 
 

@@ -104,10 +104,18 @@
  * and zero scales; signs of zero are kept; rows a receive buffer cannot hold
  * are dropped and flagged) are listed with the design notes.
  *
- * Build: gcc -O2 -std=c99 -fPIC -shared -ffp-contract=off -o liboracle.so
- *        oracle.c -lm     (no fast-math: IEEE division and fmaf are required)
+ * Threads.  The loops over independent rows (dispatch: packed rows; combine:
+ * tokens; plan step O5: experts, each walking the pairs for its own rows)
+ * may run on several OpenMP threads.  Every row is still computed by exactly
+ * the code above, on one thread, so the results do not depend on the thread
+ * count (oracle_set_threads; the tests check 1 against several).
+ *
+ * Build: gcc -O2 -std=c99 -fPIC -shared -ffp-contract=off -fopenmp
+ *        -o liboracle.so oracle.c -lm  (no fast-math: IEEE division and fmaf
+ *        are required)
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -121,6 +129,10 @@
 #define ORC_FMT_BF16 0
 #define ORC_FMT_FP8 1
 #define ORC_FMT_MX 2
+
+/* Threads the row loops may use (>= 1), and how many they use now. */
+void oracle_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
+int oracle_threads(void) { return omp_get_max_threads(); }
 
 /* ---------------------------------------------------------------- bf16 -- */
 
@@ -289,6 +301,7 @@ void oracle_plan(int64_t n, int k, int e_cnt, int ep, int a, int64_t cap,
   for (int64_t t = 0; t < n; t++) {
     for (int j = 0; j < k; j++) slot[t * k + j] = -1;
   }
+#pragma omp parallel for schedule(dynamic, 1)
   for (int x = 0; x < e_cnt; x++) {
     int32_t next = offsets[x];
     for (int64_t t = 0; t < n; t++) {
@@ -486,6 +499,9 @@ void oracle_exchange_plan(int64_t n, int k, int e_cnt, int ep, int64_t cap,
 
 /* ------------------------------------------------------------ encoders --- */
 
+static int64_t payload_row_bytes(int fmt, int64_t h);
+static int64_t scale_row_bytes(int fmt, int64_t h);
+
 /* One row of h fp32 values into one packed row.  For FP8 the payload row
  * holds h code bytes and the scale row h/128 floats; for MX the payload row
  * holds h/2 bytes (element 2m in the low nibble, 2m+1 in the high one) and
@@ -555,6 +571,16 @@ void oracle_encode_row(int fmt, int64_t h, const uint16_t *x, void *payload,
   free(v);
 }
 
+/* m hidden rows x[m][h], each encoded on its own (oracle_encode_row) into
+ * payload row i and scale row i. */
+void oracle_encode_rows(int fmt, int64_t m, int64_t h, const uint16_t *x,
+                        uint8_t *payload, uint8_t *scales) {
+  int64_t pb = payload_row_bytes(fmt, h), sb = scale_row_bytes(fmt, h);
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int64_t i = 0; i < m; i++)
+    oracle_encode_row(fmt, h, x + i * h, payload + i * pb, sb ? scales + i * sb : 0);
+}
+
 /* NVFP4 row: h/2 payload bytes (element 2m in the low nibble of byte m) and
  * h/16 E4M3 scale bytes, with global encode scale gs. */
 void oracle_encode_row_nvfp4(int64_t h, const uint16_t *x, float gs,
@@ -588,6 +614,7 @@ void oracle_dispatch_nvfp4(int64_t h, int64_t r_max, int64_t r_used,
                            const int32_t *packed_src, const uint16_t *x, float gs,
                            uint8_t *payload, uint8_t *scales, int zero_tail) {
   int64_t pb = h / 2, sb = h / 16;
+#pragma omp parallel for schedule(dynamic, 64)
   for (int64_t r = 0; r < r_max; r++) {
     if (r >= r_used && !zero_tail) continue;
     int32_t t = r < r_used ? packed_src[r] : -1;
@@ -619,6 +646,7 @@ void oracle_dispatch(int fmt, int64_t h, int64_t r_max, int64_t r_used,
                      const int32_t *packed_src, const uint16_t *x,
                      uint8_t *payload, uint8_t *scales, int zero_tail) {
   int64_t pb = payload_row_bytes(fmt, h), sb = scale_row_bytes(fmt, h);
+#pragma omp parallel for schedule(dynamic, 64)
   for (int64_t r = 0; r < r_max; r++) {
     if (r >= r_used && !zero_tail) continue;
     uint8_t *prow = payload + r * pb;
@@ -696,6 +724,7 @@ void oracle_routing_map_to_topk(int64_t n, int e_cnt, int k, const uint8_t *map,
  * correctly rounded y + acc). */
 void oracle_combine(int64_t n, int k, int64_t h, const int32_t *slot,
                     const float *w, const uint16_t *y, uint16_t *out) {
+#pragma omp parallel for schedule(dynamic, 16)
   for (int64_t t = 0; t < n; t++) {
     for (int64_t c = 0; c < h; c++) {
       float acc = 0.0f;

@@ -13,7 +13,8 @@ import torch
 import oracle
 from combine_topk_ids_amd.workloads import (WORKLOADS, make_inputs, random_bf16,
                                             random_routing)
-from gpu_helpers import SENTINEL, assert_combine_close, say, to_dev_bf16, u16
+from gpu_helpers import (SENTINEL, assert_combine_close, assert_rows_are_tokens, say,
+                         to_dev_bf16, u16)
 
 pytestmark = pytest.mark.gpu
 
@@ -64,7 +65,10 @@ def run_capacity(moe, *, ids, weights, hidden, e, ep, fmt, cap, rcap, expert_out
 
 
 def check_capacity(moe, *, ids, weights, hidden, e, ep, fmt, cf, rcap=None, expert_out=None,
-                   sample_rows=None, halves=False):
+                   per_token=False, halves=False):
+    """per_token: the oracle encodes each token once and every packed row is
+    compared with the encoding of its source token (gather form), instead
+    of the oracle's whole dispatch encoding every row."""
     n, k = ids.shape
     h = hidden.shape[1]
     cap = oracle.expert_capacity(n, k, e, cf)
@@ -76,19 +80,15 @@ def check_capacity(moe, *, ids, weights, hidden, e, ep, fmt, cf, rcap=None, expe
     for f in PLAN_KEYS:
         assert np.array_equal(got[f], pl[f]), f
     assert got["status"] == pl["status"]
-    if sample_rows is None:
+    if not per_token:
         pay, sc = oracle.dispatch(fmt, hidden, pl)
         assert np.array_equal(got["payload"], pay.view(np.uint8).reshape(pay.shape[0], -1))
         if sc is not None:
             assert np.array_equal(got["scales"], sc.view(np.uint8).reshape(sc.shape[0], -1))
         y = pay.view(np.uint16) if expert_out is None else expert_out
     else:
-        src = pl["packed_src"]
-        assert np.all(got["payload"][src < 0] == 0) and np.all(got["scales"][src < 0] == 0)
-        rows = sample_rows(src)
-        enc, enc_sc = oracle.encode_rows(fmt, hidden[src[rows]])
-        assert np.array_equal(got["payload"][rows], enc.view(np.uint8).reshape(rows.size, -1))
-        assert np.array_equal(got["scales"][rows], enc_sc.view(np.uint8).reshape(rows.size, -1))
+        enc, enc_sc = oracle.encode_rows(fmt, hidden)
+        assert_rows_are_tokens(got["payload"], got["scales"], enc, enc_sc, pl["packed_src"])
         y = expert_out
     ref = oracle.combine(pl["slot"], weights, y)
     return got, pl, assert_combine_close(got["out"], ref)
@@ -107,19 +107,19 @@ def test_capacity_bf16_workload(moe, halves):
 
 
 @pytest.mark.parametrize("halves", [False, True], ids=["three_calls", "bench_calls"])
-def test_capacity_fp8_workload_sampled(moe, halves):
+def test_capacity_fp8_workload_full(moe, halves):
+    """Every plan array, every packed and scale row (kept rows against the
+    oracle's encoding of their token, unused rows zero) and every combine
+    output of the FP8 fixed-capacity workload at full size."""
     w = WORKLOADS["capacity_fp8_n8192"]
     say(f"[capacity parity] {w.name}: {w.describe()}; halves={halves}")
     cap = oracle.expert_capacity(w.n, w.k, w.e, w.capacity_factor)
     inp = make_inputs(w, seed=0, expert_rows=w.e * cap)
-    rng = np.random.default_rng(99)
-
-    def sample(src):
-        live = np.nonzero(src >= 0)[0]
-        return np.unique(np.concatenate([live[:2], live[-2:], rng.choice(live, 508, replace=False)]))
-    check_capacity(moe, ids=inp["ids"], weights=inp["weights"], hidden=inp["hidden"], e=w.e,
-                   ep=w.ep, fmt="fp8", cf=w.capacity_factor, rcap=w.capacity,
-                   expert_out=inp["expert_out"], sample_rows=sample, halves=halves)
+    _, _, nonexact = check_capacity(moe, ids=inp["ids"], weights=inp["weights"],
+                                    hidden=inp["hidden"], e=w.e, ep=w.ep, fmt="fp8",
+                                    cf=w.capacity_factor, rcap=w.capacity,
+                                    expert_out=inp["expert_out"], per_token=True, halves=halves)
+    assert nonexact == 0
 
 
 # n, h, e, k, ep, fmt, capacity factor, masked fraction

@@ -16,7 +16,8 @@ from combine_topk_ids_amd.workloads import (WORKLOADS, make_inputs, random_bf16,
 
 pytestmark = pytest.mark.gpu
 
-from gpu_helpers import SENTINEL, assert_combine_close, say, to_dev_bf16, u16
+from gpu_helpers import (SENTINEL, assert_combine_close, assert_rows_are_tokens, say,
+                         to_dev_bf16, u16)
 
 
 @pytest.fixture(scope="module")
@@ -169,11 +170,13 @@ def test_workload_full_parity_bench_calls(moe, name):
 
 
 @pytest.mark.parametrize("halves", [False, True], ids=["three_calls", "bench_calls"])
-def test_fp8_workload_sampled_parity(moe, halves):
+def test_fp8_workload_full_parity(moe, halves):
     """FP8 1x128 workload at full size (N=8192, H=7168, E=256, k=8, EP=32):
-    whole plan, and sampled tokens' packed rows, scales and combine rows;
-    through the three calls, and through the calls and flags bench.py times
-    (moe_plan_and_dispatch_begin + _end, no zero tail)."""
+    the whole plan, every packed row and scale row (the oracle encodes each
+    token once; row r must hold the encoding of token packed_src[r]) and
+    every combine output; through the three calls, and through the calls and
+    flags bench.py times (moe_plan_and_dispatch_begin + _end, no zero tail:
+    rows past R_used keep their bytes)."""
     w = WORKLOADS["fp8_b128_n8192"]
     say(f"[parity] {w.name}: {w.describe()}; halves={halves}")
     r_max = oracle.max_rows(w.n, w.k, w.e, w.a)
@@ -184,18 +187,17 @@ def test_fp8_workload_sampled_parity(moe, halves):
     pl = oracle.plan(inp["ids"], w.e, w.ep, w.a, w.capacity, w.h)
     assert_plan_equal(got, pl)
     assert got["status"] == 0
-    rng = np.random.default_rng(123)
-    toks = np.unique(np.concatenate([[0, 1, w.n - 1], rng.choice(w.n, 253, replace=False)]))
-    enc, enc_sc = oracle.encode_rows("fp8", inp["hidden"][toks])
+    enc, enc_sc = oracle.encode_rows("fp8", inp["hidden"])
+    ru = pl["r_used"]
     pay = got["payload"].reshape(r_max, w.h)
-    sc = got["scales"].reshape(r_max, -1).view(np.float32)
-    for i, t in enumerate(toks):
-        for j in range(w.k):
-            s = pl["slot"][t, j]
-            assert np.array_equal(pay[s], enc[i]), (t, j)
-            assert np.array_equal(sc[s], enc_sc[i]), (t, j)
-    ref = oracle.combine(pl["slot"][toks], inp["weights"][toks], inp["expert_out"])
-    assert assert_combine_close(got["out"][toks], ref) == 0
+    sc = got["scales"].reshape(r_max, -1)
+    assert_rows_are_tokens(pay[:ru], sc[:ru], enc, enc_sc, pl["packed_src"][:ru])
+    if halves:
+        assert np.all(pay[ru:] == SENTINEL) and np.all(sc[ru:] == SENTINEL)
+    else:
+        assert not np.any(pay[ru:]) and not np.any(sc[ru:])
+    ref = oracle.combine(pl["slot"], inp["weights"], inp["expert_out"])
+    assert assert_combine_close(got["out"], ref) == 0
 
 
 # ----------------------------------------------------------- fuzz shapes ---
