@@ -40,7 +40,10 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, published
-DEFAULT_WORKLOAD = "uniform_bf16_n4096"
+DEFAULT_WORKLOAD = "zipf_bf16_n16384"
+# further configurations measured in the same run, each reported with its own
+# roofline under "configs" (the decode shape's µs are under "decode")
+EXTRA_WORKLOADS = ("uniform_bf16_n4096", "fp8_b128_n8192")
 METRIC = "dispatch+combine effective HBM GB/s (% of peak) on 1 GPU; µs at decode shape"
 
 
@@ -435,19 +438,37 @@ def _latencies(torch, path, step, iters, per_graph):
     return out
 
 
-def cpu_baseline(w, inp, budget_s=10.0, pass_s=2.0):
-    """The CPU oracle on the host (single thread): plan + dispatch + combine on
-    the first M tokens of the workload (a smaller instance of the same
-    routing), M chosen so that one pass takes about pass_s, repeated until
-    about budget_s of CPU time; GB/s with the same algorithmic byte formula."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_cores():
+    """Host cores this process may run on."""
+    return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(w, inp, pass_s=5.0, runs=3):
+    """The CPU oracle on the host: plan + dispatch + combine on the first M
+    tokens of the workload (a smaller instance of the same routing), M chosen
+    so that one single-thread pass takes about pass_s; the median of `runs`
+    passes on one thread, then of `runs` passes on every host core the
+    process may use (the oracle's OpenMP row loops); GB/s by wall clock with
+    the same algorithmic byte formula.  Both give bit-identical outputs."""
     import oracle
     oracle.build(force=False)
     if w.exchange:
-        return cpu_baseline_exchange(w, inp, budget_s, pass_s)
+        return cpu_baseline_exchange(w, inp, pass_s, runs)
 
     def one_pass(m):
         ids, wts, x = inp["ids"][:m], inp["weights"][:m], inp["hidden"][:m]
-        t0 = time.process_time()
+        t0 = time.perf_counter()
         kept = None
         if w.capacity_factor is not None:
             cap = oracle.expert_capacity(m, w.k, w.e, w.capacity_factor)
@@ -462,27 +483,43 @@ def cpu_baseline(w, inp, budget_s=10.0, pass_s=2.0):
         y = pay.view(np.uint16).reshape(pl["r_max"], -1) if "expert_out" not in inp \
             else inp["expert_out"]
         oracle.combine(pl["slot"], wts, y)
-        dt = time.process_time() - t0
+        dt = time.perf_counter() - t0
         sub = dataclasses.replace(w, n=m)
         return dt, step_bytes(sub, pl["r_used"], pl["r_max"], kept)["total"]
 
-    m = min(w.n, 64)
-    dt, _ = one_pass(m)
-    m = int(min(w.n, max(1, m * pass_s / max(dt, 1e-6))))
-    runs, total_bytes, t_total = 0, 0, 0.0
-    while t_total < budget_s and runs < 50:
-        dt, nbytes = one_pass(m)
-        t_total += dt
-        total_bytes += nbytes
-        runs += 1
-    return dict(value=round(total_bytes / t_total / 1e9, 3), unit="GB/s", cores=1,
-                kind="oracle",
-                sample=f"{runs} passes of plan+dispatch+combine over the first {m} of {w.n} "
-                       f"tokens of {w.name} ({w.describe()}), {t_total:.1f} s CPU, "
-                       "single thread")
+    res, m, cores = _cpu_runs(w, one_pass, min(w.n, 64), pass_s, runs)
+    return cpu_record(res, m, cores, f"the first {m} of {w.n} tokens of {w.name} "
+                                     f"({w.describe()})", runs)
 
 
-def cpu_baseline_exchange(w, inp, budget_s, pass_s):
+def _cpu_runs(w, one_pass, m0, pass_s, runs):
+    import oracle
+    cores = host_cores()
+    oracle.set_threads(1)
+    dt, _ = one_pass(m0)
+    m = int(min(w.n, max(1, m0 * pass_s / max(dt, 1e-6))))
+    res = {}
+    for threads in (1, cores):
+        oracle.set_threads(threads)
+        one_pass(min(m, 16))  # start the threads
+        meas = [one_pass(m) for _ in range(runs)]
+        gbps = sorted(nb / dt / 1e9 for dt, nb in meas)
+        res[threads] = (gbps[len(gbps) // 2], float(np.median([dt for dt, _ in meas])))
+    oracle.set_threads(cores)
+    return res, m, cores
+
+
+def cpu_record(res, m, cores, what, runs=3):
+    (one, t_one), (allc, t_all) = res[1], res[cores]
+    return dict(value=round(allc, 3), unit="GB/s", cores=cores, kind="oracle",
+                single_thread=dict(value=round(one, 3), unit="GB/s", cores=1),
+                cpu_model=cpu_model(),
+                sample=f"plan+dispatch+combine over {what}; median of {runs} passes by wall "
+                       f"clock: {t_one:.2f} s a pass on 1 thread, {t_all:.2f} s on {cores} "
+                       f"threads (OpenMP over rows; identical outputs)")
+
+
+def cpu_baseline_exchange(w, inp, pass_s, runs):
     """The CPU oracle's exchange (plan, receive buffers, reverse combine) on
     the first M tokens of every rank, with C scaled by M / N."""
     import oracle
@@ -495,87 +532,57 @@ def cpu_baseline_exchange(w, inp, budget_s, pass_s):
         ids = np.ascontiguousarray(ids3[:, :m])
         x = np.ascontiguousarray(x3[:, :m].reshape(-1, w.h))
         wts = np.ascontiguousarray(w3[:, :m].reshape(-1, w.k))
-        t0 = time.process_time()
+        t0 = time.perf_counter()
         xp = oracle.exchange_plan(ids, w.e, cap, w.h)
         pay, _ = oracle.exchange_dispatch(w.fmt, x, xp)
         y = pay.view(np.uint16).reshape(w.ep * cap, -1) if "expert_out" not in inp \
             else inp["expert_out"]
         oracle.combine(xp["recv_slot"].reshape(-1, w.k), wts, y)
-        dt = time.process_time() - t0
+        dt = time.perf_counter() - t0
         sub = dataclasses.replace(w, n=m, recv_capacity=cap)
         used = int(np.minimum(xp["recv_rows"], cap).sum())
         return dt, step_bytes(sub, used, w.ep * cap)["total"]
 
-    m = min(w.n, 16)
-    dt, _ = one_pass(m)
-    m = int(min(w.n, max(1, m * pass_s / max(dt, 1e-6))))
-    runs, total_bytes, t_total = 0, 0, 0.0
-    while t_total < budget_s and runs < 50:
-        dt, nbytes = one_pass(m)
-        t_total += dt
-        total_bytes += nbytes
-        runs += 1
-    return dict(value=round(total_bytes / t_total / 1e9, 3), unit="GB/s", cores=1,
-                kind="oracle",
-                sample=f"{runs} passes of the exchange plan, receive buffers and combine over "
-                       f"the first {m} of {w.n} tokens of each of {w.ranks} ranks of {w.name} "
-                       f"({w.describe()}; C scaled to {-(-w.capacity * m // w.n)}), "
-                       f"{t_total:.1f} s CPU, single thread")
+    res, m, cores = _cpu_runs(w, one_pass, min(w.n, 16), pass_s, runs)
+    return cpu_record(res, m, cores,
+                      f"the first {m} of {w.n} tokens of each of {w.ranks} ranks of {w.name} "
+                      f"({w.describe()}; C scaled to {-(-w.capacity * m // w.n)})", runs)
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--copies", type=int, default=0, help="buffer sets rotated over (0: auto)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--decode-workload", default="decode_mxfp4_n128",
-                    help="workload whose µs per step is reported under 'decode'")
-    ap.add_argument("--no-copy-ref", action="store_true")
-    args = ap.parse_args()
-
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build "
-              "measures one GPU's share of the work, with expert-parallel ranks simulated as "
-              "segments of one buffer.", file=sys.stderr)
-        sys.exit(2)
-
-    import torch
-    import combine_topk_ids_amd.moe as moe
-    from combine_topk_ids_amd.workloads import WORKLOADS, make_inputs
-
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    w = WORKLOADS[args.workload]
-    log(f"[bench] workload {w.name}: {w.describe()}")
+def measure(moe, torch, w, args, context=True):
+    """Time one workload: the step over rotating buffer sets, per-kernel
+    events, the roofline of the dominant kernel; with `context`, also the
+    warm step (one buffer set) and the step as three separate calls."""
     expert_cap = 0
     if w.capacity_factor is not None:
         expert_cap = moe.moe_expert_capacity(w.n, w.k, w.e, w.capacity_factor)
     r_max = buffer_rows(w, expert_cap)
+    from combine_topk_ids_amd.workloads import make_inputs
     inp = make_inputs(w, seed=0, expert_rows=r_max)
     set_bytes = (w.tokens * w.h * 2 * 2 + r_max * row_bytes(w.fmt, w.h)
                  + (r_max * w.h * 2 if "expert_out" in inp else 0))
     copies = args.copies or max(2, min(8, -(-(768 << 20) // max(set_bytes, 1)) + 1))
     path = ExchangePath(moe, torch, w, inp, copies) if w.exchange else \
         Path(moe, torch, w, inp, copies, expert_cap)
-    log(f"[bench] {copies} buffer sets of {set_bytes / 1e6:.1f} MB rotated")
+    log(f"[bench] {w.name}: {w.describe()}; {copies} buffer sets of "
+        f"{set_bytes / 1e6:.1f} MB rotated")
 
     ms, wall = time_steps(torch, path, args.steps, args.warmup)
-    log(f"[bench] timed {args.steps} steps: {ms * 1e3:.2f} us/step (wall {wall:.3f} s)")
-    # context: the same buffer set every step, so inputs may stay in the caches
-    warm_ms, _ = time_steps(torch, _SameSet(path), args.steps, args.warmup)
-    log(f"[bench] warm (one buffer set): {warm_ms * 1e3:.2f} us/step")
-    three_ms = None
-    if not w.exchange:
-        # context: the same step as the plan call, the dispatch call, the combine
-        three_ms, _ = time_steps(torch, _ThreeCalls(path), args.steps, args.warmup)
-        log(f"[bench] plan_and_dispatch {path.mode()}; as three calls: {three_ms * 1e3:.2f} us/step")
+    log(f"[bench] {w.name}: timed {args.steps} steps: {ms * 1e3:.2f} us/step (wall {wall:.3f} s)")
+    warm_ms = three_ms = None
+    if context:
+        # the same buffer set every step, so inputs may stay in the caches
+        warm_ms, _ = time_steps(torch, _SameSet(path), args.steps, args.warmup)
+        log(f"[bench] {w.name}: warm (one buffer set): {warm_ms * 1e3:.2f} us/step")
+        if not w.exchange:
+            # the same step as the plan call, the dispatch call, the combine
+            three_ms, _ = time_steps(torch, _ThreeCalls(path), args.steps, args.warmup)
+            log(f"[bench] {w.name}: plan_and_dispatch {path.mode()}; as three calls: "
+                f"{three_ms * 1e3:.2f} us/step")
     kt = time_kernels(torch, path, args.steps, moe)
-    log(f"[bench] per-kernel means (us): plan {kt['plan'] * 1e3:.2f} dispatch "
+    log(f"[bench] {w.name}: per-kernel means (us): plan {kt['plan'] * 1e3:.2f} dispatch "
         f"{kt['dispatch'] * 1e3:.2f} combine {kt['combine'] * 1e3:.2f}")
-    log("[bench] p10/p50/p90 (us): " + "; ".join(
+    log(f"[bench] {w.name}: p10/p50/p90 (us): " + "; ".join(
         f"{n} {kt[n + '_p10'] * 1e3:.2f}/{kt[n + '_p50'] * 1e3:.2f}/{kt[n + '_p90'] * 1e3:.2f}"
         for n in ("plan", "dispatch", "combine", "step")))
     ru = path.r_used()
@@ -604,21 +611,6 @@ def main():
                     traffic=traffic, algorithmic_bytes=dom_bytes,
                     avg_launch_us=round(kt[dom] * 1e3, 2))
 
-    extra = {}
-    if not args.no_copy_ref:
-        extra["stream_ref_gbps"] = round(stream_reference(torch), 1)
-        log(f"[bench] 1 GiB read + 1 GiB write streaming kernel: {extra['stream_ref_gbps']} GB/s")
-    if not args.no_decode:
-        dw = WORKLOADS[args.decode_workload]
-        dinp = make_inputs(dw, seed=0, expert_rows=buffer_rows(dw))
-        extra["decode"] = decode_latency(moe, torch, dw, dinp)
-        log(f"[bench] decode: {extra['decode']}")
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, inp)
-        log(f"[bench] cpu baseline: {cpu}")
-
     config = {"workload": w.name, "tokens": w.n, "hidden": w.h, "experts": w.e,
               "top_k": w.k, "ep_ranks_simulated": w.ep, "pad_multiple": w.a,
               "format": w.fmt, "routing": w.routing, "r_used": ru, "r_max": r_max,
@@ -633,27 +625,92 @@ def main():
     if expert_cap:
         config.update(capacity_factor=w.capacity_factor, expert_capacity=expert_cap,
                       pairs_kept=path.kept(), path="fixed expert capacity, later pairs dropped")
+    rec = dict(value=round(value, 1), unit="GB/s", ms_per_step=round(ms, 5),
+               frac_of_peak=round(value / PEAK_HBM_GBPS, 4), dtype=w.fmt, config=config,
+               bytes_per_step=b, payload_only=payload_only,
+               kernel_us={k: round(v * 1e3, 2) for k, v in kt.items()}, roofline=roofline)
+    if context:
+        rec["warm_us_per_step"] = round(warm_ms * 1e3, 2)
+        rec["three_calls_us_per_step"] = None if three_ms is None else round(three_ms * 1e3, 2)
+    del path
+    torch.cuda.empty_cache()
+    return rec, inp
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--extra", default=",".join(EXTRA_WORKLOADS),
+                    help="comma-separated workloads also measured, each under 'configs' "
+                         "('' for none)")
+    ap.add_argument("--copies", type=int, default=0, help="buffer sets rotated over (0: auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--decode-workload", default="decode_mxfp4_n128",
+                    help="workload whose µs per step is reported under 'decode'")
+    ap.add_argument("--no-copy-ref", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build "
+              "measures one GPU's share of the work, with expert-parallel ranks simulated as "
+              "segments of one buffer.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import combine_topk_ids_amd.moe as moe
+    from combine_topk_ids_amd.workloads import WORKLOADS, make_inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    w = WORKLOADS[args.workload]
+    log(f"[bench] headline workload {w.name}: {w.describe()}")
+    head, inp = measure(moe, torch, w, args, context=True)
+
+    extra = {}
+    configs = {}
+    for name in [x for x in args.extra.split(",") if x and x != w.name]:
+        rec, _ = measure(moe, torch, WORKLOADS[name], args, context=False)
+        configs[name] = rec
+    if configs:
+        extra["configs"] = configs
+    if not args.no_copy_ref:
+        extra["stream_ref_gbps"] = round(stream_reference(torch), 1)
+        log(f"[bench] 1 GiB read + 1 GiB write streaming kernel: {extra['stream_ref_gbps']} GB/s")
+    if not args.no_decode:
+        dw = WORKLOADS[args.decode_workload]
+        dinp = make_inputs(dw, seed=0, expert_rows=buffer_rows(dw))
+        extra["decode"] = decode_latency(moe, torch, dw, dinp)
+        log(f"[bench] decode: {extra['decode']}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, inp)
+        log(f"[bench] cpu baseline: {cpu}")
+
     rec = {
         "metric": METRIC,
-        "value": round(value, 1),
+        "value": head["value"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 5),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.fmt if w.fmt != "mxfp4" else "mxfp4",
+        "dtype": w.fmt,
         "data": "synthetic",
-        "config": config,
-        "frac_of_peak": round(value / PEAK_HBM_GBPS, 4),
-        "bytes_per_step": b,
-        "payload_only": payload_only,
-        "warm_us_per_step": round(warm_ms * 1e3, 2),
-        "three_calls_us_per_step": None if three_ms is None else round(three_ms * 1e3, 2),
-        "kernel_us": {k: round(v * 1e3, 2) for k, v in kt.items()},
-        "roofline": roofline,
+        "config": head["config"],
+        "frac_of_peak": head["frac_of_peak"],
+        "bytes_per_step": head["bytes_per_step"],
+        "payload_only": head["payload_only"],
+        "warm_us_per_step": head["warm_us_per_step"],
+        "three_calls_us_per_step": head["three_calls_us_per_step"],
+        "kernel_us": head["kernel_us"],
+        "roofline": head["roofline"],
         "cpu_baseline": cpu,
     }
     rec.update(extra)
