@@ -3,8 +3,16 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "moe.h"
 #include "moe_kernels.hpp"
+
+// Workspace of moe_plan_and_dispatch_noalloc: one per GPU, for the life of
+// the process.  In host code `scratch` names a host-side stand-in, not the
+// device array: host code uses only the address that hipGetSymbolAddress
+// returns for the current device (noalloc_scratch below).
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -128,6 +136,25 @@ int pd_end(const moe_problem &p, const int32_t *ids, const moe_plan &plan, const
     return launched(moe::launch_dispatch(p, plan, hidden, w, input_scale, payload, scales, s));
   return launched(moe::launch_plan_dispatch(p, ids, plan, hidden, w, input_scale, payload, scales,
                                             workspace, s));
+}
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices] = {};
+
+int noalloc_scratch(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_EHIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return MOE_EHIP;
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return MOE_OK;
 }
 
 }  // namespace
@@ -270,6 +297,23 @@ MOE_API int moe_plan_and_dispatch(const moe_problem *p, const int32_t *topk_ids,
   return pd_end(*p, topk_ids, *plan, hidden, topk_weights, input_scale, payload, scales, workspace, s);
 }
 
+MOE_API int moe_plan_and_dispatch_noalloc(const moe_problem *p, const int32_t *topk_ids,
+                                          const moe_plan *plan, const uint16_t *hidden,
+                                          const float *topk_weights, const float *input_scale,
+                                          void *payload, void *scales, void *stream) {
+  const int rc = check(p);
+  if (rc != MOE_OK) return rc;
+  const size_t need = moe::plan_workspace_bytes(*p);
+  if (need > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ESCRATCH;
+  void *ws = nullptr;
+  if (need > 0) {
+    const int src = noalloc_scratch(&ws);
+    if (src != MOE_OK) return src;
+  }
+  return moe_plan_and_dispatch(p, topk_ids, plan, hidden, topk_weights, input_scale, payload, scales,
+                               ws, stream);
+}
+
 MOE_API int moe_combine(const moe_problem *p, const moe_plan *plan, const uint16_t *expert_out,
                         const float *topk_weights, uint16_t *out, void *stream) {
   const int rc = check(p);
@@ -402,6 +446,9 @@ MOE_API const char *moe_strerror(int code) {
     case MOE_EALIGN: return "misaligned pointer (rows need 16 bytes, index arrays 4)";
     case MOE_EOVERFLOW: return "problem too large for 32-bit row indices or element counts";
     case MOE_EHIP: return "HIP launch error";
+    case MOE_ESCRATCH:
+      return "the problem's workspace exceeds the static scratch of moe_plan_and_dispatch_noalloc "
+             "(MOE_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown error code";
   }
 }

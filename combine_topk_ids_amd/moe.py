@@ -19,7 +19,8 @@ import torch  # first: libmoe then binds to the HIP runtime torch has loaded
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 
-MOE_OK, MOE_EINVAL, MOE_EALIGN, MOE_EOVERFLOW, MOE_EHIP = 0, -1, -2, -3, -4
+MOE_OK, MOE_EINVAL, MOE_EALIGN, MOE_EOVERFLOW, MOE_EHIP, MOE_ESCRATCH = 0, -1, -2, -3, -4, -5
+NOALLOC_SCRATCH_BYTES = 1 << 20  # MOE_NOALLOC_SCRATCH_BYTES
 STATUS_BAD_ID, STATUS_DUP_ID, STATUS_CAPACITY, STATUS_MAP_OVERFLOW, STATUS_DROPPED = 1, 2, 4, 8, 16
 STATUS_BAD_PLAN = 32
 FMT = {"bf16": 0, "fp8": 1, "mxfp4": 2, "nvfp4": 3}
@@ -36,7 +37,7 @@ EXPORTS = ("moe_check_problem", "moe_max_rows", "moe_expert_capacity", "moe_payl
            "moe_check_exchange", "moe_exchange_workspace_bytes", "moe_exchange_plan",
            "moe_exchange_dispatch", "moe_exchange_dispatch_scaled", "moe_exchange_dispatch_gated",
            "moe_exchange_combine", "moe_map_workspace_bytes",
-           "moe_routing_map_to_topk", "moe_strerror")
+           "moe_routing_map_to_topk", "moe_plan_and_dispatch_noalloc", "moe_strerror")
 
 
 class MoeError(RuntimeError):
@@ -87,6 +88,7 @@ def _load() -> ctypes.CDLL:
         "moe_plan_and_dispatch_mode": (ctypes.c_int, [P]),
         "moe_plan_and_dispatch_begin": (ctypes.c_int, [P, V, ctypes.POINTER(Plan), V, V]),
         "moe_plan_and_dispatch_end": (ctypes.c_int, [P, V, ctypes.POINTER(Plan), V, V, V, V, V, V, V]),
+        "moe_plan_and_dispatch_noalloc": (ctypes.c_int, [P, V, ctypes.POINTER(Plan), V, V, V, V, V, V]),
         "moe_dispatch_scaled": (ctypes.c_int, [P, ctypes.POINTER(Plan), V, V, V, V, V]),
         "moe_exchange_dispatch_scaled": (ctypes.c_int, [P, ctypes.POINTER(Exchange), V, V, V, V, V]),
         "moe_combine": (ctypes.c_int, [P, ctypes.POINTER(Plan), V, V, V, V]),
@@ -326,13 +328,14 @@ def moe_dispatch_gated(p: Problem, plan: PlanBuffers, hidden: torch.Tensor,
 
 
 def _pd_args(p: Problem, topk_ids, plan: PlanBuffers, hidden, payload, scales, topk_weights,
-             input_scale):
+             input_scale, need_workspace=True):
     r_max, pb, sb, ws = _sizes(p)
     npairs = p.n_tokens * p.top_k
     ids = _dev(topk_ids, "topk_ids", (torch.int32,), npairs)
     _dev(plan.slot, "plan.slot", (torch.int32,), npairs)
     _dev(plan.packed_src, "plan.packed_src", (torch.int32,), r_max)
-    _dev(plan.workspace, "plan.workspace", (torch.uint8,), ws)
+    if need_workspace:
+        _dev(plan.workspace, "plan.workspace", (torch.uint8,), ws)
     x = _dev(hidden, "hidden", _BF16, p.n_tokens * p.hidden)
     w = _dev(topk_weights, "topk_weights", (torch.float32,), npairs) or None
     gs = _dev(input_scale, "input_scale", (torch.float32,), 1) or None
@@ -355,6 +358,20 @@ def moe_plan_and_dispatch(p: Problem, topk_ids: torch.Tensor, plan: PlanBuffers,
     launches (moe_plan_and_dispatch_mode) where the problem allows."""
     args = _pd_args(p, topk_ids, plan, hidden, payload, scales, topk_weights, input_scale)
     _checked(lib.moe_plan_and_dispatch(*args, _stream(stream)), "moe_plan_and_dispatch")
+
+
+def moe_plan_and_dispatch_noalloc(p: Problem, topk_ids: torch.Tensor, plan: PlanBuffers,
+                                  hidden: torch.Tensor, payload: torch.Tensor,
+                                  scales: torch.Tensor | None,
+                                  topk_weights: torch.Tensor | None = None,
+                                  input_scale: torch.Tensor | None = None, stream=None) -> None:
+    """moe_plan_and_dispatch with the plan's workspace in the library's static
+    device scratch (plan.workspace is not used); raises MoeError with
+    MOE_ESCRATCH for problems whose workspace exceeds NOALLOC_SCRATCH_BYTES."""
+    args = _pd_args(p, topk_ids, plan, hidden, payload, scales, topk_weights, input_scale,
+                    need_workspace=False)
+    _checked(lib.moe_plan_and_dispatch_noalloc(*args[:-1], _stream(stream)),
+             "moe_plan_and_dispatch_noalloc")
 
 
 def moe_plan_and_dispatch_mode(p: Problem) -> int:

@@ -69,6 +69,8 @@ extern "C" {
 #define MOE_EALIGN (-2)    /* a row pointer is not 16-byte aligned          */
 #define MOE_EOVERFLOW (-3) /* R_max*H >= 2^32 (table) or rows >= 2^31       */
 #define MOE_EHIP (-4)      /* the HIP runtime reported a launch error       */
+#define MOE_ESCRATCH (-5)  /* moe_plan_and_dispatch_noalloc: the problem's
+                              workspace exceeds MOE_NOALLOC_SCRATCH_BYTES     */
 
 /* ---- bits of plan->status (device, written by moe_dispatch_plan and by
  *      moe_plan_and_dispatch) ------------------------------------------ */
@@ -441,6 +443,33 @@ MOE_API int moe_routing_map_to_topk(const moe_problem *p,
                                     const float *probs, int32_t *topk_ids,
                                     float *topk_weights, uint32_t *status,
                                     void *workspace, void *stream);
+
+/* ---- plan and dispatch with no caller workspace ----------------------------
+ *
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.
+ * moe_plan_and_dispatch_noalloc is moe_plan_and_dispatch with the plan's
+ * workspace (the counting kernel's tile histograms and fault bits) taken
+ * from a static device array of MOE_NOALLOC_SCRATCH_BYTES inside the
+ * library instead of a caller buffer: same arguments otherwise, same
+ * outputs byte for byte, same launches on `stream`.  It allocates nothing
+ * and frees nothing.  The caller still passes every input and output.
+ *   - A problem whose moe_workspace_bytes exceeds MOE_NOALLOC_SCRATCH_BYTES
+ *     (more than 262,144 histogram entries: count tiles of at most 2048
+ *     pairs times E + 1) returns MOE_ESCRATCH and launches nothing.
+ *   - Each GPU holds its own copy of the array, from its first use until the
+ *     process ends; its device address is looked up once per device (with
+ *     that device current: the stream must belong to the current device).
+ *   - Every call on one GPU shares that GPU's array, which keeps the last
+ *     call's contents (the counting kernel rewrites every entry it uses, so
+ *     nothing needs clearing).  Calls that overlap on one GPU -- on two
+ *     streams, or from two host threads without ordering -- race on it;
+ *     calls on one stream are ordered and safe. */
+#define MOE_NOALLOC_SCRATCH_BYTES (1u << 20)
+MOE_API int moe_plan_and_dispatch_noalloc(const moe_problem *p, const int32_t *topk_ids,
+                                          const moe_plan *plan, const uint16_t *hidden,
+                                          const float *topk_weights, const float *input_scale,
+                                          void *payload, void *scales, void *stream);
 
 /* Static text for a return code. */
 MOE_API const char *moe_strerror(int code);

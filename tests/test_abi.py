@@ -196,7 +196,7 @@ def test_workspace_required_only_for_multi_tile_plans(moe):
 
 
 def test_strerror(moe):
-    for c in (0, -1, -2, -3, -4, 7):
+    for c in (0, -1, -2, -3, -4, -5, 7):
         assert isinstance(moe.strerror(c), str) and moe.strerror(c)
 
 
@@ -321,3 +321,21 @@ def test_nvfp4_sizes_and_entry_points(moe):
     assert moe.lib.moe_exchange_dispatch(ref(px), ref(fx), fake, fake, fake, None) == -1
     assert moe.lib.moe_exchange_dispatch_scaled(ref(px), ref(fx), fake, None, fake, fake, None) == -1
     assert moe.lib.moe_exchange_dispatch_scaled(ref(px), ref(fx), fake, fake, fake, None, None) == -1
+
+
+def test_noalloc_refuses_a_problem_past_its_scratch(moe):
+    """moe_plan_and_dispatch_noalloc returns MOE_ESCRATCH, before any launch,
+    for a problem whose workspace exceeds MOE_NOALLOC_SCRATCH_BYTES (E = 1024
+    and 274 count tiles: 274 * 1025 * 4 bytes), and rejects an invalid
+    problem as every entry point does."""
+    p = moe.problem(70000, 64, 8, 1024, 8)
+    assert moe.moe_workspace_bytes(p) > moe.NOALLOC_SCRATCH_BYTES
+    fake = 1 << 20  # never dereferenced: the size check fails first
+    plan = moe.Plan(*([fake] * 7))
+    call = moe.lib.moe_plan_and_dispatch_noalloc
+    rc = call(ctypes.byref(p), fake, ctypes.byref(plan), fake, None, None, fake, None, None)
+    assert rc == moe.MOE_ESCRATCH == -5
+    assert "scratch" in moe.strerror(rc)
+    bad = moe.problem(64, 12, 2, 8, 4)
+    assert call(ctypes.byref(bad), fake, ctypes.byref(plan), fake, None, None, fake, None,
+                None) == moe.MOE_EINVAL
