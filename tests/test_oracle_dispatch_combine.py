@@ -281,3 +281,29 @@ def test_dispatch_rejects_inputs_it_would_read_past(orc):
     assert np.array_equal(pay[1], x[3]) and np.all(pay[2] == 0)
     with pytest.raises(ValueError):
         orc.routing_map_to_topk(np.ones((2, 4), np.uint8), np.ones((2, 3), np.float32), 2)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "mxfp4"])
+def test_threads_do_not_change_results(orc, fmt):
+    """The oracle's row loops on one thread and on several give the same bytes
+    (plan, every packed and scale row, encoded rows, combine), so the timed
+    all-cores baseline computes what the single-thread oracle computes."""
+    rng = np.random.default_rng(900)
+    n, h, e, k, ep, a = 700, 256, 32, 4, 8, 4
+    ids, w = random_routing(rng, n, e, k, masked_frac=0.1)
+    x = random_bf16(rng, (n, h))
+    res = []
+    prev = orc.threads()
+    for threads in (1, 5):
+        orc.set_threads(threads)
+        assert orc.threads() == threads
+        pl = orc.plan(ids, e, ep, a, n * min(k, e // ep), h)
+        pay, sc = orc.dispatch(fmt, x, pl)
+        enc, enc_sc = orc.encode_rows(fmt, x)
+        y = random_bf16(np.random.default_rng(901), (pl["r_max"], h))
+        out = orc.combine(pl["slot"], w, y)
+        res.append([pl["slot"], pl["packed_src"], pl["expert_offsets"], pay, enc, out]
+                   + ([sc, enc_sc] if sc is not None else []))
+    orc.set_threads(prev)
+    for a_, b_ in zip(*res):
+        assert np.array_equal(a_, b_)
