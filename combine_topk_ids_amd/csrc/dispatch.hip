@@ -856,16 +856,6 @@ hipError_t launch_dispatch(const moe_problem &p, const moe_plan &plan, const uin
   return launch_args(g, p.fmt, stream);
 }
 
-PlanDispatchMode plan_dispatch_mode(const moe_problem &p) {
-  if (p.expert_capacity != 0) return PlanDispatchMode::kSeparate;
-  const int64_t npairs = p.n_tokens * p.top_k;
-  if (npairs <= kSmallPairs) return PlanDispatchMode::kOneLaunch;
-  const PlanGeom geo = plan_geometry(p);
-  if (static_cast<int64_t>(geo.ntiles) * p.n_experts <= kTileHist && max_rows(p) <= INT32_MAX)
-    return PlanDispatchMode::kTiled;
-  return PlanDispatchMode::kSeparate;
-}
-
 hipError_t launch_plan_dispatch(const moe_problem &p, const int32_t *ids, const moe_plan &plan,
                                 const uint16_t *hidden, const float *gates, const float *gscale,
                                 void *payload, void *scales, void *workspace, hipStream_t stream) {

@@ -178,49 +178,14 @@ __global__ __launch_bounds__(kThreads) void exchange_remap_kernel(ExchangeArgs g
   for (int64_t i = used + static_cast<int64_t>(xb) * kThreads + tid; i < g.cap; i += stride) src[i] = -1;
 }
 
-size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
-
-// Workspace: [R][E+1] offsets and [R][N*k] packed_src of the per-rank
-// plans, then R copies of the single-rank plan workspace.
-struct Layout {
-  size_t offsets, packed_src, plan_ws, total;
-  size_t plan_ws_bytes;  // per rank
-};
-
-moe_problem rank_problem(const moe_problem &p) {
-  moe_problem q = p;
-  q.pad_multiple = 1;
-  q.recv_capacity = INT64_MAX;  // capacity applies to receive buffers only
-  q.flags = 0;
-  q.expert_capacity = 0;
-  return q;
-}
-
-Layout layout(const moe_problem &p) {
-  const size_t R = static_cast<size_t>(p.ep);
-  Layout L;
-  size_t at = 0;
-  L.offsets = at;
-  at += align256(R * (p.n_experts + 1) * sizeof(int32_t));
-  L.packed_src = at;
-  at += align256(R * static_cast<size_t>(p.n_tokens) * p.top_k * sizeof(int32_t));
-  L.plan_ws_bytes = plan_workspace_bytes(rank_problem(p));
-  L.plan_ws = at;
-  at += R * L.plan_ws_bytes;
-  L.total = at;
-  return L;
-}
-
 }  // namespace
-
-size_t exchange_workspace_bytes(const moe_problem &p) { return layout(p).total; }
 
 hipError_t launch_exchange_plan(const moe_problem &p, const int32_t *ids, const moe_exchange &x,
                                 void *workspace, hipStream_t stream) {
-  const Layout L = layout(p);
+  const ExchangeLayout L = exchange_layout(p);
   uint8_t *ws = static_cast<uint8_t *>(workspace);
   const int R = p.ep;
-  const moe_problem q = rank_problem(p);
+  const moe_problem q = exchange_rank_problem(p);
   int32_t *offsets = reinterpret_cast<int32_t *>(ws + L.offsets);
 
   // 1. every rank's own plan, one launch

@@ -51,8 +51,9 @@ namespace {
 
 constexpr int kThreads = kPlanThreads;                  // 8 waves
 constexpr int kWaves = kPlanWaves;
-constexpr int kTilePairs = 2048;                        // count tile, whole tokens
-constexpr int kSubPairs = kThreads;                     // sub-tile: one chunk per wave
+constexpr int kTilePairs = kPlanTilePairs;             // count tile, whole tokens
+constexpr int kSubPairs = kPlanSubPairs;                // sub-tile: one chunk per wave
+static_assert(kSubPairs == kThreads, "an assign block takes one 64-pair chunk per wave");
 constexpr int kPairsPerThread = kTilePairs / kThreads;  // staging loads per thread
 constexpr int kHistBatch = 16;                          // column loads in flight
 static_assert(kMaxExperts <= 2 * kThreads, "the expert scan gives each thread two experts");
@@ -500,30 +501,6 @@ void launch_k(const PlanArgs &g, bool fused, int e, int ranks, hipStream_t strea
 }
 
 }  // namespace
-
-PlanGeom plan_geometry(const moe_problem &p) {
-  PlanGeom geo;
-  geo.npairs = p.n_tokens * p.top_k;
-  geo.tile_tokens = max(1, kTilePairs / p.top_k);
-  geo.tile_pairs = static_cast<int64_t>(geo.tile_tokens) * p.top_k;
-  geo.ntiles = p.n_tokens == 0 ? 1
-                               : static_cast<int>((p.n_tokens + geo.tile_tokens - 1) / geo.tile_tokens);
-  geo.single = geo.ntiles == 1;
-  // sub-tiles per count tile: every tile but the last holds tile_pairs pairs
-  const int64_t span = geo.single ? geo.npairs : geo.tile_pairs;
-  geo.subs = span > kSubPairs ? static_cast<int>((span + kSubPairs - 1) / kSubPairs) : 1;
-  int bits = 0;
-  while ((1 << bits) < p.n_experts) ++bits;
-  geo.key_bits = bits;
-  return geo;
-}
-
-size_t plan_workspace_bytes(const moe_problem &p) {
-  const PlanGeom geo = plan_geometry(p);
-  if (geo.single) return 0;
-  const size_t bytes = static_cast<size_t>(geo.ntiles) * (p.n_experts + 1) * sizeof(int32_t);
-  return (bytes + 255) & ~static_cast<size_t>(255);
-}
 
 namespace {
 

@@ -30,8 +30,8 @@
 namespace moe {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kLaneExperts = 16;  // map bytes per lane
+constexpr int kThreads = kMapThreads;
+constexpr int kLaneExperts = kMapLaneExperts;  // map bytes per lane
 
 struct MapArgs {
   const uint8_t *map;
@@ -133,25 +133,7 @@ __global__ __launch_bounds__(kThreads) void map_status_kernel(MapArgs g) {
   if (threadIdx.x == 0) *g.status = s_fl;
 }
 
-// lanes per token: ceil(E / 16) rounded up to a power of two (E <= 1024)
-int lanes_per_token(int e) {
-  const int need = (e + kLaneExperts - 1) / kLaneExperts;
-  int lpt = 1;
-  while (lpt < need) lpt <<= 1;
-  return lpt;
-}
-
-int map_blocks(const moe_problem &p) {
-  const int64_t per = kThreads / lanes_per_token(p.n_experts);
-  return static_cast<int>((p.n_tokens + per - 1) / per);
-}
-
 }  // namespace
-
-size_t map_workspace_bytes(const moe_problem &p) {
-  const size_t bytes = static_cast<size_t>(map_blocks(p)) * sizeof(uint32_t);
-  return (bytes + 255) & ~static_cast<size_t>(255);
-}
 
 hipError_t launch_routing_map_to_topk(const moe_problem &p, const uint8_t *map, const float *probs,
                                       int32_t *ids, float *weights, uint32_t *status, void *workspace,
@@ -166,7 +148,7 @@ hipError_t launch_routing_map_to_topk(const moe_problem &p, const uint8_t *map, 
   g.n = p.n_tokens;
   g.e = p.n_experts;
   g.k = p.top_k;
-  g.lpt = lanes_per_token(p.n_experts);
+  g.lpt = map_lanes_per_token(p.n_experts);
   g.nblocks = map_blocks(p);
   g.vec = p.n_experts % 16 == 0 && (reinterpret_cast<uintptr_t>(map) & 15) == 0;
   if (g.nblocks > 0) map_to_topk_kernel<<<g.nblocks, kThreads, 0, stream>>>(g);

@@ -38,18 +38,19 @@
 // after the counting are the same in both modes.
 #pragma once
 
+#include "host_checks.hpp"
 #include "moe_device.hpp"
 
 namespace moe {
 
-constexpr int kSmallPairs = 2048;    // pairs a small plan holds
+// kSmallPairs: pairs a small plan holds; kTileHist: histogram entries
+// (tiles * E) a tiled plan reads (host_checks.hpp, which picks the mode)
 constexpr int kSmallThreads = 256;   // one workgroup
 constexpr int kSmallWaves = kSmallThreads / kWave;
 constexpr int kSmallLoads = kSmallPairs / kSmallThreads;  // IDs per thread
 constexpr int kSmallTargets = kSmallThreads;              // own pairs, one per thread
 constexpr int kSmallIds = kSmallPairs + kSmallTargets;    // LDS IDs: tiled mode reads up to this many
 constexpr int kTileLoads = kSmallIds / kSmallThreads;     // IDs per thread in tiled mode
-constexpr int kTileHist = 2048;                           // histogram entries (tiles * E) a tiled plan reads
 constexpr int kTileHistLoads = kTileHist / kSmallThreads;
 static_assert(kMaxExperts <= 4 * kSmallThreads, "the expert scan gives each thread four experts");
 static_assert(kSmallTargets >= kSmallWaves * kMaxTopK, "own pairs: up to one token per wave");

@@ -25,6 +25,9 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
+# A separately built copy to load instead (the sanitizer test builds one with
+# address and undefined-behaviour checks and runs the pins against it).
+PREBUILT = os.environ.get("ORACLE_PREBUILT_LIB")
 
 FMT = {"bf16": 0, "fp8": 1, "mxfp4": 2}
 BAD_ID, DUP_ID, CAPACITY, MAP_OVERFLOW, DROPPED = 1, 2, 4, 8, 16
@@ -34,6 +37,8 @@ _lib = None
 
 def build(force: bool = True) -> str:
     """Compile ``oracle.c`` into ``liboracle.so`` next to it."""
+    if PREBUILT:
+        return PREBUILT
     if force or not os.path.exists(LIB):
         tmp = LIB + ".tmp%d" % os.getpid()
         subprocess.check_call(
@@ -46,9 +51,12 @@ def build(force: bool = True) -> str:
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB):
-            build(force=False)
-        lib = ctypes.CDLL(LIB)
+        if PREBUILT:
+            lib = ctypes.CDLL(PREBUILT)
+        else:
+            if not os.path.exists(LIB):
+                build(force=False)
+            lib = ctypes.CDLL(LIB)
         p = ctypes.c_void_p
         i64, i32 = ctypes.c_int64, ctypes.c_int
         lib.oracle_max_rows.restype = i64
