@@ -3,7 +3,7 @@
 //
 // What is computed (pages cited by title and section):
 //   NKI permute_a2av API reference -- description and :return: (rows packed
-//     per destination, then deterministic zero padding).
+//     per destination; unused rows are zero bytes).
 //   NeMo Automodel token_dispatcher API -- get_permuted_hidden_states_by_experts
 //     (rows permuted into expert order by a fused kernel),
 //     TokenDispatcherConfig.moe_router_expert_pad_multiple (pad rows).
@@ -379,8 +379,8 @@ __device__ void slab_nvfp4(const DispatchArgs &g, int slab, int my_slot, const R
 }
 
 // ---- gated copies: row slot[t][j] holds encode(fl32(w[t][j] * x[t])) -------
-// (DeepSpeed v0.19.4 function index, page 15: token representations
-// pre-multiplied by router scores before expert compute.)  The slab is read
+// (DeepSpeed v0.19.4 function index, page 15: the entry on scaling token
+// rows by their router scores ahead of the experts.)  The slab is read
 // once; every copy is multiplied by its own gate and encoded on its own.  A
 // block maximum of the products needs no new reduction: rounding is
 // monotone, so max |fl32(w x_i)| = fl32(|w| max |x_i|).

@@ -5,8 +5,8 @@
 //   NKI permute_a2av API reference -- description: the receive layout is the
 //     packed cumsum of the receive counts; the (4, EP) table's rows 2-3 hold
 //     receive counts and displacements in elements; :return: a [C, H]
-//     receive buffer of source-major packed rows followed by deterministic
-//     zero padding.
+//     receive buffer holds each source's rows in rank order, then zero
+//     rows.
 //   DeepSpeed v0.19.4 function index, page 15 -- SplitPlan entries: one
 //     all-to-all exchanges the [ep_size, E_local] count matrix; a rank
 //     receives the matrix rows that cover its experts.

@@ -32,8 +32,8 @@
  *     send displacements, receive counts and receive displacements, in
  *     elements), :param packed_source_indices: (int32 source rows in [0, N),
  *     destination-major), :param recv_capacity: (dropless bound
- *     N * min(top_k, L); duplicate IDs void it), :return: (packed rows, then
- *     deterministic zero padding).
+ *     N * min(top_k, L); duplicate IDs void it), :return: (the output
+ *     buffer: rows in use, then rows of zeros).
  *   NeMo Automodel token_dispatcher API: dispatch_preprocess2 (compact
  *     token_indices[T, K] and token_probs[T, K]), dispatch_postprocess (rows
  *     permuted by expert plus tokens per expert), _indices_to_multihot (-1
@@ -178,12 +178,19 @@ typedef struct moe_plan {
 /* ---- host-only helpers (no GPU work, safe without a device) ------------- */
 
 /* MOE_OK if the problem is well formed, else the error code the entry
- * points would return for it. */
+ * points would return for it.  The problem's fields are the ones the NKI
+ * permute_a2av API reference states (description and parameters:
+ * hidden_states [N, H], the routing, EP, recv_capacity), with E and the
+ * pad multiple of the NeMo Automodel token_dispatcher API
+ * (TokenDispatcherConfig). */
 MOE_API int moe_check_problem(const moe_problem *p);
 
 /* R_max = N*k + E*(A-1): rows of the static packed buffer (always >= R_used);
  * E*cap with a fixed expert capacity.  Negative error code if the problem is
- * invalid. */
+ * invalid.  (NKI permute_a2av API reference, :param recv_capacity: and
+ * :return: -- a static-shape buffer that every routing fits; NeMo Automodel
+ * token_dispatcher API, TokenDispatcherConfig.moe_router_expert_pad_multiple
+ * -- at most A-1 pad rows per expert.) */
 MOE_API int64_t moe_max_rows(const moe_problem *p);
 
 /* Capacity per expert for a capacity factor cf >= 0: ceil(cf * N * k / E),
@@ -191,13 +198,16 @@ MOE_API int64_t moe_max_rows(const moe_problem *p);
 MOE_API int64_t moe_expert_capacity(int64_t n_tokens, int32_t top_k,
                                     int32_t n_experts, double capacity_factor);
 
-/* Bytes of one payload row (2H, H or H/2) and of one scale row (0, 4*H/128
- * or H/32).  Negative error code if the problem is invalid. */
+/* Bytes of one payload row (2H, H or H/2) and of one scale row (0, 4*H/128,
+ * H/32 or H/16).  Negative error code if the problem is invalid.  (Mojo shmem
+ * ep_comm module: BF16TokenFormat, BlockwiseFP8TokenFormat, MXTokenFormat,
+ * NVBlockScaledTokenFormat.) */
 MOE_API int64_t moe_payload_row_bytes(const moe_problem *p);
 MOE_API int64_t moe_scale_row_bytes(const moe_problem *p);
 
 /* Device scratch bytes moe_dispatch_plan needs (0 if none; the pointer may
- * then be NULL).  The caller owns it; its contents need no initialisation
+ * then be NULL).  This is this library's own scratch (the counting kernel's
+ * tile histograms); the pages define no workspace.  The caller owns it; its contents need no initialisation
  * and are dead once the plan's kernels have run.  Returns 0 for an invalid
  * problem (moe_dispatch_plan reports the error). */
 MOE_API size_t moe_workspace_bytes(const moe_problem *p);
@@ -205,20 +215,32 @@ MOE_API size_t moe_workspace_bytes(const moe_problem *p);
 /* ---- entry points -------------------------------------------------------- */
 
 /* Routing plan from topk_ids (device int32 [N][k], -1 = masked): fills every
- * array of *plan.  workspace: moe_workspace_bytes(p) device bytes, 256-byte
- * aligned.  Deterministic: no output depends on the order in which atomic
- * operations land. */
+ * array of *plan.  (NKI permute_a2av API reference, description -- counts,
+ * cumsum offsets and the (4, EP) table in elements -- and :param
+ * recv_capacity: -- the per-rank bound, CAPACITY; NeMo Automodel
+ * token_dispatcher API, dispatch_postprocess -- tokens per expert -- and
+ * TokenDispatcherConfig.moe_router_expert_pad_multiple; DeepSpeed v0.19.4
+ * function index, page 15, the SplitPlan entry -- the per-expert histogram
+ * as an [ep_size, E_local] matrix.)  workspace: moe_workspace_bytes(p)
+ * device bytes, 256-byte aligned.  Deterministic: no output depends on the
+ * order in which atomic operations land. */
 MOE_API int moe_dispatch_plan(const moe_problem *p, const int32_t *topk_ids,
                               const moe_plan *plan, void *workspace,
                               void *stream);
 
-/* Pack token rows: hidden (device bf16 bits [N][H]) is read once per token;
+/* Pack token rows (NKI permute_a2av API reference, description and :return:
+ * -- rows permuted into destination-major order, unused rows zero; NeMo
+ * Automodel token_dispatcher API, get_permuted_hidden_states_by_experts;
+ * Mojo shmem ep_comm module, the token formats named at moe_fmt):
+ * hidden (device bf16 bits [N][H]) is read once per token;
  * each valid pair (t, j) writes encode(hidden[t]) to packed row
  * plan->slot[t*k+j] of payload (and its scale row of scales); pad rows of
  * every expert are written as zero bytes; rows past R_used are zeroed only
  * with MOE_FLAG_ZERO_TAIL.  payload/scales layouts are given by p->fmt;
  * scales must be NULL for MOE_FMT_BF16.  Reads slot, expert_counts and
- * expert_offsets of a plan made for the same problem. */
+ * expert_offsets of a plan made for the same problem; a slot outside
+ * [0, R_max) is skipped and pad rows are never written outside the buffer,
+ * whatever those arrays hold. */
 MOE_API int moe_dispatch(const moe_problem *p, const moe_plan *plan,
                          const uint16_t *hidden, void *payload, void *scales,
                          void *stream);
@@ -234,8 +256,8 @@ MOE_API int moe_dispatch_scaled(const moe_problem *p, const moe_plan *plan,
 /* Gated dispatch: as moe_dispatch, but each valid pair (t, j) writes
  * encode(fl32(topk_weights[t][j] * hidden[t][c]) for every c), the token row
  * pre-multiplied by its gate, to packed row slot[t][j] (DeepSpeed v0.19.4
- * function index, page 15: pre-multiplying token representations by router
- * scores before expert compute).  Each copy is encoded on its own: for FP8
+ * function index, page 15, the entry on applying the router scores to the
+ * token rows before the experts run).  Each copy is encoded on its own: for FP8
  * its block scale is fl32(fl32(|w| * amax) / 448) and its codes
  * E4M3(fl32(v / s)) with v = fl32(w * x); for MX-FP4 its exponent comes from
  * fl32(|w| * amax).  topk_weights: device float [N][k].  A combine of gated
@@ -297,13 +319,19 @@ MOE_API int moe_plan_and_dispatch_end(const moe_problem *p, const int32_t *topk_
                                       void *payload, void *scales, void *workspace,
                                       void *stream);
 
-/* Combine: out[t][c] = bf16_rne( fp32 fused multiply-add chain, starting
+/* Combine (DeepSpeed v0.19.4 function index, page 15, the combine entry --
+ * each token's expert outputs gathered back and weighted by the gate
+ * values; NeMo Automodel token_dispatcher API,
+ * TokenDispatcherConfig.moe_router_dtype -- the weighting in fp32):
+ * out[t][c] = bf16_rne( fp32 fused multiply-add chain, starting
  * from +0 and running over j = 0..k-1 in order, of
  * topk_weights[t][j] * expert_out[slot[t][j]][c] ), skipping slots < 0.
- * expert_out: device bf16 bits [R_max][H] (only rows some slot names are
- * read); topk_weights: device float [N][k], or NULL for weights of 1 (the
- * unweighted sum that follows a gated dispatch); out: device bf16 bits
- * [N][H]. */
+ * expert_out: device bf16 bits [R_max][H]; only rows that some slot names
+ * are read (each row through a bounds-checked load of that row alone, so a
+ * masked slot reads nothing, and a slot outside [0, R_max) is skipped like a
+ * masked one); it may be NULL when R_max = 0.  topk_weights: device float
+ * [N][k], or NULL for weights of 1 (the unweighted sum that follows a gated
+ * dispatch); out: device bf16 bits [N][H]. */
 MOE_API int moe_combine(const moe_problem *p, const moe_plan *plan,
                         const uint16_t *expert_out, const float *topk_weights,
                         uint16_t *out, void *stream);
@@ -330,8 +358,8 @@ MOE_API int moe_combine(const moe_problem *p, const moe_plan *plan,
  *
  * Passages: NKI permute_a2av API reference, description (the receive layout
  * is the packed cumsum of recv_counts; table rows 2-3 hold receive counts
- * and displacements) and :return: ([C, H], source-major packed rows followed
- * by deterministic zero padding); DeepSpeed v0.19.4 function index, page
+ * and displacements) and :return: (a [C, H] buffer per rank: the rows of
+ * each source in turn, then zero rows up to C); DeepSpeed v0.19.4 function index, page
  * 15, SplitPlan entries (one all-to-all of the [ep_size, E_local] count
  * matrix; the rows a rank receives from it); Mojo
  * ep.dispatch_async.block.scaled.nv struct, recv_count_ptrs (tokens
@@ -410,9 +438,10 @@ MOE_API int moe_exchange_dispatch_gated(const moe_problem *p,
 /* Reverse exchange and combine: out[s][t][c] = bf16_rne( fp32 fused
  * multiply-add chain over j = 0..k-1 in order, from +0, of
  * topk_weights[s][t][j] * expert_out[recv_slot[s][t][j]][c] ), skipping
- * receive rows < 0.  expert_out: device bf16 bits [EP][C][H];
- * topk_weights: device float [EP][N][k], or NULL for weights of 1; out:
- * device bf16 bits [EP][N][H]. */
+ * receive rows < 0.  expert_out: device bf16 bits [EP][C][H], of which only
+ * rows that some pair names are read; it may be NULL when C = 0 (no receive
+ * row exists).  topk_weights: device float [EP][N][k], or NULL for weights
+ * of 1; out: device bf16 bits [EP][N][H]. */
 MOE_API int moe_exchange_combine(const moe_problem *p, const moe_exchange *x,
                                  const uint16_t *expert_out,
                                  const float *topk_weights, uint16_t *out,

@@ -43,8 +43,8 @@
  *             - NKI permute_a2av API reference: description (the receive
  *               layout is the packed cumsum of recv_counts; the table's rows
  *               2-3 are receive counts and displacements) and :return: (C
- *               rows, source-major packed rows followed by deterministic zero
- *               padding).
+ *               rows per rank: each source's rows in rank order, then zero
+ *               rows).
  *             - DeepSpeed v0.19.4 function index, page 15: SplitPlan entries
  *               (one all-to-all of the [ep_size, E_local] count matrix; the
  *               rows a rank receives from it).
@@ -76,8 +76,9 @@
  *   gated dispatch  every copy (t, j) carries the token row multiplied by its
  *             gate, fl32(w[t,j] * x), encoded in the payload format; combine
  *             then sums the expert rows without weights.
- *             - DeepSpeed v0.19.4 function index, page 15: pre-multiplying
- *               token representations by router scores before expert compute.
+ *             - DeepSpeed v0.19.4 function index, page 15: the entry on
+ *               scaling token rows by their router scores ahead of the
+ *               experts.
  *   NVFP4     E2M1 codes with one E4M3 scale per 16 values and one fp32
  *             global encode scale gs given by the caller: per block, the
  *             scale code sf = E4M3(fl32(fl32(amax / 6) * gs)) (saturating),
