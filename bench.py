@@ -43,7 +43,7 @@ PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, published
 DEFAULT_WORKLOAD = "zipf_bf16_n16384"
 # further configurations measured in the same run, each reported with its own
 # roofline under "configs" (the decode shape's µs are under "decode")
-EXTRA_WORKLOADS = ("uniform_bf16_n4096", "fp8_b128_n8192")
+EXTRA_WORKLOADS = ("uniform_bf16_n4096", "fp8_b128_n8192", "gated_map_bf16_n4096")
 METRIC = "dispatch+combine effective HBM GB/s (% of peak) on 1 GPU; µs at decode shape"
 
 
@@ -63,7 +63,10 @@ def step_bytes(w, r_used, r_max, kept=None):
     r_used = receive rows in use over all buffers, r_max = EP * C; the
     dispatch writes every receive row (live rows, then zero rows).  Fixed
     expert capacity: r_used = r_max = E * cap rows, all written; kept = pairs
-    kept, the rows the combine reads."""
+    kept, the rows the combine reads.  Gates at dispatch: the dispatch also
+    reads the gates, the combine does not.  Routing given as a dense map: the
+    plan also converts it (reads the map's N*E bytes and the probabilities
+    of the kept experts, writes the IDs and gates)."""
     t = w.tokens
     nk = t * w.k
     if kept is not None:
@@ -78,6 +81,11 @@ def step_bytes(w, r_used, r_max, kept=None):
         plan = 4 * nk + 4 * nk + 4 * r_max                     # ids, slot, packed_src
         dispatch = 2 * t * w.h + r_used * row_bytes(w.fmt, w.h)  # read x once, write live+pad rows
         combine = 4 * nk + 4 * nk + 2 * w.h * nk + 2 * t * w.h   # slot, w, k rows of y, out
+    if w.gated:
+        dispatch += 4 * nk   # the gates, applied to each copy
+        combine -= 4 * nk    # no weights in the combine
+    if w.routing_input == "map":
+        plan += t * w.e + 4 * nk + 4 * nk + 4 * nk  # map, kept probabilities, ids, gates
     return dict(plan=plan, dispatch=dispatch, combine=combine,
                 total=plan + dispatch + combine)
 
@@ -123,6 +131,10 @@ class Path:
         if "expert_out" in inp:
             y = torch.from_numpy(inp["expert_out"].view(np.int16)).to(dev).view(torch.bfloat16)
         self.gs = torch.tensor([w.input_scale], dtype=torch.float32, device=dev)
+        self.from_map = w.routing_input == "map"
+        if self.from_map:
+            rmap = torch.from_numpy(inp["map"]).to(dev)
+            probs = torch.from_numpy(inp["probs"]).to(dev)
         self.sets = []
         for c in range(copies):
             plan = moe.alloc_plan(self.p, dev)
@@ -130,27 +142,44 @@ class Path:
             payload.view(torch.uint8).zero_()
             if scales is not None:
                 scales.zero_()
-            self.sets.append(dict(
+            s = dict(
                 x=x if c == 0 else x.clone(), ids=ids if c == 0 else ids.clone(),
                 w=wts if c == 0 else wts.clone(),
                 y=(y if c == 0 else y.clone()) if y is not None else payload,
                 plan=plan, payload=payload, scales=scales,
-                out=torch.empty((w.n, w.h), dtype=torch.bfloat16, device=dev)))
+                out=torch.empty((w.n, w.h), dtype=torch.bfloat16, device=dev))
+            if self.from_map:
+                # the IDs and gates are written by the map conversion each step;
+                # its status word and workspace are buffers of their own
+                s.update(map=rmap if c == 0 else rmap.clone(),
+                         probs=probs if c == 0 else probs.clone(),
+                         map_status=torch.empty(1, dtype=torch.int32, device=dev),
+                         map_ws=torch.empty(max(moe.moe_map_workspace_bytes(self.p), 256),
+                                            dtype=torch.uint8, device=dev))
+            self.sets.append(s)
+
+    def _routing(self, s):
+        """A dense routing map is turned into the compact IDs and gates."""
+        if self.from_map:
+            self.moe.moe_routing_map_to_topk(self.p, s["map"], s["probs"], s["ids"], s["w"],
+                                             s["map_status"], s["map_ws"])
 
     def step(self, i, ev=None):
         s = self.sets[i % len(self.sets)]
         m, p = self.moe, self.p
         gs = self.gs if self.w.fmt == "nvfp4" else None
+        gates = s["w"] if self.w.gated else None
         if ev is not None:
             ev[0].record()
+        self._routing(s)
         m.moe_plan_and_dispatch_begin(p, s["ids"], s["plan"])
         if ev is not None:
             ev[1].record()
         m.moe_plan_and_dispatch_end(p, s["ids"], s["plan"], s["x"], s["payload"], s["scales"],
-                                    input_scale=gs)
+                                    topk_weights=gates, input_scale=gs)
         if ev is not None:
             ev[2].record()
-        m.moe_combine(p, s["plan"], s["y"], s["w"], s["out"])
+        m.moe_combine(p, s["plan"], s["y"], None if self.w.gated else s["w"], s["out"])
         if ev is not None:
             ev[3].record()
 
@@ -159,12 +188,15 @@ class Path:
         plan's kernels, then the dispatch kernel)."""
         s = self.sets[i % len(self.sets)]
         m, p = self.moe, self.p
+        self._routing(s)
         m.moe_dispatch_plan(p, s["ids"], s["plan"])
         if self.w.fmt == "nvfp4":
             m.moe_dispatch_scaled(p, s["plan"], s["x"], self.gs, s["payload"], s["scales"])
+        elif self.w.gated:
+            m.moe_dispatch_gated(p, s["plan"], s["x"], s["w"], s["payload"], s["scales"])
         else:
             m.moe_dispatch(p, s["plan"], s["x"], s["payload"], s["scales"])
-        m.moe_combine(p, s["plan"], s["y"], s["w"], s["out"])
+        m.moe_combine(p, s["plan"], s["y"], None if self.w.gated else s["w"], s["out"])
 
     def mode(self):
         return {self.moe.PD_ONE_LAUNCH: "one_launch", self.moe.PD_TILED: "tiled",
@@ -625,6 +657,10 @@ def measure(moe, torch, w, args, context=True):
     if expert_cap:
         config.update(capacity_factor=w.capacity_factor, expert_capacity=expert_cap,
                       pairs_kept=path.kept(), path="fixed expert capacity, later pairs dropped")
+    if w.gated:
+        config["gates"] = "applied at dispatch; combine without weights"
+    if w.routing_input == "map":
+        config["routing_input"] = "dense multihot map + dense probabilities, converted each step"
     rec = dict(value=round(value, 1), unit="GB/s", ms_per_step=round(ms, 5),
                frac_of_peak=round(value / PEAK_HBM_GBPS, 4), dtype=w.fmt, config=config,
                bytes_per_step=b, payload_only=payload_only,

@@ -47,6 +47,8 @@ class Workload:
     ranks: int = 1    # simulated source ranks, N tokens each (exchange workloads: EP)
     capacity_factor: float | None = None  # fixed per-expert capacity from this factor
     input_scale: float = 1.0    # NVFP4 global encode scale handed to the dispatch
+    gated: bool = False         # gates applied at dispatch, unweighted combine
+    routing_input: str = "topk"  # "topk" | "map": dense multihot map + probabilities
 
     @property
     def l(self) -> int:
@@ -72,6 +74,10 @@ class Workload:
         tail = f", C={self.capacity} rows per receive buffer" if self.exchange else ""
         if self.capacity_factor is not None:
             tail += f", expert capacity factor {self.capacity_factor}"
+        if self.gated:
+            tail += ", gates applied at dispatch"
+        if self.routing_input == "map":
+            tail += ", routing given as a dense multihot map with dense probabilities"
         return (f"{head}N={self.n} H={self.h} E={self.e} k={self.k} EP={self.ep} "
                 f"A={self.a} {self.fmt} {self.routing} routing, "
                 f"{self.experts} experts{tail}")
@@ -117,6 +123,12 @@ WORKLOADS = {
         Workload("exchange_fp8_ep4_n2048", n=2048, h=7168, e=256, k=8, ep=4,
                  a=1, fmt="fp8", routing="softmax", experts="random",
                  recv_capacity=20480, ranks=4),
+        # the uniform prefill share with the routing handed over as a dense
+        # multihot map and dense probabilities (converted to top-k on the
+        # device), gates applied at dispatch, unweighted combine
+        Workload("gated_map_bf16_n4096", n=4096, h=4096, e=64, k=6, ep=8,
+                 a=128, fmt="bf16", routing="softmax", experts="identity",
+                 gated=True, routing_input="map"),
         # decode-sized exchange across 8 simulated ranks
         Workload("exchange_mxfp4_ep8_n128", n=128, h=7168, e=256, k=8, ep=8,
                  a=1, fmt="mxfp4", routing="softmax", experts="random",
@@ -160,7 +172,11 @@ def make_inputs(w: Workload, seed: int = 0, expert_rows: int | None = None):
 
     Returns a dict with ``ids`` (int32 [T,k]), ``weights`` (float32 [T,k]),
     ``hidden`` (uint16 bf16 bits [T,H]), T = ranks * N, and, for random experts,
-    ``expert_out`` (uint16 bf16 bits [expert_rows, H]).
+    ``expert_out`` (uint16 bf16 bits [expert_rows, H]).  Workloads whose
+    routing is handed over as a dense map also get ``map`` (uint8 [T,E], 1
+    where a token routes to an expert) and ``probs`` (float32 [T,E], the
+    token's gate weight for those experts, 0 elsewhere): the same routing in
+    the multihot form, nothing drawn.
     """
     rng = np.random.Generator(np.random.PCG64(seed))
     ids, weights = router(rng, w)
@@ -171,6 +187,13 @@ def make_inputs(w: Workload, seed: int = 0, expert_rows: int | None = None):
             raise ValueError("random experts need expert_rows")
         out["expert_out"] = to_bf16_bits(
             rng.standard_normal((expert_rows, w.h), dtype=np.float32))
+    if w.routing_input == "map":
+        m = np.zeros((w.tokens, w.e), np.uint8)
+        probs = np.zeros((w.tokens, w.e), np.float32)
+        rows = np.arange(w.tokens)[:, None]
+        m[rows, ids] = 1
+        probs[rows, ids] = weights
+        out["map"], out["probs"] = m, probs
     return out
 
 

@@ -80,3 +80,16 @@ def test_paths_name_their_dispatch_kernel():
     """The roofline names the kernel of the dispatch call on either path."""
     for cls in (bench.Path, bench.ExchangePath):
         assert callable(getattr(cls, "dispatch_kernel", None)), cls.__name__
+
+
+def test_gated_map_step_bytes():
+    """Gates at dispatch, routing given as a dense map (N=4096, E=64, k=6,
+    A=128): the plan also reads the map (N*E bytes) and the kept
+    probabilities and writes IDs and gates; the dispatch reads the gates;
+    the combine reads no weights."""
+    w = WORKLOADS["gated_map_bf16_n4096"]
+    b = bench.step_bytes(w, 28928, 32704)
+    nk = 4096 * 6
+    assert b["plan"] == 4 * nk + 4 * nk + 4 * 32704 + 4096 * 64 + 3 * 4 * nk
+    assert b["dispatch"] == 2 * 4096 * 4096 + 28928 * 8192 + 4 * nk
+    assert b["combine"] == 4 * nk + 2 * 4096 * nk + 2 * 4096 * 4096

@@ -221,3 +221,47 @@ def test_routing_map_end_to_end(moe):
     pay, _ = oracle.dispatch("bf16", x, pl)
     ref = oracle.combine(pl["slot"], rw, pay)
     assert assert_combine_close(u16(out), ref) == 0
+
+
+@pytest.mark.parametrize("three_calls", [False, True], ids=["bench_step", "three_calls"])
+def test_gated_map_workload_bench_step(moe, three_calls):
+    """The benchmark's own step for gated_map_bf16_n4096 (N = H = 4096, E = 64,
+    k = 6, A = 128; tiled plan-and-dispatch): the dense map and probabilities
+    converted on the device, then moe_plan_and_dispatch_begin / _end with the
+    gates (or, as three calls, the plan and the gated dispatch), then the
+    unweighted combine, on both buffer sets it rotates over; every IDs,
+    gates, plan array, packed row and output against the oracle's same
+    steps."""
+    import bench
+    w = WORKLOADS["gated_map_bf16_n4096"]
+    say(f"[gated map workload] {w.describe()}; three_calls={three_calls}")
+    inp = make_inputs(w, seed=0)
+    path = bench.Path(moe, torch, w, inp, copies=2)
+    assert path.mode() == "tiled"
+    for s in path.sets:
+        s["payload"].view(torch.uint8).fill_(SENTINEL)
+        s["ids"].fill_(-9)
+        s["w"].fill_(9.0)
+        s["map_status"].fill_(77)
+    for i in range(2):
+        (path.step_three_calls if three_calls else path.step)(i)
+    torch.cuda.synchronize()
+    rids, rw, rst = oracle.routing_map_to_topk(inp["map"], inp["probs"], w.k)
+    assert rst == 0
+    pl = oracle.plan(rids, w.e, w.ep, w.a, w.capacity, w.h)
+    ru = pl["r_used"]
+    ref_pay, _ = oracle.dispatch_gated("bf16", inp["hidden"], pl, rw, zero_tail=False)
+    ref_out = oracle.combine(pl["slot"], None, ref_pay)
+    for s in path.sets:
+        assert np.array_equal(s["ids"].cpu().numpy(), rids)
+        assert np.array_equal(s["w"].cpu().numpy(), rw)
+        assert int(s["map_status"].item()) == 0
+        plan = s["plan"]
+        assert plan.read_status() == pl["status"] == 0
+        for key in ("expert_counts", "expert_offsets", "dest_counts", "slot", "packed_src"):
+            assert np.array_equal(getattr(plan, key).cpu().numpy(), pl[key]), key
+        assert np.array_equal(plan.rank_table.cpu().numpy().view(np.uint32), pl["rank_table"])
+        got = u16(s["payload"])
+        assert np.array_equal(got[:ru], ref_pay[:ru])
+        assert np.all(got[ru:].view(np.uint8) == SENTINEL)
+        assert assert_combine_close(u16(s["out"]), ref_out) == 0
