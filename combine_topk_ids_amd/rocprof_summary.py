@@ -1,7 +1,12 @@
 """Summaries of rocprofv3 output (rocpd SQLite databases) for libmoe's kernels.
 
-    python -m combine_topk_ids_amd.rocprof_summary trace DB [--title T]
-        per-kernel launch count and average / min / max duration (markdown)
+    python -m combine_topk_ids_amd.rocprof_summary trace DB [--title T] [--phases]
+        per-kernel launch count and average / min / max duration (markdown);
+        with --phases, per phase of the run: launches separated from the
+        previous libmoe launch by more than --gap-ms (default 300) start a
+        new phase, so the workloads bench.py measures one after another
+        (with seconds of input generation between them) get tables of their
+        own even where two of them launch the same kernel on the same grid
 
     python -m combine_topk_ids_amd.rocprof_summary counters \\
         --fetch FETCH_DB --write WRITE_DB --workload NAME [--json OUT]
@@ -56,6 +61,36 @@ def trace_table(db: str, only_moe: bool = True) -> list[dict]:
     return out
 
 
+def trace_phases(db: str, gap_ms: float = 300.0) -> list[list[dict]]:
+    """trace_table split into phases of the run (see the module docstring)."""
+    con = sqlite3.connect(db)
+    rows = con.execute("select name, start, end, duration, grid_x, workgroup_x from kernels "
+                       "order by start").fetchall()
+    phases, cur, last_end = [], [], None
+    for n, st, en, d, gx, wx in rows:
+        if "moe::" not in n:
+            continue
+        if last_end is not None and st - last_end > gap_ms * 1e6:
+            phases.append(cur)
+            cur = []
+        cur.append((n, d, gx, wx))
+        last_end = en if last_end is None else max(last_end, en)
+    if cur:
+        phases.append(cur)
+    out = []
+    for ph in phases:
+        groups = collections.OrderedDict()
+        for n, d, gx, wx in ph:
+            groups.setdefault((n, gx, wx), []).append(d)
+        tab = []
+        for (n, gx, wx), ds in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+            tab.append(dict(kernel=short_name(n), calls=len(ds), avg_us=sum(ds) / len(ds) / 1e3,
+                            min_us=min(ds) / 1e3, max_us=max(ds) / 1e3,
+                            grid=f"{gx // max(wx, 1)}x{wx}"))
+        out.append(tab)
+    return out
+
+
 def counter_table(db: str, counter: str) -> dict:
     con = sqlite3.connect(db)
     rows = con.execute(
@@ -104,6 +139,8 @@ def main(argv=None):
     t = sub.add_parser("trace")
     t.add_argument("db")
     t.add_argument("--title", default="")
+    t.add_argument("--phases", action="store_true")
+    t.add_argument("--gap-ms", type=float, default=300.0)
     c = sub.add_parser("counters")
     c.add_argument("--fetch", required=True)
     c.add_argument("--write", required=True)
@@ -111,14 +148,18 @@ def main(argv=None):
     c.add_argument("--json")
     a = ap.parse_args(argv)
     if a.cmd == "trace":
-        rows = trace_table(a.db)
+        tables = trace_phases(a.db, a.gap_ms) if a.phases else [trace_table(a.db)]
         if a.title:
             print(f"### {a.title}\n")
-        print("| kernel | grid (blocks x threads) | launches | avg us | min us | max us |")
-        print("|---|---|---|---|---|---|")
-        for r in rows:
-            print(f"| {r['kernel']} | {r['grid']} | {r['calls']} | {r['avg_us']:.2f} | "
-                  f"{r['min_us']:.2f} | {r['max_us']:.2f} |")
+        for i, rows in enumerate(tables):
+            if a.phases:
+                print(f"Phase {i + 1}\n")
+            print("| kernel | grid (blocks x threads) | launches | avg us | min us | max us |")
+            print("|---|---|---|---|---|---|")
+            for r in rows:
+                print(f"| {r['kernel']} | {r['grid']} | {r['calls']} | {r['avg_us']:.2f} | "
+                      f"{r['min_us']:.2f} | {r['max_us']:.2f} |")
+            print()
     else:
         rec = counters(a.fetch, a.write, a.workload)
         text = json.dumps(rec, indent=1)

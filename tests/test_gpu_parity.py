@@ -402,3 +402,44 @@ def test_graph_capture_replays_match_eager(moe):
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), it
     pl = oracle.plan(inp["ids"], w.e, w.ep, w.a, w.capacity, w.h)
     assert np.array_equal(plan.slot.cpu().numpy(), pl["slot"])
+
+
+def test_largest_buffer_the_table_allows(moe):
+    """N = 131071, H = 4096, E = 128, k = 8, A = 1: R_max * H = 4,294,934,528,
+    the largest element count below 2^32 that the uint32 table allows (one
+    more token is refused), a payload of 8.6 GB, so row byte offsets run far
+    past 4 GiB.  The whole plan against the oracle; the packed rows of 4096
+    sampled rows (the last ones included) against the oracle's encoding of
+    their tokens; every combine output through the identity round trip
+    (weights summing to 1, so combine(dispatch(x)) is x bit for bit)."""
+    n, h, e, k, ep = 131071, 4096, 128, 8, 16
+    assert moe.moe_check_problem(moe.problem(n + 1, h, k, e, ep)) == moe.MOE_EOVERFLOW
+    p = moe.problem(n, h, k, e, ep)
+    r_max = moe.moe_max_rows(p)
+    assert r_max * h == 4294934528 < 1 << 32
+    say(f"[edge] largest buffer: N={n} H={h} E={e} k={k}, R_max={r_max}, "
+        f"payload {r_max * h * 2 / 1e9:.1f} GB")
+    rng = np.random.default_rng(2026)
+    ids, w = random_routing(rng, n, e, k)
+    x = random_bf16(rng, (n, h))
+    plan = moe.alloc_plan(p)
+    payload, _ = moe.alloc_payload(p)
+    x_d = to_dev_bf16(x)
+    ids_d = torch.from_numpy(ids).cuda()
+    out = torch.empty_like(x_d)
+    moe.moe_plan_and_dispatch_begin(p, ids_d, plan)
+    moe.moe_plan_and_dispatch_end(p, ids_d, plan, x_d, payload, None)
+    moe.moe_combine(p, plan, payload, torch.from_numpy(w).cuda(), out)
+    torch.cuda.synchronize()
+    pl = oracle.plan(ids, e, ep, 1, n * min(k, e // ep), h)
+    assert plan.read_status() == pl["status"] == 0
+    for key in ("expert_counts", "expert_offsets", "dest_counts", "slot", "packed_src"):
+        assert np.array_equal(getattr(plan, key).cpu().numpy(), pl[key]), key
+    rows = np.unique(np.concatenate([np.arange(8), r_max - 1 - np.arange(64),
+                                     rng.choice(r_max, 4024, replace=False)]))
+    got = u16(payload[torch.from_numpy(rows).cuda()])
+    enc, _ = oracle.encode_rows("bf16", x[pl["packed_src"][rows]])
+    assert np.array_equal(got, enc)
+    negz = x_d.view(torch.int16) == -32768  # -0 comes back as +0
+    same = (out.view(torch.int16) == x_d.view(torch.int16)) | (negz & (out.view(torch.int16) == 0))
+    assert bool(same.all())
