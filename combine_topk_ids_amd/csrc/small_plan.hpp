@@ -50,6 +50,7 @@ constexpr int kSmallWaves = kSmallThreads / kWave;
 constexpr int kSmallLoads = kSmallPairs / kSmallThreads;  // IDs per thread
 constexpr int kSmallTargets = kSmallThreads;              // own pairs, one per thread
 constexpr int kSmallIds = kSmallPairs + kSmallTargets;    // LDS IDs: tiled mode reads up to this many
+constexpr int kRankBatch = 16;  // own IDs own_slot reads per batch, unconditionally
 constexpr int kTileLoads = kSmallIds / kSmallThreads;     // IDs per thread in tiled mode
 constexpr int kTileHistLoads = kTileHist / kSmallThreads;
 static_assert(kMaxExperts <= 4 * kSmallThreads, "the expert scan gives each thread four experts");
@@ -68,7 +69,8 @@ struct SmallPlanArgs {
 
 // LDS arrays of a small plan (ints).
 struct SmallPlanLds {
-  int *ids;     // [kSmallIds] valid ID or -1, pairs lo .. (lo = 0 in small mode)
+  int *ids;     // [kSmallIds] valid ID or -1, pairs lo .. (lo = 0 in small mode),
+                // then kRankBatch entries that own_slot may read and ignore
   int *cnt;     // [E]   pairs per expert (while counting, small mode: those from p0 on)
   int *before;  // [E]   pairs per expert before p0
   int *off;     // [E+1] padded exclusive cumsum, off[E] = R_used
@@ -76,13 +78,13 @@ struct SmallPlanLds {
 };
 
 __host__ __device__ constexpr size_t small_plan_lds_bytes(int e) {
-  return (static_cast<size_t>(kSmallIds) + 4 * static_cast<size_t>(e) + 2) * sizeof(int);
+  return (static_cast<size_t>(kSmallIds + kRankBatch) + 4 * static_cast<size_t>(e) + 2) * sizeof(int);
 }
 
 __device__ __forceinline__ SmallPlanLds small_plan_lds(int *smem, int e) {
   SmallPlanLds s;
   s.ids = smem;
-  s.cnt = s.ids + kSmallIds;
+  s.cnt = s.ids + kSmallIds + kRankBatch;
   s.before = s.cnt + e;
   s.off = s.before + e;
   s.cpre = s.off + e + 1;
@@ -238,13 +240,17 @@ __device__ __forceinline__ int own_slot(const SmallPlanLds &s, int lo, int p0, i
   const int *own = s.ids + (p0 - lo);
   const int j = p - p0;
   int r = s.before[e];
-  // 16 LDS reads in flight at a time
-  for (int q0 = 0; q0 < j; q0 += 16) {
-    int w[16];
+  // kRankBatch LDS reads in flight at a time: every read of a batch is
+  // issued, then one wait.  A read under its own condition would be compiled
+  // into a read and a wait each.  The last batch may read up to
+  // kRankBatch - 1 entries past p - lo (inside the ids array and its slack);
+  // those are not counted.
+  for (int q0 = 0; q0 < j; q0 += kRankBatch) {
+    int w[kRankBatch];
 #pragma unroll
-    for (int q = 0; q < 16; ++q) w[q] = q0 + q < j ? own[q0 + q] : -1;
+    for (int q = 0; q < kRankBatch; ++q) w[q] = own[q0 + q];
 #pragma unroll
-    for (int q = 0; q < 16; ++q) r += w[q] == e ? 1 : 0;
+    for (int q = 0; q < kRankBatch; ++q) r += q0 + q < j && w[q] == e ? 1 : 0;
   }
   const int64_t row = static_cast<int64_t>(s.off[e]) + r;
   return r < 0 || r >= s.cnt[e] || row < 0 || row >= r_max ? kBadSlot : static_cast<int>(row);
@@ -294,9 +300,13 @@ __device__ uint32_t small_plan(const SmallPlanArgs &g, const SmallPlanLds &s, co
     for (int t = tid; t < g.n; t += kSmallThreads) {
       const int *row = s.ids + t * g.k;
       if (g.k <= 8) {
+        // all 8 read unconditionally (t * k + 7 < kSmallPairs + 7, inside
+        // the ids array), then masked
         int e[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) e[j] = j < g.k ? row[j] : -1;
+        for (int j = 0; j < 8; ++j) e[j] = row[j];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) e[j] = j < g.k ? e[j] : -1;
 #pragma unroll
         for (int j = 1; j < 8; ++j)
 #pragma unroll
