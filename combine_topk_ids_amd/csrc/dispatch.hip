@@ -101,9 +101,10 @@ struct DispatchArgs {
   // segment d keeps its first min(seg_used[d], seg_rows) rows.  One segment
   // (the whole buffer, used = R_used) for a single packed buffer; one per
   // receive buffer for the exchange.
-  const int32_t *seg_used;
+  const int32_t *seg_used;  // null: one segment, used_rows rows used
   int nseg;
   int64_t seg_rows;
+  int used_rows;
 };
 
 template <bool NT, typename V>
@@ -315,11 +316,13 @@ __device__ void slab_mx(const DispatchArgs &g, int slab, int my_slot, const RawS
     if (kLE == 8) am = max(am, dpp<kQuadSwap2>(am));
     const int X = mx_exponent(am);
     const float mul = __uint_as_float(static_cast<uint32_t>(127 - X) << 23);  // 2^-X
+    const bool hw = ballot(nan_bits(am)) == 0;  // hardware codes unless a NaN
 #pragma unroll
     for (int qd = 0; qd < kLE / 8; ++qd) {
-      uint32_t v = 0;
+      float q[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v |= e2m1_rne_sat(f[c][8 * qd + i] * mul) << (4 * i);
+      for (int i = 0; i < 8; ++i) q[i] = f[c][8 * qd + i] * mul;
+      const uint32_t v = e2m1_lane8(q, hw);
       w[c][qd] = am == 0 ? 0u : v;
     }
     sbyte[c] = am == 0 ? 0 : static_cast<uint8_t>(X + 127);
@@ -361,10 +364,14 @@ __device__ void slab_nvfp4(const DispatchArgs &g, int slab, int my_slot, const R
   const float ts = (__uint_as_float(am) / 6.0f) * gs;
   const uint32_t sf = e4m3_pair_hw(fminf(fmaxf(ts, -448.0f), 448.0f), 0.0f) & 0xFFu;
   const float sfv = e4m3_magnitude(sf & 0x7Fu);
+  // hardware codes unless a NaN value or a global scale that makes one
+  const bool hw = ballot(nan_bits(am)) == 0 && fabsf(gs) <= 0x1.fffffep127f;
   uint32_t w = 0;
   if (sfv != 0.0f) {
+    float q[kLE];
 #pragma unroll
-    for (int i = 0; i < kLE; ++i) w |= e2m1_rne_sat((f[i] * gs) / sfv) << (4 * i);
+    for (int i = 0; i < kLE; ++i) q[i] = (f[i] * gs) / sfv;
+    w = e2m1_lane8(q, hw);
   }
   for (int j = 0; j < g.k; ++j) {
     const int d = __builtin_amdgcn_readlane(my_slot, j);
@@ -478,6 +485,7 @@ __device__ void slab_mx_gated(const DispatchArgs &g, int slab, int my_slot, cons
   am = max(am, dpp<kQuadSwap1>(am));
   if (kLE == 8) am = max(am, dpp<kQuadSwap2>(am));
   const float amax = __uint_as_float(am);
+  const bool finite_x = ballot(nan_bits(am)) == 0;
   for (int j = 0; j < g.k; ++j) {
     const int d = __builtin_amdgcn_readlane(my_slot, j);
     if (d < 0) continue;
@@ -486,12 +494,15 @@ __device__ void slab_mx_gated(const DispatchArgs &g, int slab, int my_slot, cons
     const uint32_t ab = __float_as_uint(amj);
     const int X = mx_exponent(ab);
     const float mul = __uint_as_float(static_cast<uint32_t>(127 - X) << 23);  // 2^-X
+    // hardware codes unless a NaN value, or a gate that makes one
+    const bool hw = finite_x && fabsf(wj) <= 0x1.fffffep127f;
     uint32_t w8[kLE / 8];
 #pragma unroll
     for (int qd = 0; qd < kLE / 8; ++qd) {
-      uint32_t v = 0;
+      float q[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v |= e2m1_rne_sat((wj * f[8 * qd + i]) * mul) << (4 * i);
+      for (int i = 0; i < 8; ++i) q[i] = (wj * f[8 * qd + i]) * mul;
+      const uint32_t v = e2m1_lane8(q, hw);
       w8[qd] = ab == 0 ? 0u : v;
     }
     if (elem < g.h) {
@@ -544,7 +555,8 @@ template <bool NT>
 __device__ void zero_tails(const DispatchArgs &g, int blk, int wave) {
   const int64_t stride = static_cast<int64_t>(g.tail_blocks) * kWaves;
   for (int d = 0; d < g.nseg; ++d) {
-    const int64_t used = max(min(static_cast<int64_t>(g.seg_used[d]), g.seg_rows), int64_t{0});
+    const int64_t u = g.seg_used ? g.seg_used[d] : g.used_rows;
+    const int64_t used = max(min(u, g.seg_rows), int64_t{0});
     const int64_t base = d * g.seg_rows;
     for (int64_t r = used + static_cast<int64_t>(blk) * kWaves + wave; r < g.seg_rows; r += stride)
       zero_row<NT>(g, base + r);
@@ -640,6 +652,36 @@ struct PlanDispatchArgs {
 static_assert(kThreads == kSmallThreads, "one small plan per dispatch workgroup");
 static_assert(MOE_TAIL_FIRST == 0, "the one-launch kernel places the token workgroups first");
 
+// Workgroup 0's share of a one-launch plan: counts, offsets, the (4, EP)
+// table and the status, from the plan in LDS.
+template <bool TILED>
+__device__ void write_plan_arrays(const PlanDispatchArgs &g, const SmallPlanLds &s, uint32_t fl) {
+  const int E = g.sp.e, tid = threadIdx.x;
+  for (int e = tid; e < E; e += kThreads) {
+    g.counts[e] = s.cnt[e];
+    g.offsets[e] = s.off[e];
+  }
+  if (tid == 0) {
+    g.offsets[E] = s.off[E];
+    // tiled: the counting kernel cleared the status word, and other
+    // workgroups may OR BAD_PLAN into it; one launch: written here alone
+    if constexpr (TILED)
+      atomicOr(g.status, fl | (s.off[E] < 0 || s.off[E] > g.r_max ? MOE_STATUS_BAD_PLAN : 0u));
+    else
+      *g.status = fl;
+  }
+  const int L = g.sp.l;
+  for (int rk = tid; rk < g.sp.ep; rk += kThreads) {
+    const int lo = rk * L, hi = lo + L;
+    const int S = s.cpre[hi] - s.cpre[lo];
+    g.dest_counts[rk] = S;
+    g.table[rk] = static_cast<uint32_t>(S) * g.h;
+    g.table[g.sp.ep + rk] = static_cast<uint32_t>(s.cpre[lo]) * g.h;
+    g.table[2 * g.sp.ep + rk] = static_cast<uint32_t>(s.off[hi] - s.off[lo]) * g.h;
+    g.table[3 * g.sp.ep + rk] = static_cast<uint32_t>(s.off[lo]) * g.h;
+  }
+}
+
 template <int FMT, bool NT, bool GATED, bool TILED>
 __global__ __launch_bounds__(kThreads) void plan_dispatch_kernel(PlanDispatchArgs g) {
   extern __shared__ int smem[];
@@ -688,31 +730,7 @@ __global__ __launch_bounds__(kThreads) void plan_dispatch_kernel(PlanDispatchArg
   else
     fl = small_plan(g.sp, s, v, p0, b == 0);
 
-  if (b == 0) {
-    for (int e = tid; e < E; e += kThreads) {
-      g.counts[e] = s.cnt[e];
-      g.offsets[e] = s.off[e];
-    }
-    if (tid == 0) {
-      g.offsets[E] = s.off[E];
-      // tiled: the counting kernel cleared the status word, and other
-      // workgroups may OR BAD_PLAN into it; one launch: written here alone
-      if constexpr (TILED)
-        atomicOr(g.status, fl | (s.off[E] < 0 || s.off[E] > g.r_max ? MOE_STATUS_BAD_PLAN : 0u));
-      else
-        *g.status = fl;
-    }
-    const int L = g.sp.l;
-    for (int rk = tid; rk < g.sp.ep; rk += kThreads) {
-      const int lo = rk * L, hi = lo + L;
-      const int S = s.cpre[hi] - s.cpre[lo];
-      g.dest_counts[rk] = S;
-      g.table[rk] = static_cast<uint32_t>(S) * g.h;
-      g.table[g.sp.ep + rk] = static_cast<uint32_t>(s.cpre[lo]) * g.h;
-      g.table[2 * g.sp.ep + rk] = static_cast<uint32_t>(s.off[hi] - s.off[lo]) * g.h;
-      g.table[3 * g.sp.ep + rk] = static_cast<uint32_t>(s.off[lo]) * g.h;
-    }
-  }
+  if (b == 0) write_plan_arrays<TILED>(g, s, fl);
   // the wave's own token's slots, found by the wave itself; they and the
   // token's packed_src rows are written by the wave of its slab 0.  A pair
   // the histograms do not account for (tiled mode, a workspace that does
@@ -748,6 +766,169 @@ __global__ __launch_bounds__(kThreads) void plan_dispatch_kernel(PlanDispatchArg
     dp.offsets = s.off;
     dp.seg_used = s.off + E;
     dispatch_body<FMT, NT, GATED>(dp, b, wave);
+  }
+}
+
+// ---- one launch without padding: slots by counting smaller keys --------------
+// With A = 1 the packed row of a valid pair is the number of valid pairs
+// ahead of it in (expert, flat pair index) order: the stable counting sort
+// of the plan, whose offsets are then the unpadded cumsum.  As 21-bit keys
+// (expert << 11 | pair index; masked and invalid pairs get a key above
+// every valid one) the row of pair p is the count of keys below p's key,
+// which also ranks the equal IDs of one token.  A token workgroup counts
+// these for its own pairs (those of its at most kWaves tokens) without LDS
+// atomics (about 64 cycles each on this chip) and with one barrier: each
+// wave holds a quarter of the keys (ID u * 256 + tid in register u), counts
+// for every own pair the keys below it in that quarter with one ballot per
+// register, and stores the count; after the barrier a pair's row is the sum
+// of the four counts.  Workgroup 0 builds the whole plan in LDS all the
+// same, for the counts, offsets, table, status and the packed_src tail,
+// and stores no payload; the token workgroups are 1 .. token_blocks, then
+// the tail workgroups.
+constexpr uint32_t kNoKey = 0xFFFFFFFFu;
+constexpr int kOwnMax = kWaves * kMaxTopK;  // own pairs of a workgroup, at most
+static_assert(kSmallPairs <= 2048 && kMaxExperts <= 1024, "keys: 11 index bits, 10 expert bits");
+static_assert(kOwnMax <= 4 * kWave, "own keys: four registers a lane");
+
+// Key registers per thread (IDs u * kThreads + tid) for a one-launch problem.
+__host__ __device__ constexpr int rank_regs(int64_t npairs) {
+  return npairs <= kThreads ? 1 : npairs <= 4 * kThreads ? 4 : kSmallPairs / kThreads;
+}
+
+template <int FMT, bool NT, bool GATED, int NR>
+__global__ __launch_bounds__(kThreads) void plan_dispatch_rank_kernel(PlanDispatchArgs g) {
+  extern __shared__ int smem[];
+  __shared__ int s_cnt[kWaves][kOwnMax];  // per wave: keys below each own pair
+  __shared__ int s_used[kWaves];
+  const int E = g.sp.e, k = g.sp.k;
+  const int np = g.sp.n * k;
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  if (b == 0) {
+    const SmallPlanLds s = small_plan_lds(smem, E);
+    int v[kSmallLoads];
+    small_plan_load(g.sp, v);
+    const uint32_t fl = small_plan(g.sp, s, v, 0, true);
+    write_plan_arrays<false>(g, s, fl);
+    for (int row = max(s.off[E], 0) + tid; row < g.r_max; row += kThreads) g.packed_src[row] = -1;
+    return;
+  }
+  const DispatchArgs &d = g.d;
+  const int bb = b - 1;
+  const bool tok = bb < d.token_blocks;
+  const int blk = tok && FMT != MOE_FMT_BF16 ? xcd_local_block(bb, d.token_blocks) : bb;
+  // (token, slab) of this wave and the workgroup's own pairs (every pair of
+  // its tokens).  With at least kWaves slabs a token, a token has
+  // ceil(slabs / kWaves) workgroups of its own (token_blocks = N times
+  // that), so the own pairs are the token's k; otherwise consecutive waves
+  // take consecutive (token, slab) items and a workgroup spans up to
+  // kWaves tokens.
+  int t, slab, p0 = 0, p1 = 0;
+  if (d.slabs >= kWaves) {
+    const int wpt = (d.slabs + kWaves - 1) / kWaves;
+    t = tok ? blk / wpt : 0;
+    slab = (blk - t * wpt) * kWaves + wave;
+    if (tok && t < g.sp.n) {
+      p0 = t * k;
+      p1 = p0 + k;
+    }
+  } else {
+    const int q = blk * kWaves + wave;  // the grid size keeps q within int
+    t = tok ? q / d.slabs : 0;
+    slab = q - t * d.slabs;
+    if (tok) {
+      const int t0 = (blk * kWaves) / d.slabs;
+      const int t1 = min(g.sp.n - 1, (blk * kWaves + kWaves - 1) / d.slabs);
+      if (t0 < g.sp.n) {
+        p0 = t0 * k;
+        p1 = (t1 + 1) * k;
+      }
+    }
+  }
+  const int own_n = p1 - p0;  // <= kOwnMax
+  const bool live = tok && t < g.sp.n && slab < d.slabs;
+
+  // this thread's IDs, the workgroup's own IDs (pair p0 + r * 64 + lane in
+  // register r) and the slab: bounds-checked loads, all in flight together
+  const auto ids = buffer_rsrc(g.sp.ids, static_cast<uint32_t>(np) * 4u);
+  int x[NR];
+#pragma unroll
+  for (int u = 0; u < NR; ++u)
+    x[u] = __builtin_amdgcn_raw_buffer_load_b32(ids, (u * kThreads + tid) * 4, 0, kLoadDefault);
+  const auto own_ids = buffer_rsrc(g.sp.ids + p0, 4u * static_cast<uint32_t>(own_n));
+  int o[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) o[r] = __builtin_amdgcn_raw_buffer_load_b32(own_ids, (r * kWave + lane) * 4, 0, kLoadDefault);
+  const auto tok_ids = buffer_rsrc(g.sp.ids + (live ? t * k : 0), live ? 4u * static_cast<uint32_t>(k) : 0u);
+  const int own = __builtin_amdgcn_raw_buffer_load_b32(tok_ids, lane * 4, 0, kLoadDefault);  // pair (t, lane)
+  const RawSlab raw = load_slab_buf<FMT, GATED>(d, t, slab, live);
+
+  uint32_t key[NR];
+  int used = 0;  // valid pairs among this wave's quarter
+#pragma unroll
+  for (int u = 0; u < NR; ++u) {
+    const int i = u * kThreads + tid;
+    const bool ok = i < np && x[u] >= 0 && x[u] < E;
+    key[u] = ok ? (static_cast<uint32_t>(x[u]) << 11) | static_cast<uint32_t>(i) : kNoKey;
+    used += __popcll(ballot(ok));
+  }
+  uint32_t okey[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int j = r * kWave + lane, p = p0 + j;
+    okey[r] = j < own_n && o[r] >= 0 && o[r] < E ? (static_cast<uint32_t>(o[r]) << 11) | static_cast<uint32_t>(p) : kNoKey;
+  }
+  // keys of this quarter below each own key: four own keys an iteration,
+  // four independent chains of ballots (counts for lanes past own_n are
+  // computed and not used)
+  int cnt[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int jn = min(own_n - r * kWave, kWave);
+    for (int jj = 0; jj < jn; jj += 4) {
+      uint32_t kq[4];
+      int c[4] = {0, 0, 0, 0};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kq[i] = __builtin_amdgcn_readlane(okey[r], min(jj + i, kWave - 1));
+#pragma unroll
+      for (int u = 0; u < NR; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) c[i] += __popcll(ballot(key[u] < kq[i]));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) cnt[r] = lane == jj + i ? c[i] : cnt[r];
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    if (r * kWave + lane < own_n) s_cnt[wave][r * kWave + lane] = cnt[r];
+  if (lane == 0) s_used[wave] = used;
+  __syncthreads();
+
+  // the own token's pairs (lane j < k): the row is the sum of the counts
+  int my_slot = -1;
+  if (live && lane < k && own >= 0 && own < E) {
+    const int j = t * k + lane - p0;  // < own_n
+    int row = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) row += s_cnt[w][j];
+    if (row >= 0 && row < g.r_max) my_slot = row;
+  }
+  if (live && slab == 0 && lane < k) {
+    g.slot[t * k + lane] = my_slot;
+    if (my_slot >= 0) g.packed_src[my_slot] = t;
+  }
+  if (live) {
+    emit_slab<FMT, NT, GATED>(d, slab, my_slot, raw);
+  } else if (!tok && bb < g.dispatch_blocks) {
+    // zero tail rows after R_used (no pad rows without padding)
+    int u_all = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) u_all += s_used[w];
+    DispatchArgs dp = d;
+    dp.seg_used = nullptr;
+    dp.used_rows = u_all;
+    dispatch_body<FMT, NT, GATED>(dp, bb, wave);
   }
 }
 
@@ -838,6 +1019,40 @@ void launch_plan_dispatch_fmt(const PlanDispatchArgs &g, int grid, size_t lds, h
     plan_dispatch_kernel<FMT, kNT, false, TILED><<<grid, kThreads, lds, stream>>>(g);
 }
 
+template <int FMT, int NR>
+void launch_plan_dispatch_rank_nr(const PlanDispatchArgs &g, int grid, size_t lds, hipStream_t stream) {
+  constexpr bool kNT = MOE_DISPATCH_NT_STORE != 0;
+  if (FMT != MOE_FMT_NVFP4_B16 && g.d.w)
+    plan_dispatch_rank_kernel<FMT, kNT, FMT != MOE_FMT_NVFP4_B16, NR><<<grid, kThreads, lds, stream>>>(g);
+  else
+    plan_dispatch_rank_kernel<FMT, kNT, false, NR><<<grid, kThreads, lds, stream>>>(g);
+}
+
+template <int FMT>
+void launch_plan_dispatch_rank_fmt(const PlanDispatchArgs &g, int nr, int grid, size_t lds, hipStream_t stream) {
+  if (nr == 1) launch_plan_dispatch_rank_nr<FMT, 1>(g, grid, lds, stream);
+  else if (nr == 4) launch_plan_dispatch_rank_nr<FMT, 4>(g, grid, lds, stream);
+  else launch_plan_dispatch_rank_nr<FMT, kSmallPairs / kThreads>(g, grid, lds, stream);
+}
+
+void launch_plan_dispatch_rank(const PlanDispatchArgs &g, int fmt, int nr, int grid, size_t lds, hipStream_t stream) {
+  if (fmt == MOE_FMT_BF16) launch_plan_dispatch_rank_fmt<MOE_FMT_BF16>(g, nr, grid, lds, stream);
+  else if (fmt == MOE_FMT_FP8_E4M3_B128) launch_plan_dispatch_rank_fmt<MOE_FMT_FP8_E4M3_B128>(g, nr, grid, lds, stream);
+  else if (fmt == MOE_FMT_NVFP4_B16) launch_plan_dispatch_rank_fmt<MOE_FMT_NVFP4_B16>(g, nr, grid, lds, stream);
+  else launch_plan_dispatch_rank_fmt<MOE_FMT_MXFP4_B32>(g, nr, grid, lds, stream);
+}
+
+// Ballots a wave of the counting one-launch kernel makes: (own pairs of a
+// workgroup, at most) x (key registers).  Above kRankSteps the workgroup-wide
+// plan in LDS is faster.
+constexpr int kRankSteps = 512;
+int rank_steps(const moe_problem &p, int slabs) {
+  // tokens a workgroup can touch: one with whole workgroups per token
+  const int64_t span = slabs >= kWaves ? 1 : (kWaves - 2 + slabs) / slabs + 1;
+  const int64_t tokens = p.n_tokens < span ? p.n_tokens : span;
+  return static_cast<int>(tokens * p.top_k * rank_regs(p.n_tokens * p.top_k));
+}
+
 template <bool TILED>
 void launch_plan_dispatch_any(const PlanDispatchArgs &g, int fmt, int grid, size_t lds, hipStream_t stream) {
   if (fmt == MOE_FMT_BF16) launch_plan_dispatch_fmt<MOE_FMT_BF16, TILED>(g, grid, lds, stream);
@@ -884,7 +1099,15 @@ hipError_t launch_plan_dispatch(const moe_problem &p, const int32_t *ids, const 
   const int grid = max(g.dispatch_blocks, 1);  // N = 0 still writes the plan
   const size_t lds = small_plan_lds_bytes(p.n_experts);
   if (mode == PlanDispatchMode::kOneLaunch) {
-    launch_plan_dispatch_any<false>(g, p.fmt, grid, lds, stream);
+    if (one_launch_direct(p) && rank_steps(p, g.d.slabs) <= kRankSteps) {  // workgroup 0 plans
+      PlanDispatchArgs gr = g;
+      if (g.d.slabs >= kWaves) {  // whole workgroups per token
+        gr.d.token_blocks = static_cast<int>(p.n_tokens) * ((g.d.slabs + kWaves - 1) / kWaves);
+        gr.dispatch_blocks = gr.d.token_blocks + gr.d.pad_blocks + gr.d.tail_blocks;
+      }
+      launch_plan_dispatch_rank(gr, p.fmt, rank_regs(p.n_tokens * p.top_k), gr.dispatch_blocks + 1, lds, stream);
+    } else
+      launch_plan_dispatch_any<false>(g, p.fmt, grid, lds, stream);
     return hipGetLastError();
   }
   // tiled: the counting kernel has written the histograms and fault bits

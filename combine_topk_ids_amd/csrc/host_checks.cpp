@@ -60,6 +60,10 @@ PlanDispatchMode plan_dispatch_mode(const moe_problem &p) {
   return PlanDispatchMode::kSeparate;
 }
 
+bool one_launch_direct(const moe_problem &p) {
+  return plan_dispatch_mode(p) == PlanDispatchMode::kOneLaunch && p.pad_multiple == 1;
+}
+
 moe_problem exchange_rank_problem(const moe_problem &p) {
   moe_problem q = p;
   q.pad_multiple = 1;

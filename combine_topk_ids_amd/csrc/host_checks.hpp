@@ -56,6 +56,12 @@ size_t plan_workspace_bytes(const moe_problem &p);
 // kernels then the dispatch.  The first two take no fixed expert capacity.
 enum class PlanDispatchMode { kOneLaunch, kTiled, kSeparate };
 PlanDispatchMode plan_dispatch_mode(const moe_problem &p);
+// In one-launch mode without padding (A = 1), a pair's packed row is the
+// count of valid pairs ahead of it in (expert, pair index) order, which a
+// workgroup can count for its own pairs with ballots and one barrier, while
+// workgroup 0 writes the plan arrays (the dispatch launcher also bounds the
+// ballots a wave makes); otherwise every workgroup builds the plan in LDS.
+bool one_launch_direct(const moe_problem &p);
 
 // Workspace of the exchange plan: [EP][E+1] offsets and [EP][N*k] packed_src
 // of the per-rank plans, then EP copies of the single-rank plan workspace.

@@ -191,6 +191,34 @@ __device__ __forceinline__ uint32_t e2m1_rne_sat(float v) {
   return c | ((__float_as_uint(v) >> 28) & 8u);
 }
 
+// gfx950's conversion of two fp32 values to E2M1 codes, unscaled (scale
+// operand 1.0), into byte SEL of `old`: a in the low nibble, b in the high
+// one.  Equal to e2m1_rne_sat (nearest even, saturating) for every fp32
+// input but NaN, which it saturates to 6 (checked exhaustively by the
+// test-support kernels).
+template <int SEL>
+__device__ __forceinline__ uint32_t e2m1_pair_hw(uint32_t old, float a, float b) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, SEL);
+}
+
+// Eight E2M1 codes of a lane, value i in bits 4i..4i+3.  With `hw`,
+// gfx950's conversion (four independent byte conversions); otherwise the
+// software rule.  The two agree on every input but NaN, which the hardware
+// saturates to 6 and e2m1_rne_sat turns into a signed zero code, so callers
+// pass hw only for a wave whose values hold no NaN (wave-uniform).
+__device__ __forceinline__ uint32_t e2m1_lane8(const float (&q)[8], bool hw) {
+  if (hw)
+    return e2m1_pair_hw<0>(0u, q[0], q[1]) | e2m1_pair_hw<1>(0u, q[2], q[3]) |
+           e2m1_pair_hw<2>(0u, q[4], q[5]) | e2m1_pair_hw<3>(0u, q[6], q[7]);
+  uint32_t v = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v |= e2m1_rne_sat(q[i]) << (4 * i);
+  return v;
+}
+
+// Magnitude bits above those of infinity: a NaN.
+__device__ __forceinline__ bool nan_bits(uint32_t abs_bits) { return abs_bits > 0x7F800000u; }
+
 // E8M0 exponent X of a block with maximum magnitude bits `amax_bits` > 0:
 // floor(log2 amax) - 2, clamped below at -127 (subnormal maxima land there).
 __device__ __forceinline__ int mx_exponent(uint32_t amax_bits) {

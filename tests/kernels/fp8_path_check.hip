@@ -8,6 +8,14 @@
 //   s = fl32(a/448).
 // fp8_convert_check: for every fp32 bit pattern with |v| < 464, gfx950's
 //   conversion equals the software E4M3 rule.
+// fp4_convert_check: for every fp32 bit pattern v but NaN (infinities
+//   included), gfx950's E2M1 pair conversion (e2m1_pair_hw) of (v, -v) into
+//   each of the four bytes equals the software E2M1 rule (e2m1_rne_sat:
+//   nearest even, saturating at 6), and leaves the other three bytes of the
+//   destination as they were.  NaN, which the hardware saturates to 6 and
+//   the software rule maps to a signed zero code, is left to e2m1_lane8's
+//   software path; cnt[3] counts the NaN patterns whose hardware code is
+//   not +-6.
 // Outputs: cnt[0] pairs tested, cnt[1] mismatches, cnt[2] records written,
 // rec[3*i..] (inputs, got, want) of the first 8 mismatches.
 #include "moe_device.hpp"
@@ -79,5 +87,46 @@ extern "C" __attribute__((visibility("default"))) int fp8_convert_check(unsigned
                                                                         unsigned int *rec,
                                                                         void *stream) {
   convert_kernel<<<8192, 256, 0, static_cast<hipStream_t>(stream)>>>(cnt, rec);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+__global__ void fp4_convert_kernel(unsigned long long *cnt, unsigned int *rec) {
+  unsigned long long bad = 0, tested = 0;
+  const uint64_t stride = static_cast<uint64_t>(gridDim.x) * blockDim.x;
+  const uint32_t keep = 0xA5C3E1F0u;  // bytes that must survive
+  for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < (1ull << 32);
+       i += stride) {
+    const uint32_t u = static_cast<uint32_t>(i);
+    const float v = __uint_as_float(u), w = __uint_as_float(u ^ 0x80000000u);
+    if (v != v) {  // NaN: the hardware saturates (sign kept)
+      const uint32_t h = e2m1_pair_hw<0>(0u, v, w);
+      const uint32_t sat = (u >> 31) ? 0x7Fu : 0xF7u;  // (v, -v) = (-6, +6) or (+6, -6)
+      if (h != sat) atomicAdd(&cnt[3], 1ull);
+      continue;
+    }
+    const uint32_t pair = e2m1_rne_sat(v) | (e2m1_rne_sat(w) << 4);
+    const uint32_t g0 = e2m1_pair_hw<0>(keep, v, w), g1 = e2m1_pair_hw<1>(keep, v, w);
+    const uint32_t g2 = e2m1_pair_hw<2>(keep, v, w), g3 = e2m1_pair_hw<3>(keep, v, w);
+    ++tested;
+    const bool ok = g0 == ((keep & ~0xFFu) | pair) && g1 == ((keep & ~0xFF00u) | (pair << 8)) &&
+                    g2 == ((keep & ~0xFF0000u) | (pair << 16)) && g3 == ((keep & 0xFFFFFFu) | (pair << 24));
+    if (!ok) {
+      ++bad;
+      const unsigned long long slot = atomicAdd(&cnt[2], 1ull);
+      if (slot < 8) {
+        rec[3 * slot] = u;
+        rec[3 * slot + 1] = g0;
+        rec[3 * slot + 2] = (keep & ~0xFFu) | pair;
+      }
+    }
+  }
+  atomicAdd(&cnt[0], tested);
+  atomicAdd(&cnt[1], bad);
+}
+
+extern "C" __attribute__((visibility("default"))) int fp4_convert_check(unsigned long long *cnt,
+                                                                        unsigned int *rec,
+                                                                        void *stream) {
+  fp4_convert_kernel<<<8192, 256, 0, static_cast<hipStream_t>(stream)>>>(cnt, rec);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

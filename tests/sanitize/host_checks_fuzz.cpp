@@ -91,6 +91,10 @@ void check_accepted(const moe_problem &p) {
   const PlanDispatchMode m = plan_dispatch_mode(p);
   if (m == PlanDispatchMode::kOneLaunch) EXPECT(p.n_tokens * p.top_k <= kSmallPairs && p.expert_capacity == 0);
   if (m == PlanDispatchMode::kTiled) EXPECT((int64_t)g.ntiles * p.n_experts <= kTileHist && p.expert_capacity == 0);
+  if (one_launch_direct(p)) {  // keys (expert << 11 | pair index) fit 21 bits
+    EXPECT(m == PlanDispatchMode::kOneLaunch && p.pad_multiple == 1);
+    EXPECT(p.n_tokens * p.top_k <= kSmallPairs && kSmallPairs <= 2048 && p.n_experts <= 1024);
+  }
   EXPECT(map_workspace_bytes(p) % 256 == 0);
   EXPECT((int64_t)map_blocks(p) * (kMapThreads / map_lanes_per_token(p.n_experts)) >= p.n_tokens);
 }

@@ -29,7 +29,7 @@ def lib():
     import combine_topk_ids_amd.moe  # noqa: F401  (HIP runtime through torch)
     assert os.path.exists(LIB), f"{LIB} is not built (run __graft_entry__.build())"
     h = ctypes.CDLL(LIB)
-    for fn in (h.fp8_quotient_check, h.fp8_convert_check):
+    for fn in (h.fp8_quotient_check, h.fp8_convert_check, h.fp4_convert_check):
         fn.argtypes = [ctypes.c_void_p] * 3
         fn.restype = ctypes.c_int
     return h
@@ -57,3 +57,21 @@ def test_hw_e4m3_conversion_matches_software_rule(lib):
     print(f"[fp8] fp32 values |v| < 464 tested: {tested}, mismatches: {bad}", flush=True)
     assert tested == 2278555648
     assert bad == 0, examples
+
+
+def test_hw_e2m1_conversion_matches_software_rule(lib):
+    """gfx950's packed E2M1 conversion against the software rule, for every
+    fp32 bit pattern but NaN (and its negation) in each destination byte; a
+    NaN saturates to +-6 in hardware (the library's encoders take the
+    software rule for a wave that holds one)."""
+    cnt = torch.zeros(4, dtype=torch.int64, device="cuda")
+    rec = torch.zeros(24, dtype=torch.int32, device="cuda")
+    assert lib.fp4_convert_check(cnt.data_ptr(), rec.data_ptr(),
+                                 torch.cuda.current_stream().cuda_stream) == 0
+    torch.cuda.synchronize()
+    tested, bad, nrec, nan_other = (int(v) for v in cnt.cpu().numpy())
+    recs = rec.cpu().numpy().view(np.uint32).reshape(8, 3)[:min(nrec, 8)]
+    print(f"[fp4] fp32 values tested: {tested}, mismatches: {bad}", flush=True)
+    assert tested == (1 << 32) - 2 * ((1 << 23) - 1)   # every pattern but the NaNs
+    assert bad == 0, [[hex(v) for v in row] for row in recs]
+    assert nan_other == 0

@@ -155,6 +155,17 @@ SHAPES = [
     (4000, 128, 12, 2, 3, 1, "fp8", 0.0, True, False),    # tiled, E = 12
     (150, 128, 257, 8, 257, 2, "bf16", 0.1, False, True),  # E = 257: the scan spans two waves
     (1000, 128, 260, 4, 4, 2, "fp8", 0.1, True, True),    # tiled, E = 260
+    # one launch without padding: a workgroup counts the keys below its own
+    # pairs while (own pairs) x (key registers) <= 512, else the plan in LDS
+    (200, 64, 1024, 8, 64, 1, "bf16", 0.1, False, True),   # E = 1024: the widest keys
+    (227, 96, 64, 9, 8, 1, "mxfp4", 0.05, True, True),     # 36 own pairs x 8 registers
+    (228, 64, 64, 9, 8, 1, "bf16", 0.0, False, False),     # the same, no tail
+    (64, 2048, 16, 4, 4, 1, "bf16", 0.5, False, True),     # half masked, 4 waves a token
+    (1, 4096, 8, 8, 2, 1, "fp8", 0.0, True, True),         # one token, 8 waves
+    (30, 64, 128, 64, 8, 1, "bf16", 0.1, False, True),     # 256 own pairs x 8: plan in LDS
+    (31, 64, 128, 16, 8, 1, "mxfp4", 0.0, True, True),     # 64 own pairs x 4 registers
+    (4, 7168, 256, 8, 8, 1, "mxfp4", 0.0, False, False),   # 32 pairs: one key register
+    (9, 8200, 32, 4, 4, 1, "bf16", 0.1, True, True),       # 5 slabs: 2 workgroups a token, 3 idle waves
 ]
 
 
@@ -174,7 +185,8 @@ def test_plan_and_dispatch_shapes(moe, idx):
 def test_plan_and_dispatch_nvfp4_shapes(moe):
     rng = np.random.default_rng(44)
     for n, h, e, k, ep, a, gs in ((128, 256, 32, 8, 4, 2, 3.0), (40, 64, 8, 3, 2, 5, 0.01),
-                                  (300, 96, 64, 6, 8, 1, 400.0), (1500, 96, 64, 6, 8, 2, 7.0)):
+                                  (300, 96, 64, 6, 8, 1, 400.0), (1500, 96, 64, 6, 8, 2, 7.0),
+                                  (70, 1536, 64, 8, 8, 1, 5.0), (16, 7168, 256, 8, 8, 1, 336.0)):
         say(f"[plan+dispatch] nvfp4 N={n} H={h} E={e} k={k} A={a} gs={gs}")
         ids, _ = random_routing(rng, n, e, k, masked_frac=0.1)
         check_pd(moe, ids=ids, hidden=random_bf16(rng, (n, h)), e=e, ep=ep, a=a, fmt="nvfp4",
@@ -201,6 +213,21 @@ def test_plan_and_dispatch_faults_and_empty(moe):
     got, pl = check_pd(moe, ids=ids, hidden=random_bf16(rng, (n, 64)), e=e, ep=4, a=2,
                        fmt="bf16", cap=900)
     assert got["status"] == 1 | 2 | 4
+    say("[plan+dispatch] DUP, BAD and CAPACITY in one launch without padding")
+    n = 200
+    ids, _ = random_routing(rng, n, e, k)
+    ids[n - 1, 3] = ids[n - 1, 2]
+    ids[0, 0] = 16
+    ids[77, 1] = -9
+    got, pl = check_pd(moe, ids=ids, hidden=random_bf16(rng, (n, 64)), e=e, ep=4, a=1,
+                       fmt="bf16", cap=150)
+    assert got["status"] == 1 | 2 | 4
+    say("[plan+dispatch] N = 0 without padding, with a zero tail")
+    check_pd(moe, ids=np.zeros((0, 2), np.int32), hidden=np.zeros((0, 64), np.uint16), e=4,
+             ep=2, a=1, fmt="bf16", cap=0)
+    say("[plan+dispatch] every pair masked, no padding")
+    check_pd(moe, ids=np.full((40, 5), -1, np.int32), hidden=random_bf16(rng, (40, 128)), e=6,
+             ep=3, a=1, fmt="fp8")
     say("[plan+dispatch] N = 0 with pad rows and a zero tail")
     check_pd(moe, ids=np.zeros((0, 2), np.int32), hidden=np.zeros((0, 64), np.uint16), e=4,
              ep=2, a=3, fmt="bf16", cap=0)
