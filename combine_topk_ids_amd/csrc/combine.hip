@@ -14,7 +14,7 @@
 // for j = 0..k-1 in order, skipping masked slots: the same fp32 rounding
 // sequence on every element, so results do not depend on the launch shape.
 // Without weights (rows gated at dispatch: DeepSpeed v0.19.4 function index,
-// page 15, pre-multiplying by router scores) every w is 1.
+// page 15, the entry on scaling rows by router scores) every w is 1.
 //
 // Design for gfx950.  One wave64 per (token, column slab); each lane owns 8
 // consecutive columns (one 16-byte bf16 vector) of every 512-column chunk of
