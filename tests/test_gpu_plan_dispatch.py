@@ -149,6 +149,7 @@ SHAPES = [
     (100, 128, 64, 64, 8, 2, "bf16", 0.1, False, True),   # k = 64: 32-token tiles
     (300, 256, 1024, 8, 64, 1, "mxfp4", 0.1, False, True),  # 2 x 1024 = 2048 entries: the most tiled
     (600, 256, 1024, 8, 64, 3, "bf16", 0.0, False, True),   # 3 x 1024 entries: separate launches
+    (5000, 128, 256, 8, 8, 16, "fp8", 0.05, True, True),   # separate, 20 tiles x 256, 16-row pads
     (3000, 384, 32, 5, 4, 7, "fp8", 0.3, True, True),     # tiled, quantised workgroup order
     (2500, 1024, 128, 8, 8, 128, "mxfp4", 0.05, True, False),  # tiled, 128-row pads
     (3000, 128, 100, 4, 5, 3, "bf16", 0.1, False, True),  # tiled, E = 100 (does not divide 256)
