@@ -203,8 +203,15 @@ class Path:
                 self.moe.PD_SEPARATE: "separate"}[self.moe.moe_plan_and_dispatch_mode(self.p)]
 
     def dispatch_kernel(self):
-        """The kernel _end launches."""
-        return "dispatch_kernel" if self.mode() == "separate" else "plan_dispatch_kernel"
+        """The kernel _end launches: in one launch without padding the kernel
+        that counts each pair's row (the library takes it up to 512 ballots a
+        wave, which every one-launch workload here is far below)."""
+        m = self.mode()
+        if m == "separate":
+            return "dispatch_kernel"
+        if m == "one_launch" and self.w.a == 1:
+            return "plan_dispatch_rank_kernel"
+        return "plan_dispatch_kernel"
 
     def r_used(self):
         return int(self.sets[0]["plan"].expert_offsets[-1].item())
@@ -633,7 +640,7 @@ def measure(moe, torch, w, args, context=True):
     dom_bytes = b[dom]
     if dom == "dispatch":
         kname = path.dispatch_kernel()
-        if kname == "plan_dispatch_kernel":
+        if kname.startswith("plan_dispatch"):
             # it also reads the IDs and writes slot and packed_src
             dom_bytes = b["dispatch"] + b["plan"]
     achieved = dom_bytes / (kt[dom] * 1e-3) / 1e9
