@@ -735,7 +735,7 @@ __global__ __launch_bounds__(kThreads) void plan_dispatch_kernel(PlanDispatchArg
   // token's packed_src rows are written by the wave of its slab 0.  A pair
   // the histograms do not account for (tiled mode, a workspace that does
   // not count these IDs) is left unplaced and reported.
-  int my_slot = live && lane < k ? own_slot(s, TILED ? tlo : 0, p0, t * k + lane, g.r_max) : -1;
+  int my_slot = live && lane < k ? own_slot(s, TILED ? tlo : 0, p0, t * k + lane, g.r_max, g.sp.ecap) : -1;
   const bool bad = my_slot == kBadSlot;
   if (bad) my_slot = -1;
   if (live && slab == 0) {
@@ -748,7 +748,7 @@ __global__ __launch_bounds__(kThreads) void plan_dispatch_kernel(PlanDispatchArg
   // packed_src = -1 on the unused rows of each expert and on the tail, never
   // outside the buffer
   const int stride = gridDim.x * kThreads;
-  const int per = g.sp.a - 1;
+  const int per = g.sp.ecap > 0 ? g.sp.ecap : g.sp.a - 1;  // unused rows an expert, at most
   for (int qq = b * kThreads + tid; qq < E * per; qq += stride) {
     const int e = qq / per;
     const int64_t row = static_cast<int64_t>(s.off[e]) + s.cnt[e] + (qq - e * per);
@@ -1084,6 +1084,7 @@ hipError_t launch_plan_dispatch(const moe_problem &p, const int32_t *ids, const 
   g.sp.e = p.n_experts;
   g.sp.ep = p.ep;
   g.sp.a = p.pad_multiple;
+  g.sp.ecap = static_cast<int>(p.expert_capacity);
   g.sp.l = p.n_experts / p.ep;
   g.sp.cap = p.recv_capacity;
   g.counts = plan.expert_counts;

@@ -51,7 +51,6 @@ size_t plan_workspace_bytes(const moe_problem &p) {
 }
 
 PlanDispatchMode plan_dispatch_mode(const moe_problem &p) {
-  if (p.expert_capacity != 0) return PlanDispatchMode::kSeparate;
   const int64_t npairs = p.n_tokens * p.top_k;
   if (npairs <= kSmallPairs) return PlanDispatchMode::kOneLaunch;
   const PlanGeom geo = plan_geometry(p);
@@ -61,7 +60,8 @@ PlanDispatchMode plan_dispatch_mode(const moe_problem &p) {
 }
 
 bool one_launch_direct(const moe_problem &p) {
-  return plan_dispatch_mode(p) == PlanDispatchMode::kOneLaunch && p.pad_multiple == 1;
+  return plan_dispatch_mode(p) == PlanDispatchMode::kOneLaunch && p.pad_multiple == 1 &&
+         p.expert_capacity == 0;
 }
 
 moe_problem exchange_rank_problem(const moe_problem &p) {

@@ -53,10 +53,12 @@ size_t plan_workspace_bytes(const moe_problem &p);
 // How moe_plan_and_dispatch runs a problem: one launch (at most kSmallPairs
 // pairs), tiled (the counting kernel, then one launch that finishes the plan
 // and dispatches; at most kTileHist histogram entries), or the plan's
-// kernels then the dispatch.  The first two take no fixed expert capacity.
+// kernels then the dispatch.  A fixed expert capacity takes the same modes
+// (each expert's first cap pairs kept, the rest dropped by the launch that
+// places them).
 enum class PlanDispatchMode { kOneLaunch, kTiled, kSeparate };
 PlanDispatchMode plan_dispatch_mode(const moe_problem &p);
-// In one-launch mode without padding (A = 1), a pair's packed row is the
+// In one-launch mode without padding (A = 1) or capacity, a pair's packed row is the
 // count of valid pairs ahead of it in (expert, pair index) order, which a
 // workgroup can count for its own pairs with ballots and one barrier, while
 // workgroup 0 writes the plan arrays (the dispatch launcher also bounds the

@@ -59,6 +59,7 @@ static_assert(kSmallTargets >= kSmallWaves * kMaxTopK, "own pairs: up to one tok
 struct SmallPlanArgs {
   const int32_t *ids;  // [n][k]
   int n, k, e, ep, a;
+  int ecap;            // fixed rows per expert (0: dropless, padded to A)
   int l;               // E / EP, experts per destination
   int64_t cap;         // recv_capacity (rows per destination)
   // tiled mode only
@@ -158,13 +159,22 @@ __device__ uint32_t plan_finish(const SmallPlanArgs &g, const SmallPlanLds &s, u
   // ---- totals; padded and unpadded exclusive scans (4 experts a thread) ---
   {
     const int e0 = 4 * tid;
-    int c[4], p[4], sc = 0, sp = 0;
+    // segment sizes: c padded to A, or the fixed capacity; with a fixed
+    // capacity the unpadded sums count the kept pairs, min(c, cap)
+    int c[4], kc[4], p[4], sc = 0, sp = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       c[q] = e0 + q < E ? s.cnt[e0 + q] + (TOTAL ? 0 : s.before[e0 + q]) : 0;
-      // no integer division when there is no padding (a long dependent chain)
-      p[q] = g.a == 1 ? c[q] : ((c[q] + g.a - 1) / g.a) * g.a;
-      sc += c[q];
+      if (g.ecap > 0) {
+        kc[q] = min(c[q], g.ecap);
+        p[q] = e0 + q < E ? g.ecap : 0;
+        if (c[q] > g.ecap) fl |= MOE_STATUS_DROPPED;
+      } else {
+        kc[q] = c[q];
+        // no integer division when there is no padding (a long dependent chain)
+        p[q] = g.a == 1 ? c[q] : ((c[q] + g.a - 1) / g.a) * g.a;
+      }
+      sc += kc[q];
       sp += p[q];
     }
     const int ip = wave_incl_scan(sp), ic = wave_incl_scan(sc);
@@ -197,7 +207,7 @@ __device__ uint32_t plan_finish(const SmallPlanArgs &g, const SmallPlanLds &s, u
         s.cpre[e0 + q] = xc;
       }
       xp += p[q];
-      xc += c[q];
+      xc += kc[q];
     }
     if (tid == 0) {
       s.off[E] = tp;
@@ -212,9 +222,9 @@ __device__ uint32_t plan_finish(const SmallPlanArgs &g, const SmallPlanLds &s, u
   for (int r = tid; r < g.ep; r += kSmallThreads)
     if (s.cpre[(r + 1) * L] - s.cpre[r * L] > g.cap) fl |= MOE_STATUS_CAPACITY;
   const uint64_t b0 = ballot(fl & MOE_STATUS_BAD_ID), b1 = ballot(fl & MOE_STATUS_DUP_ID),
-                 b2 = ballot(fl & MOE_STATUS_CAPACITY);
+                 b2 = ballot(fl & MOE_STATUS_CAPACITY), b3 = ballot(fl & MOE_STATUS_DROPPED);
   const uint32_t wfl = (b0 ? MOE_STATUS_BAD_ID : 0u) | (b1 ? MOE_STATUS_DUP_ID : 0u) |
-                       (b2 ? MOE_STATUS_CAPACITY : 0u);
+                       (b2 ? MOE_STATUS_CAPACITY : 0u) | (b3 ? MOE_STATUS_DROPPED : 0u);
   if (lane == 0 && wfl) atomicOr(&s_fl, wfl);
   __syncthreads();
   return s_fl;
@@ -232,9 +242,10 @@ __device__ uint32_t plan_finish(const SmallPlanArgs &g, const SmallPlanLds &s, u
 // row inside the buffer [0, r_max).  From a plan of the IDs themselves it
 // always does; in tiled mode the counts come from histograms in memory,
 // and if those do not count these IDs the pair gets kBadSlot instead.
+// With a fixed capacity `ecap`, a pair ranked at or past it is dropped (-1).
 constexpr int kBadSlot = -2;
 
-__device__ __forceinline__ int own_slot(const SmallPlanLds &s, int lo, int p0, int p, int r_max) {
+__device__ __forceinline__ int own_slot(const SmallPlanLds &s, int lo, int p0, int p, int r_max, int ecap) {
   const int e = s.ids[p - lo];
   if (e < 0) return -1;
   const int *own = s.ids + (p0 - lo);
@@ -252,8 +263,10 @@ __device__ __forceinline__ int own_slot(const SmallPlanLds &s, int lo, int p0, i
 #pragma unroll
     for (int q = 0; q < kRankBatch; ++q) r += q0 + q < j && w[q] == e ? 1 : 0;
   }
+  if (r < 0 || r >= s.cnt[e]) return kBadSlot;
+  if (ecap > 0 && r >= ecap) return -1;
   const int64_t row = static_cast<int64_t>(s.off[e]) + r;
-  return r < 0 || r >= s.cnt[e] || row < 0 || row >= r_max ? kBadSlot : static_cast<int>(row);
+  return row < 0 || row >= r_max ? kBadSlot : static_cast<int>(row);
 }
 
 // Fills cnt, off, cpre and ids for the whole problem and before (each

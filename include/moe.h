@@ -273,12 +273,14 @@ MOE_API int moe_dispatch_gated(const moe_problem *p, const moe_plan *plan,
  * permute_a2av API reference, description: one call computes the layout
  * from the routing and permutes the rows into it.  How it runs
  * (moe_plan_and_dispatch_mode): problems with at most 2048 (token, k) pairs
- * and no fixed expert capacity run as one launch, in which every workgroup
- * computes the plan in LDS before its share of the dispatch; larger ones
- * without a fixed capacity whose count tiles times E is at most 2048 run
- * the plan's counting kernel and then one launch in which every workgroup
- * finishes the plan it needs from the tile histograms and dispatches; the
- * rest run the plan's kernels and then the dispatch.  Equivalent to
+ * run as one launch, in which every workgroup finds the rows of its own
+ * pairs before its share of the dispatch (by counting sort keys when there
+ * is no padding and no fixed capacity, else from the plan built in LDS);
+ * larger ones whose count tiles times E is at most 2048 run the plan's
+ * counting kernel and then one launch in which every workgroup finishes
+ * the plan it needs from the tile histograms and dispatches; the rest run
+ * the plan's kernels and then the dispatch.  A fixed expert capacity drops
+ * the pairs ranked past it in the launch that places them.  Equivalent to
  * moe_plan_and_dispatch_begin followed by moe_plan_and_dispatch_end.
  * workspace: moe_workspace_bytes(p) bytes (none for the one-launch sizes).
  * Arguments, layouts and errors as in the calls it replaces. */

@@ -89,10 +89,10 @@ void check_accepted(const moe_problem &p) {
   EXPECT(ws % 256 == 0);
   EXPECT(g.single ? ws == 0 : ws >= (size_t)g.ntiles * (p.n_experts + 1) * 4);
   const PlanDispatchMode m = plan_dispatch_mode(p);
-  if (m == PlanDispatchMode::kOneLaunch) EXPECT(p.n_tokens * p.top_k <= kSmallPairs && p.expert_capacity == 0);
-  if (m == PlanDispatchMode::kTiled) EXPECT((int64_t)g.ntiles * p.n_experts <= kTileHist && p.expert_capacity == 0);
+  if (m == PlanDispatchMode::kOneLaunch) EXPECT(p.n_tokens * p.top_k <= kSmallPairs);
+  if (m == PlanDispatchMode::kTiled) EXPECT((int64_t)g.ntiles * p.n_experts <= kTileHist && r_max <= INT32_MAX);
   if (one_launch_direct(p)) {  // keys (expert << 11 | pair index) fit 21 bits
-    EXPECT(m == PlanDispatchMode::kOneLaunch && p.pad_multiple == 1);
+    EXPECT(m == PlanDispatchMode::kOneLaunch && p.pad_multiple == 1 && p.expert_capacity == 0);
     EXPECT(p.n_tokens * p.top_k <= kSmallPairs && kSmallPairs <= 2048 && p.n_experts <= 1024);
   }
   EXPECT(map_workspace_bytes(p) % 256 == 0);

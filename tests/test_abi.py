@@ -167,7 +167,7 @@ def test_plan_and_dispatch_halves_reject_as_the_whole(moe):
 def test_plan_and_dispatch_mode(moe):
     """One launch up to 2048 pairs; tiled while (count tiles of
     floor(2048 / k) tokens) x E <= 2048; the plan's kernels then the
-    dispatch otherwise, and always with a fixed expert capacity."""
+    dispatch otherwise.  A fixed expert capacity takes the same modes."""
     one, tiled, sep = moe.PD_ONE_LAUNCH, moe.PD_TILED, moe.PD_SEPARATE
     mode = moe.moe_plan_and_dispatch_mode
     assert mode(moe.problem(0, 64, 2, 4, 2)) == one
@@ -179,8 +179,9 @@ def test_plan_and_dispatch_mode(moe):
     assert mode(moe.problem(2048 * 8, 64, 1, 8, 2)) == tiled          # k = 1: 8 tiles x 8
     assert mode(moe.problem(8192, 7168, 8, 256, 8)) == sep            # 32 x 256
     assert mode(moe.problem(16384, 4096, 8, 128, 16)) == sep          # 64 x 128
-    assert mode(moe.problem(100, 256, 4, 8, 2, expert_capacity=60)) == sep
-    assert mode(moe.problem(4096, 4096, 6, 64, 8, expert_capacity=384)) == sep
+    assert mode(moe.problem(100, 256, 4, 8, 2, expert_capacity=60)) == one
+    assert mode(moe.problem(4096, 4096, 6, 64, 8, expert_capacity=384)) == tiled
+    assert mode(moe.problem(8192, 7168, 8, 256, 8, expert_capacity=320)) == sep
     bad = moe.problem(64, 256, 2, 8, 4)
     bad.hidden = 7
     assert moe.lib.moe_plan_and_dispatch_mode(ctypes.byref(bad)) == -1

@@ -135,18 +135,22 @@ FUZZ = [
 ]
 
 
+@pytest.mark.parametrize("halves", [False, True], ids=["three_calls", "bench_calls"])
 @pytest.mark.parametrize("idx", range(len(FUZZ)),
                          ids=[f"n{c[0]}_h{c[1]}_e{c[2]}_k{c[3]}_{c[5]}_cf{c[6]}" for c in FUZZ])
-def test_capacity_fuzz_shapes(moe, idx):
+def test_capacity_fuzz_shapes(moe, idx, halves):
+    """Every shape through the plan and dispatch calls, and through
+    moe_plan_and_dispatch's halves, which drop the pairs past the capacity in
+    the launch that places them (one launch, tiled or separate by size)."""
     n, h, e, k, ep, fmt, cf, masked = FUZZ[idx]
-    say(f"[capacity fuzz] N={n} H={h} E={e} k={k} EP={ep} {fmt} cf={cf} masked={masked}")
+    say(f"[capacity fuzz] N={n} H={h} E={e} k={k} EP={ep} {fmt} cf={cf} masked={masked} halves={halves}")
     rng = np.random.default_rng(700 + idx)
     ids, wts = random_routing(rng, n, e, k, masked_frac=masked)
     x = random_bf16(rng, (n, h))
     cap = oracle.expert_capacity(n, k, e, cf)
     y = None if fmt == "bf16" else random_bf16(rng, (max(e * cap, 1), h))
     check_capacity(moe, ids=ids, weights=wts, hidden=x, e=e, ep=ep, fmt=fmt, cf=cf,
-                   rcap=int(rng.integers(1, n * k + 1)), expert_out=y)
+                   rcap=int(rng.integers(1, n * k + 1)), expert_out=y, halves=halves)
 
 
 def test_capacity_faults_and_skew(moe):
@@ -157,7 +161,15 @@ def test_capacity_faults_and_skew(moe):
     ids[:, 0] = 3               # expert 3 gets every token: most are dropped
     ids[10, 1] = 3              # repeated ID
     ids[20, 2] = 40             # out of range
-    say("[capacity faults] skew to one expert, DUP and BAD")
-    got, _, _ = check_capacity(moe, ids=ids, weights=wts, hidden=random_bf16(rng, (n, h)), e=e,
-                               ep=4, fmt="bf16", cf=1.0, rcap=n)
-    assert got["status"] & (1 | 2 | 16) == (1 | 2 | 16)
+    x = random_bf16(rng, (n, h))
+    for halves in (False, True):
+        say(f"[capacity faults] skew to one expert, DUP and BAD; halves={halves}")
+        got, _, _ = check_capacity(moe, ids=ids, weights=wts, hidden=x, e=e, ep=4, fmt="bf16",
+                                   cf=1.0, rcap=n, halves=halves)
+        assert got["status"] & (1 | 2 | 16) == (1 | 2 | 16)
+    small = ids[:300]  # 1200 pairs: one launch
+    for halves in (False, True):
+        say(f"[capacity faults] one-launch size; halves={halves}")
+        got, _, _ = check_capacity(moe, ids=small, weights=wts[:300], hidden=x[:300], e=e, ep=4,
+                                   fmt="bf16", cf=1.0, rcap=300, halves=halves)
+        assert got["status"] & (1 | 2 | 16) == (1 | 2 | 16)
