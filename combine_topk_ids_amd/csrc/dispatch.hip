@@ -217,12 +217,11 @@ __device__ __forceinline__ void unpack_lane(const RawSlab &r, int c, float (&f)[
   }
 }
 
-// Cache policy of the bf16 row stores.  Device scope (sc1) sends the full
-// 16-byte-per-lane rows on past the XCD's L2 at once; on the uniform
-// workload (4096 tokens x 6 rows of 8 KiB) the dispatch ran 44.0 -> 43.1 us
-// with it, and the Zipf and capacity workloads were unchanged.  The FP8
-// rows, stored 8 bytes per lane with a scale beside them, ran 6-9% slower
-// with it, so the quantising formats keep default stores.
+// Cache policy of the bf16 row stores: device scope (the sc1 bit).  Against
+// default stores, the uniform workload's dispatch (4096 tokens x 6 rows of
+// 8 KiB) ran 44.0 -> 43.1 us with it, and the Zipf and capacity workloads
+// did not change.  The same bit made the FP8 dispatch 6-9% slower, so the
+// quantising formats keep default stores.
 constexpr int kStoreDevice = 16;
 constexpr int kStoreNT = 2;
 
