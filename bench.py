@@ -698,7 +698,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build "
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the library "
               "measures one GPU's share of the work, with expert-parallel ranks simulated as "
               "segments of one buffer.", file=sys.stderr)
         sys.exit(2)
