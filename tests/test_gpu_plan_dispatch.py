@@ -167,6 +167,8 @@ SHAPES = [
     (31, 64, 128, 16, 8, 1, "mxfp4", 0.0, True, True),     # 64 own pairs x 4 registers
     (4, 7168, 256, 8, 8, 1, "mxfp4", 0.0, False, False),   # 32 pairs: one key register
     (9, 8200, 32, 4, 4, 1, "bf16", 0.1, True, True),       # 5 slabs: 2 workgroups a token, 3 idle waves
+    (256, 7168, 256, 8, 8, 1, "fp8", 0.0, False, True),    # 2048 pairs counted, 14 slabs a token
+    (2048, 64, 32, 1, 4, 1, "bf16", 0.1, False, False),    # k = 1, 2048 tokens: 8 key registers, 4 tokens a workgroup
 ]
 
 
