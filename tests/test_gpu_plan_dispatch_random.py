@@ -56,11 +56,15 @@ def draw(idx):
 
 def test_random_cases_cover_every_mode(moe):
     modes = set()
+    counted = set()  # one launch without padding: rows by counting keys, by key registers
     for idx in range(N_CASES):
         n, h, e, k, ep, a, fmt, *_ = draw(idx)
-        modes.add(moe.moe_plan_and_dispatch_mode(moe.problem(n, h, k, e, ep, pad_multiple=a,
-                                                             fmt=fmt)))
+        mode = moe.moe_plan_and_dispatch_mode(moe.problem(n, h, k, e, ep, pad_multiple=a, fmt=fmt))
+        modes.add(mode)
+        if mode == moe.PD_ONE_LAUNCH and a == 1:
+            counted.add(1 if n * k <= 256 else 4 if n * k <= 1024 else 8)
     assert modes == {moe.PD_ONE_LAUNCH, moe.PD_TILED, moe.PD_SEPARATE}
+    assert counted == {1, 4, 8}
 
 
 @pytest.mark.parametrize("idx", range(N_CASES))
